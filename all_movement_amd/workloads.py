@@ -1,0 +1,287 @@
+"""Seeded synthetic workloads for the all_to_all_v exchange.
+
+Input generation only: this module builds count matrices, payload bytes,
+sentinel-filled targets and zeroed signals.  It holds none of the exchange's
+arithmetic (no displacements, no placement) and imports neither the HIP
+binding nor the oracle, so both sides can draw the same inputs from it.
+
+The five workloads (c1..c5) are the exchange at growing sizes:
+
+* c1  P=4, fp32, counts uniform in [0, 64], core_num 1 (one block).
+* c2  P=8, fp32, counts uniform in [0, 4096] with 10% of entries forced to 0,
+      core_num 10 (folds to 8 blocks).
+* c3  P=8, int8, an MoE dispatch: 4096 tokens per source rank, each routed to
+      2 distinct ranks drawn without replacement with Zipf(1.2) popularity
+      (rank d has weight (d+1)^-1.2), 7168 bytes per token; core_num 64.
+      The token-and-routing form follows the EP (expert parallel) data flow of
+      the CANN BatchMatMulReduceScatterAllToAll page.
+* c4  P=32, fp32, counts uniform in [0, 2^19] with 20% zeros, core_num 256.
+* c5  P=8, fp32, equal counts 2^25: the AllToAll at the end of the CANN
+      BatchMatMulReduceScatterAllToAll op, per rank (E/ep=8, ep*C=8*2048,
+      H/tp=2048) to (E=64, C=2048, H/tp=2048), input already packed by
+      destination; core_num 256.
+
+Payload bytes come from a counter-based SplitMix64 stream (Steele, Lea and
+Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014; the
+finalizer constants are Vigna's published splitmix64), so any byte can be
+regenerated on its own: byte i of stream ``seed`` is byte ``i % 8`` (little
+endian) of ``mix(seed + (i // 8 + 1) * 0x9E3779B97F4A7C15)``.  Counts and
+routing come from ``numpy.random.Generator(PCG64(k))`` for workload k.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+FP32 = 0
+INT8 = 1
+ELEM_SIZE = {FP32: 4, INT8: 1}
+SENTINEL = 0xA5
+
+_GOLDEN = 0x9E3779B97F4A7C15
+_M1 = 0xBF58476D1CE4E5B9
+_M2 = 0x94D049BB133111EB
+
+
+def _signed(x: int) -> int:
+    x &= (1 << 64) - 1
+    return x - (1 << 64) if x >= 1 << 63 else x
+
+
+# ---------------------------------------------------------------- payload bytes
+
+def random_words_np(seed: int, first_word: int, nwords: int) -> np.ndarray:
+    """SplitMix64 words ``first_word .. first_word+nwords-1`` of stream ``seed``."""
+    with np.errstate(over="ignore"):
+        i = np.arange(first_word + 1, first_word + 1 + nwords, dtype=np.uint64)
+        z = np.uint64(seed & ((1 << 64) - 1)) + i * np.uint64(_GOLDEN)
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(_M1)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(_M2)
+        z = z ^ (z >> np.uint64(31))
+    return z
+
+
+def random_bytes_np(seed: int, start: int, n: int) -> np.ndarray:
+    """Bytes ``start .. start+n-1`` of stream ``seed`` as uint8 (numpy, any offset)."""
+    if n <= 0:
+        return np.zeros(0, np.uint8)
+    w0 = start // 8
+    w1 = (start + n + 7) // 8
+    b = random_words_np(seed, w0, w1 - w0).view(np.uint8)
+    off = start - w0 * 8
+    return b[off:off + n].copy()
+
+
+def fill_random_(t, seed: int, chunk_words: int = 1 << 24) -> None:
+    """Fill a flat uint8 torch tensor (CPU or GPU) with stream ``seed`` from byte 0.
+
+    Same bits as :func:`random_bytes_np`; integer ops only, chunked so the
+    temporaries stay small.  ``t.numel()`` need not be a multiple of 8.
+    """
+    import torch
+    assert t.dtype == torch.uint8 and t.dim() == 1 and t.is_contiguous()
+    n = t.numel()
+    nwords = (n + 7) // 8
+    g, m1, m2 = _signed(_GOLDEN), _signed(_M1), _signed(_M2)
+    sd = _signed(seed)
+    for w0 in range(0, nwords, chunk_words):
+        w1 = min(nwords, w0 + chunk_words)
+        z = torch.arange(w0 + 1, w1 + 1, dtype=torch.int64, device=t.device)
+        z.mul_(g).add_(sd)
+        z.bitwise_xor_((z >> 30) & ((1 << 34) - 1)).mul_(m1)
+        z.bitwise_xor_((z >> 27) & ((1 << 37) - 1)).mul_(m2)
+        z.bitwise_xor_((z >> 31) & ((1 << 33) - 1))
+        b = z.view(torch.uint8)
+        lo, hi = w0 * 8, min(n, w1 * 8)
+        t[lo:hi].copy_(b[: hi - lo])
+
+
+# ---------------------------------------------------------------- count matrices
+
+def uniform_counts(rng: np.random.Generator, P: int, hi: int, zero_frac: float) -> np.ndarray:
+    """Counts uniform in [0, hi] with exactly round(zero_frac*P*P) entries forced to 0."""
+    C = rng.integers(0, hi + 1, size=(P, P), dtype=np.int64)
+    nz = int(round(zero_frac * P * P))
+    if nz:
+        idx = rng.choice(P * P, size=nz, replace=False)
+        C.reshape(-1)[idx] = 0
+    return C.astype(np.int32)
+
+
+def moe_routing(rng: np.random.Generator, P: int, tokens: int, topk: int,
+                zipf_s: float) -> np.ndarray:
+    """bool [P(src), tokens, P(dst)]: each token picks ``topk`` distinct ranks.
+
+    Sampling without replacement proportional to weight (d+1)^-s, done with
+    the Gumbel-top-k construction (equivalent to drawing ranks one at a time
+    without replacement, each draw proportional to the remaining weights).
+    """
+    logw = -zipf_s * np.log(np.arange(1, P + 1, dtype=np.float64))
+    keys = logw[None, None, :] + rng.gumbel(size=(P, tokens, P))
+    top = np.argsort(-keys, axis=2, kind="stable")[:, :, :topk]
+    mask = np.zeros((P, tokens, P), dtype=bool)
+    np.put_along_axis(mask, top, True, axis=2)
+    return mask
+
+
+# ---------------------------------------------------------------- workloads
+
+@dataclass
+class Workload:
+    name: str
+    description: str
+    P: int
+    dtype: int
+    core_num: int
+    S: int
+    in_slab: int            # bytes per input slab
+    tgt_slab: int           # bytes per target slab
+    counts: np.ndarray      # int32 [P, P], elements
+    payload_seed: int
+    # c3 only: token payloads are duplicated into both destinations.
+    routing: np.ndarray | None = None
+    token_bytes: int = 0
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def elem(self) -> int:
+        return ELEM_SIZE[self.dtype]
+
+    @property
+    def payload_bytes(self) -> int:
+        return int(self.counts.astype(np.int64).sum()) * self.elem
+
+    @property
+    def in_bytes(self) -> int:
+        return self.P * self.in_slab
+
+    @property
+    def tgt_bytes(self) -> int:
+        return self.P * self.tgt_slab
+
+    def summary(self) -> dict:
+        return {"workload": self.name, "P": self.P,
+                "dtype": "fp32" if self.dtype == FP32 else "int8",
+                "core_num": self.core_num, "signal": [self.P, self.S],
+                "in_slab_bytes": self.in_slab, "tgt_slab_bytes": self.tgt_slab,
+                "payload_bytes": self.payload_bytes}
+
+
+def workload(k: int, scale: int = 1) -> Workload:
+    """Workload c``k`` (k = 1..5).  ``scale`` > 1 shrinks c3..c5 for quick tests
+    (the count distribution keeps its shape, sizes divide by ``scale``)."""
+    rng = np.random.Generator(np.random.PCG64(k))
+    seed = 1000 + k
+    if k == 1:
+        P = 4
+        C = uniform_counts(rng, P, 64, 0.0)
+        slab = 64 * P * 4
+        return Workload("c1_p4_fp32_uniform64", "P=4 fp32 counts U[0,64], core_num 1",
+                        P, FP32, 1, 1, slab, slab, C, seed)
+    if k == 2:
+        P = 8
+        C = uniform_counts(rng, P, 4096, 0.1)
+        slab = 4096 * P * 4
+        return Workload("c2_p8_fp32_uniform4096", "P=8 fp32 counts U[0,4096] 10% zero, core_num 10",
+                        P, FP32, 10, 8, slab, slab, C, seed)
+    if k == 3:
+        P, tokens, hidden = 8, 4096 // scale, 7168
+        route = moe_routing(rng, P, tokens, 2, 1.2)
+        n = route.sum(axis=1).astype(np.int64)          # [src, dst] tokens
+        C = (n * hidden).astype(np.int32)
+        return Workload("c3_p8_int8_moe_top2_zipf1.2", "P=8 int8 MoE dispatch, 4096 tok/rank top-2 "
+                        "Zipf(1.2), hidden 7168, core_num 64",
+                        P, INT8, 64, 64, 2 * tokens * hidden, P * tokens * hidden, C, seed,
+                        routing=route, token_bytes=hidden)
+    if k == 4:
+        P = 32
+        hi = (1 << 19) // scale
+        C = uniform_counts(rng, P, hi, 0.2)
+        slab = P * hi * 4
+        return Workload("c4_p32_fp32_uniform2^19", "P=32 fp32 counts U[0,2^19] 20% zero, core_num 256",
+                        P, FP32, 256, 256, slab, slab, C, seed)
+    if k == 5:
+        P = 8
+        n = (1 << 25) // scale                          # (E/ep)*C*(H/tp) elements
+        C = np.full((P, P), n, dtype=np.int32)
+        slab = P * n * 4
+        return Workload("c5_p8_fp32_equal_bmm_rs_a2a", "P=8 fp32 equal counts 2^25 "
+                        "(E/ep=8, ep*C=8*2048, H/tp=2048) -> (E=64, C=2048, H/tp=2048), core_num 256",
+                        P, FP32, 256, 256, slab, slab, C, seed,
+                        extra={"E_over_ep": 8, "ep": 8, "C": 2048 // scale, "H_over_tp": 2048})
+    raise ValueError(f"no workload c{k}")
+
+
+def custom(P: int, dtype: int, counts: np.ndarray, core_num: int = 1, S: int | None = None,
+           in_slab: int | None = None, tgt_slab: int | None = None, seed: int = 7,
+           name: str = "custom") -> Workload:
+    """A workload with the given counts; slabs default to the exact maxima (rounded to 16)."""
+    C = np.ascontiguousarray(counts, dtype=np.int32)
+    e = ELEM_SIZE[dtype]
+    rows = int(C.astype(np.int64).sum(axis=1).max(initial=0)) * e
+    cols = int(C.astype(np.int64).sum(axis=0).max(initial=0)) * e
+    if in_slab is None:
+        in_slab = max(16, (rows + 15) // 16 * 16)
+    if tgt_slab is None:
+        tgt_slab = max(16, (cols + 15) // 16 * 16)
+    if S is None:
+        S = max(1, core_num if core_num < P else (core_num // P) * P)
+    return Workload(name, name, P, dtype, core_num, S, in_slab, tgt_slab, C, seed)
+
+
+# ---------------------------------------------------------------- buffers
+
+def input_bytes_np(w: Workload) -> np.ndarray:
+    """The whole input allocation as uint8 numpy (host)."""
+    if w.routing is None:
+        return random_bytes_np(w.payload_seed, 0, w.in_bytes)
+    return _moe_input(w, np)
+
+
+def input_tensor(w: Workload, device):
+    """The whole input allocation as a flat uint8 torch tensor on ``device``."""
+    import torch
+    t = torch.empty(w.in_bytes, dtype=torch.uint8, device=device)
+    if w.routing is None:
+        fill_random_(t, w.payload_seed)
+        return t
+    tok = torch.empty(w.P * w.routing.shape[1] * w.token_bytes, dtype=torch.uint8, device=device)
+    fill_random_(tok, w.payload_seed)
+    tok = tok.view(w.P, w.routing.shape[1], w.token_bytes)
+    slabs = t.view(w.P, w.in_slab)
+    for s in range(w.P):
+        pos = 0
+        for d in range(w.P):
+            idx = np.nonzero(w.routing[s, :, d])[0]
+            n = idx.size * w.token_bytes
+            if n:
+                src = tok[s].index_select(0, torch.as_tensor(idx, device=device))
+                slabs[s, pos:pos + n].copy_(src.reshape(-1))
+            pos += n
+        if pos < w.in_slab:
+            slabs[s, pos:].fill_(0)
+    return t
+
+
+def _moe_input(w: Workload, xp) -> np.ndarray:
+    tokens = w.routing.shape[1]
+    tok = random_bytes_np(w.payload_seed, 0, w.P * tokens * w.token_bytes)
+    tok = tok.reshape(w.P, tokens, w.token_bytes)
+    out = np.zeros((w.P, w.in_slab), np.uint8)
+    for s in range(w.P):
+        pos = 0
+        for d in range(w.P):
+            idx = np.nonzero(w.routing[s, :, d])[0]
+            n = idx.size * w.token_bytes
+            out[s, pos:pos + n] = tok[s, idx].reshape(-1)
+            pos += n
+    return out.reshape(-1)
+
+
+def target_np(w: Workload) -> np.ndarray:
+    return np.full(w.tgt_bytes, SENTINEL, np.uint8)
+
+
+def signal_np(w: Workload) -> np.ndarray:
+    return np.zeros((w.P, w.S), np.int32)

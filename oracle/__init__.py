@@ -1,0 +1,137 @@
+"""CPU oracle for the variable-count all-to-all exchange (all_to_all_v).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The product path (the
+HIP library and its Python binding) never imports, links or calls it, and it
+imports nothing from the product path: the two share no code.
+
+Two independent implementations live here:
+
+* ``liba2av_oracle.so`` (``a2av_oracle.c``): plain C loops, one ``memcpy`` per
+  (source, destination) segment, its own argument checks, its own prefix sums.
+* :mod:`oracle.brute`: a pure-Python brute force for tiny P that builds each
+  destination slab by concatenating byte strings.
+
+Semantics follow the five-operand ``all_to_all_v(input, target, signal,
+send_counts, recv_counts, core_num)`` of the PyPTO "LowerL2TensorCollectives
+Pass" page (section "Behavior"); segment addressing follows the ncclx
+``ctranAllToAllvIbImpl`` pseudocode on the "vccl alltoallv dev log" page
+(section 5).  Parity status per function is stated in ``a2av_oracle.c``; the
+signal's +1-per-exchange value is "parity unpinned" (the pages do not fix it).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "a2av_oracle.c")
+_LIB = os.path.join(_HERE, "liba2av_oracle.so")
+
+OK = 0
+ERR_NULLPTR = 1
+ERR_INVALID_ARGS = 2
+ERR_UNSUPPORTED_DTYPE = 3
+ERR_OVER_CAPACITY = 4
+ERR_LAUNCH_CAPACITY = 5
+
+FP32 = 0
+INT8 = 1
+ELEM_SIZE = {FP32: 4, INT8: 1}
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``oracle/liba2av_oracle.so``."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-shared", "-fPIC",
+             "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        L.a2av_oracle_blocks.argtypes = [i64, i64]
+        L.a2av_oracle_blocks.restype = i64
+        run_args = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i64]
+        L.a2av_oracle_run.argtypes = run_args
+        L.a2av_oracle_run.restype = ctypes.c_int
+        L.a2av_oracle_check.argtypes = run_args
+        L.a2av_oracle_check.restype = ctypes.c_int
+        L.a2av_oracle_displacements.argtypes = [vp, i32, i32, vp, vp]
+        L.a2av_oracle_displacements.restype = None
+        L.a2av_oracle_move.argtypes = [vp, vp, vp, i32, i32, i64, i64]
+        L.a2av_oracle_move.restype = None
+        _lib = L
+    return _lib
+
+
+def blocks(P: int, L: int) -> int:
+    """CalAllToAllVBlocks(P, L) as the oracle computes it (-1 on bad input)."""
+    return int(lib().a2av_oracle_blocks(P, L))
+
+
+def _ptr(a: np.ndarray | None) -> int | None:
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def run(input_bytes: np.ndarray, target_bytes: np.ndarray, signal: np.ndarray,
+        send_counts: np.ndarray, recv_counts: np.ndarray, *, P: int, S: int,
+        in_slab: int, tgt_slab: int, core_num: int, dtype: int,
+        capacity: int = 0) -> int:
+    """Run the exchange in place on host numpy buffers; returns a status.
+
+    ``input_bytes`` / ``target_bytes`` are flat uint8 arrays of ``P*in_slab`` /
+    ``P*tgt_slab`` bytes; ``signal`` is int32 ``[P, S]``; counts are int32
+    ``[P, P]``.  On error nothing is written.
+    """
+    for a, n in ((input_bytes, P * in_slab), (target_bytes, P * tgt_slab)):
+        assert a.dtype == np.uint8 and a.size == n
+    assert signal.dtype == np.int32 and signal.size == P * S
+    assert send_counts.dtype == np.int32 and send_counts.size == P * P
+    assert recv_counts.dtype == np.int32 and recv_counts.size == P * P
+    return int(lib().a2av_oracle_run(
+        _ptr(input_bytes), _ptr(target_bytes), _ptr(signal), _ptr(send_counts),
+        _ptr(recv_counts), P, S, in_slab, tgt_slab, core_num, dtype, capacity))
+
+
+def check(input_ptr, target_ptr, signal_ptr, send_ptr, recv_ptr, *, P, S, in_slab,
+          tgt_slab, core_num, dtype, capacity=0, send_counts=None, signal=None) -> int:
+    """Argument checks only, on raw addresses (counts/signal read when given)."""
+    return int(lib().a2av_oracle_check(
+        input_ptr, target_ptr, signal_ptr, send_ptr, recv_ptr, P, S, in_slab, tgt_slab,
+        core_num, dtype, capacity))
+
+
+def displacements(send_counts: np.ndarray, dtype: int) -> tuple[np.ndarray, np.ndarray]:
+    """(sdispl[s][d], rdispl[d][s]) in bytes, int64 [P, P] each."""
+    C = np.ascontiguousarray(send_counts, dtype=np.int32)
+    P = C.shape[0]
+    sd = np.zeros((P, P), np.int64)
+    rd = np.zeros((P, P), np.int64)
+    lib().a2av_oracle_displacements(_ptr(C), P, dtype, _ptr(sd), _ptr(rd))
+    return sd, rd
+
+
+def move(input_bytes: np.ndarray, target_bytes: np.ndarray, send_counts: np.ndarray, *,
+         P: int, dtype: int, in_slab: int, tgt_slab: int) -> None:
+    """The segment-copy step alone (no checks); counts must be valid."""
+    C = np.ascontiguousarray(send_counts, dtype=np.int32)
+    lib().a2av_oracle_move(_ptr(input_bytes), _ptr(target_bytes), _ptr(C), P, dtype,
+                           in_slab, tgt_slab)

@@ -1,0 +1,301 @@
+/*
+ * a2av_oracle.c -- plain CPU oracle for the variable-count all-to-all exchange.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file: only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header, helper or
+ * table with the HIP library; the only thing the two agree on is the numeric
+ * value of each status code, because both report to the same callers.
+ *
+ * What it computes (the op of the PyPTO "LowerL2TensorCollectives Pass" page,
+ * section "Behavior": all_to_all_v(input, target, signal, send_counts,
+ * recv_counts, core_num)), with P virtual ranks laid out as slabs of one
+ * allocation:
+ *
+ *   input   P slabs of in_slab bytes, slab s packed by destination d = 0..P-1
+ *   target  P slabs of tgt_slab bytes, slab d packed by source s = 0..P-1
+ *   signal  [P, S] int32
+ *   send_counts [P, P] int32, element counts, send_counts[s][d] = s -> d
+ *   recv_counts [P, P] int32, written: recv_counts[d][s] = send_counts[s][d]
+ *
+ * The segment addressing follows the ncclx ctranAllToAllvIbImpl pseudocode on
+ * the "vccl alltoallv dev log" page (section 5, "ref / meta ncclx"): the send
+ * buffer of peer d starts at sendbuff + sDispls[d] * typeSize, the receive
+ * buffer of peer s at recvbuff + rDispls[s] * typeSize, and sendCounts[d] *
+ * typeSize bytes move.  The displacements are the exclusive prefix sums of the
+ * counts (no displacement operand exists in the five-operand statement).
+ *
+ * Parity status of every function here is recorded at its definition.  There
+ * is no floating-point arithmetic: payload moves as raw bytes.
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+
+/* Status values (same numbers as the library reports). */
+#define OR_OK 0
+#define OR_ERR_NULLPTR 1
+#define OR_ERR_INVALID_ARGS 2
+#define OR_ERR_UNSUPPORTED_DTYPE 3
+#define OR_ERR_OVER_CAPACITY 4
+#define OR_ERR_LAUNCH_CAPACITY 5
+
+#define OR_DTYPE_FP32 0
+#define OR_DTYPE_INT8 1
+
+#define OR_MAX_P 64
+#define OR_INT32_MAX 2147483647LL
+
+/*
+ * CalAllToAllVBlocks(P, L): the admitted block count.  "Launch width" section
+ * of the LowerL2TensorCollectives page: B = L when L < P, otherwise the
+ * largest multiple of P that does not exceed L.  Written as the definition
+ * (search downward from L for the first multiple of P), not as a division.
+ * Returns -1 when P < 1 or L < 1.
+ * Pinned by: the page's printed case L=10, P=8 -> 8, the rule L<P -> L, and a
+ * brute-force enumeration of multiples in the tests.
+ */
+int64_t a2av_oracle_blocks(int64_t P, int64_t L)
+{
+    if (P < 1 || L < 1)
+        return -1;
+    if (L < P)
+        return L;
+    for (int64_t m = L; m >= P; --m)
+        if (m % P == 0)
+            return m;
+    return -1; /* unreachable: P itself is a multiple of P and P <= L */
+}
+
+static int64_t elem_size(int32_t dtype)
+{
+    return dtype == OR_DTYPE_FP32 ? 4 : 1;
+}
+
+/* Half-open byte ranges [a, a+na) and [b, b+nb) share at least one byte. */
+static int ranges_overlap(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb)
+{
+    if (na == 0 || nb == 0)
+        return 0;
+    return a < b + nb && b < a + na;
+}
+
+/*
+ * The argument checks, in this order (the first failing one is reported and
+ * nothing is written):
+ *   1. a null operand                                   -> NULLPTR
+ *   2. dtype not FP32 / INT8 ("Constraints and diagnostics": the supported
+ *      dtypes)                                          -> UNSUPPORTED_DTYPE
+ *   3. P outside [1, 64], S < 1, a slab size < 1        -> INVALID_ARGS
+ *   4. core_num outside [1, INT32_MAX] (same section)   -> INVALID_ARGS
+ *   5. signal stride S < B, B the folded block count    -> INVALID_ARGS
+ *   6. B > 1 and B above the co-resident capacity (all admitted blocks must be
+ *      resident at once; an over-capacity sync-start launch is refused, not
+ *      partially launched; "Launch width")              -> LAUNCH_CAPACITY
+ *      (capacity <= 0 means "no limit"; the GPU's limit is a device property)
+ *   7. any two of the five operands share a byte (the pairwise-distinct window
+ *      rule of "Current limitations")                   -> INVALID_ARGS
+ *   8. a slab size that is not a whole number of elements -> INVALID_ARGS
+ *   9. a negative count                                 -> INVALID_ARGS
+ *  10. a source row or destination column whose bytes exceed its slab
+ *                                                       -> OVER_CAPACITY
+ *  11. signal[r][b] (r < P, b < B) not all equal        -> INVALID_ARGS
+ * Checks 9-11 are this implementation's reading of the count-matrix cases
+ * the page's system test names (0 / 1 / capacity / over-capacity / negative)
+ * and of the barrier's need for a common starting value.
+ */
+static int check_args(const void *input, const void *target, const int32_t *signal,
+                      const int32_t *send_counts, const int32_t *recv_counts,
+                      int32_t P, int32_t S, int64_t in_slab, int64_t tgt_slab,
+                      int64_t core_num, int32_t dtype, int64_t capacity)
+{
+    if (!input || !target || !signal || !send_counts || !recv_counts)
+        return OR_ERR_NULLPTR;
+    if (dtype != OR_DTYPE_FP32 && dtype != OR_DTYPE_INT8)
+        return OR_ERR_UNSUPPORTED_DTYPE;
+    if (P < 1 || P > OR_MAX_P || S < 1 || in_slab < 1 || tgt_slab < 1)
+        return OR_ERR_INVALID_ARGS;
+    if (core_num < 1 || core_num > OR_INT32_MAX)
+        return OR_ERR_INVALID_ARGS;
+    int64_t B = a2av_oracle_blocks(P, core_num);
+    if ((int64_t)S < B)
+        return OR_ERR_INVALID_ARGS;
+    if (B > 1 && capacity > 0 && B > capacity)
+        return OR_ERR_LAUNCH_CAPACITY;
+
+    uintptr_t base[5] = {(uintptr_t)input, (uintptr_t)target, (uintptr_t)signal,
+                         (uintptr_t)send_counts, (uintptr_t)recv_counts};
+    uint64_t len[5] = {(uint64_t)P * (uint64_t)in_slab, (uint64_t)P * (uint64_t)tgt_slab,
+                       (uint64_t)P * (uint64_t)S * 4u, (uint64_t)P * (uint64_t)P * 4u,
+                       (uint64_t)P * (uint64_t)P * 4u};
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (ranges_overlap(base[i], len[i], base[j], len[j]))
+                return OR_ERR_INVALID_ARGS;
+
+    int64_t e = elem_size(dtype);
+    if (in_slab % e != 0 || tgt_slab % e != 0)
+        return OR_ERR_INVALID_ARGS;
+
+    for (int32_t s = 0; s < P; ++s)
+        for (int32_t d = 0; d < P; ++d)
+            if (send_counts[s * P + d] < 0)
+                return OR_ERR_INVALID_ARGS;
+
+    for (int32_t s = 0; s < P; ++s) {
+        int64_t row = 0;
+        for (int32_t d = 0; d < P; ++d)
+            row += (int64_t)send_counts[s * P + d];
+        if (row * e > in_slab)
+            return OR_ERR_OVER_CAPACITY;
+    }
+    for (int32_t d = 0; d < P; ++d) {
+        int64_t col = 0;
+        for (int32_t s = 0; s < P; ++s)
+            col += (int64_t)send_counts[s * P + d];
+        if (col * e > tgt_slab)
+            return OR_ERR_OVER_CAPACITY;
+    }
+
+    int32_t first = signal[0];
+    for (int32_t r = 0; r < P; ++r)
+        for (int64_t b = 0; b < B; ++b)
+            if (signal[(int64_t)r * S + b] != first)
+                return OR_ERR_INVALID_ARGS;
+    return OR_OK;
+}
+
+/* Argument checks alone (used by the tests to pin each diagnostic). */
+int a2av_oracle_check(const void *input, const void *target, const int32_t *signal,
+                      const int32_t *send_counts, const int32_t *recv_counts,
+                      int32_t P, int32_t S, int64_t in_slab, int64_t tgt_slab,
+                      int64_t core_num, int32_t dtype, int64_t capacity)
+{
+    return check_args(input, target, signal, send_counts, recv_counts, P, S, in_slab,
+                      tgt_slab, core_num, dtype, capacity);
+}
+
+/*
+ * Step 2: recv_counts[d][s] = send_counts[s][d].  Each destination learns how
+ * much every source sends it: the count matrix transposed.
+ * Pinned by: closed form (numpy transpose) in the tests.
+ */
+static void transpose_counts(const int32_t *send_counts, int32_t *recv_counts, int32_t P)
+{
+    for (int32_t s = 0; s < P; ++s)
+        for (int32_t d = 0; d < P; ++d)
+            recv_counts[d * P + s] = send_counts[s * P + d];
+}
+
+/*
+ * Step 3: byte displacements, the exclusive prefix sums of the counts.
+ *   sdispl[s][d] = sum over d' < d of send_counts[s][d'] * e  (send side)
+ *   rdispl[d][s] = sum over s' < s of send_counts[s'][d] * e  (receive side)
+ * Pinned by: closed form (numpy exclusive cumsum) in the tests.
+ */
+static void displacements(const int32_t *C, int32_t P, int64_t e,
+                          int64_t *sdispl, int64_t *rdispl)
+{
+    for (int32_t s = 0; s < P; ++s) {
+        int64_t off = 0;
+        for (int32_t d = 0; d < P; ++d) {
+            sdispl[s * P + d] = off;
+            off += (int64_t)C[s * P + d] * e;
+        }
+    }
+    for (int32_t d = 0; d < P; ++d) {
+        int64_t off = 0;
+        for (int32_t s = 0; s < P; ++s) {
+            rdispl[d * P + s] = off;
+            off += (int64_t)C[s * P + d] * e;
+        }
+    }
+}
+
+/*
+ * Step 4, the payload move, one memcpy per (source, destination) segment:
+ *   target[d*tgt_slab + rdispl[d][s] .. + C[s][d]*e) =
+ *   input [s*in_slab  + sdispl[s][d] .. + C[s][d]*e)
+ * Bytes of a target slab past its received total are left as they were.
+ * Pinned by: brute force (per-slab byte concatenation) on every count matrix
+ * in {0,1,2}^(2x2) and {0,1}^(3x3), the P=1 identity, the equal-count case
+ * reducing to a block transpose, and the round trip with transposed counts.
+ */
+static void move_segments(const uint8_t *input, uint8_t *target, const int32_t *C,
+                          int32_t P, int64_t e, int64_t in_slab, int64_t tgt_slab,
+                          const int64_t *sdispl, const int64_t *rdispl)
+{
+    for (int32_t s = 0; s < P; ++s)
+        for (int32_t d = 0; d < P; ++d) {
+            int64_t nbytes = (int64_t)C[s * P + d] * e;
+            if (nbytes == 0)
+                continue;
+            memcpy(target + (int64_t)d * tgt_slab + rdispl[d * P + s],
+                   input + (int64_t)s * in_slab + sdispl[s * P + d], (size_t)nbytes);
+        }
+}
+
+/*
+ * Step 5, the signal: every block b < B of every rank r < P arrives once, so
+ * signal[r][b] grows by one (32-bit wraparound); entries with b >= B are left
+ * alone.  The pages fix only that the signal is [NR, S] with S >= B and that
+ * reusing it orders exchanges; the +1-per-exchange value is this
+ * implementation's reading of the per-peer sequence-counter barrier on the
+ * "vccl alltoallv dev log" page (section 6.1).  Parity unpinned by the pages:
+ * the tests check this definition, nothing more.
+ */
+static void arrive(int32_t *signal, int32_t P, int32_t S, int64_t B)
+{
+    for (int32_t r = 0; r < P; ++r)
+        for (int64_t b = 0; b < B; ++b) {
+            uint32_t v = (uint32_t)signal[(int64_t)r * S + b];
+            signal[(int64_t)r * S + b] = (int32_t)(v + 1u);
+        }
+}
+
+/*
+ * The whole exchange on host buffers.  Returns a status; on any error no
+ * output byte changes.  capacity <= 0 disables the co-resident check.
+ */
+int a2av_oracle_run(const void *input, void *target, int32_t *signal,
+                    const int32_t *send_counts, int32_t *recv_counts,
+                    int32_t P, int32_t S, int64_t in_slab, int64_t tgt_slab,
+                    int64_t core_num, int32_t dtype, int64_t capacity)
+{
+    int st = check_args(input, target, signal, send_counts, recv_counts, P, S, in_slab,
+                        tgt_slab, core_num, dtype, capacity);
+    if (st != OR_OK)
+        return st;
+    int64_t e = elem_size(dtype);
+    int64_t B = a2av_oracle_blocks(P, core_num);
+    int64_t sdispl[OR_MAX_P * OR_MAX_P];
+    int64_t rdispl[OR_MAX_P * OR_MAX_P];
+    transpose_counts(send_counts, recv_counts, P);
+    displacements(send_counts, P, e, sdispl, rdispl);
+    move_segments((const uint8_t *)input, (uint8_t *)target, send_counts, P, e, in_slab,
+                  tgt_slab, sdispl, rdispl);
+    arrive(signal, P, S, B);
+    return OR_OK;
+}
+
+/* Displacements alone, for the closed-form pins (no checks). */
+void a2av_oracle_displacements(const int32_t *send_counts, int32_t P, int32_t dtype,
+                               int64_t *sdispl, int64_t *rdispl)
+{
+    displacements(send_counts, P, elem_size(dtype), sdispl, rdispl);
+}
+
+/*
+ * The segment-copy step alone on prepared buffers (no checks, counts assumed
+ * valid): the loop the benchmark times as the CPU baseline.
+ */
+void a2av_oracle_move(const void *input, void *target, const int32_t *send_counts,
+                      int32_t P, int32_t dtype, int64_t in_slab, int64_t tgt_slab)
+{
+    int64_t e = elem_size(dtype);
+    int64_t sdispl[OR_MAX_P * OR_MAX_P];
+    int64_t rdispl[OR_MAX_P * OR_MAX_P];
+    displacements(send_counts, P, e, sdispl, rdispl);
+    move_segments((const uint8_t *)input, (uint8_t *)target, send_counts, P, e, in_slab,
+                  tgt_slab, sdispl, rdispl);
+}
