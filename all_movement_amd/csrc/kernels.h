@@ -1,0 +1,67 @@
+// kernels.h -- device-side data shared by the count kernel (K1) and the
+// segment-copy kernel (K2), and their launch parameters.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace a2av {
+
+// Words written by K1 for one run and read by every K2 launch of that run.
+struct alignas(64) RunPlan {
+  int32_t valid;        // 1 when the run's counts and signal passed the device checks
+  int32_t base_signal;  // common value of signal[r][b] (r < P, b < B) at entry
+  int64_t total_bytes;  // payload bytes T of the run
+  uint32_t arrived;     // admitted blocks that have raised their flags
+  int32_t error;        // latched status (first failure since the last query)
+};
+
+// Device workspace layout, carved out of one allocation by the host.
+struct Workspace {
+  RunPlan* plan;
+  int64_t* prefix;   // [P*P + 1] exclusive prefix of segment bytes, s-major order
+  int64_t* src_off;  // [P*P] byte offset of segment (s, d) inside `input`
+  int64_t* dst_off;  // [P*P] byte offset of segment (s, d) inside `target`
+  uint32_t* blk_cnt; // [max blocks] workgroups of each block that finished copying
+};
+
+struct CountParams {
+  const int32_t* send_counts;
+  int32_t* recv_counts;
+  const int32_t* signal;
+  Workspace ws;
+  int64_t in_slab;
+  int64_t tgt_slab;
+  int32_t P;
+  int32_t S;
+  int32_t B;
+  int32_t elem;
+};
+
+struct CopyParams {
+  const uint8_t* input;
+  uint8_t* target;
+  int32_t* signal;
+  Workspace ws;
+  int64_t chunk_lo;   // flattened payload range of this launch (clamped to T on device)
+  int64_t chunk_hi;
+  int32_t nseg;       // P*P
+  int32_t P;
+  int32_t S;
+  int32_t B;
+  int32_t G;          // workgroups per admitted block
+  int32_t last;       // 1 on the run's final launch: raise the block flags
+  int32_t wait;       // 1 when the final launch is cooperative (B > 1): wait for all blocks
+  int32_t spin_limit;
+};
+
+constexpr int kCountThreads = 1024;
+constexpr int kCopyThreads = 1024;
+
+// Launch helpers (defined in kernels.hip).
+hipError_t launch_count(const CountParams& p, hipStream_t stream);
+hipError_t launch_copy(const CopyParams& p, int workgroups, bool cooperative, hipStream_t stream);
+hipError_t copy_occupancy(int* wgs_per_cu);
+
+}  // namespace a2av

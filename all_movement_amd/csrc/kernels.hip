@@ -1,0 +1,410 @@
+// kernels.hip -- the two gfx950 kernels of the all_to_all_v exchange.
+//
+// K1 (count_kernel, one 1024-thread workgroup): checks the count matrix and
+// the signal on the device, writes recv_counts as the transpose of
+// send_counts, and derives every segment's source and target byte offsets
+// with wave64 exclusive scans (send side along d, receive side along s, and
+// the flattened s-major payload prefix that K2 partitions).
+//
+// K2 (copy_kernel, W = B * G workgroups): each workgroup copies one
+// contiguous share of the flattened payload.  Inside a segment the copy is
+// destination-aligned: 128-bit nontemporal loads and stores in the body,
+// byte stores for the at most 15 bytes at either end, so no byte outside a
+// segment is ever written.  When source and destination are not congruent
+// mod 16 the body is realigned through LDS: each wave stages 64 aligned
+// source words plus one, then every lane funnels its word and its
+// neighbour's with v_alignbyte.  On the run's final launch every admitted
+// block raises its flag in every rank's signal row, and when B > 1 (a
+// cooperative launch) every workgroup waits, with a bounded spin, until all
+// B blocks have arrived.  The block/flag protocol is the block-aware
+// exchange barrier of the PyPTO "LowerL2TensorCollectives Pass" page
+// ("Launch width": all admitted blocks co-resident; a refused launch rather
+// than a partial one) with per-peer sequence counters as in the start
+// barrier of the "vccl alltoallv dev log" page (section 6.1).
+#include "a2av.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace a2av {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kUnroll = 8;          // 16-byte words in flight per lane
+constexpr int64_t kTileBytes = 16384; // flattened payload bytes per wave task
+
+// ------------------------------------------------------------------ K1
+
+__device__ inline int64_t wave_inclusive_scan(int64_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t y = __shfl_up(v, o, kWave);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
+  __shared__ int32_t C[kMaxP * kMaxP];
+  __shared__ int64_t rowsum[kMaxP];
+  __shared__ int64_t colsum[kMaxP];
+  __shared__ int64_t rowbase[kMaxP + 1];
+  __shared__ int flags;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  constexpr int kWaves = kCountThreads / kWave;
+  const int P = p.P;
+  const int PP = P * P;
+
+  if (tid == 0) flags = 0;
+  __syncthreads();
+
+  // Load the counts; note negatives (bit 0) and a signal that is not uniform
+  // over the admitted entries (bit 2).
+  int bad = 0;
+  for (int i = tid; i < PP; i += kCountThreads) {
+    const int32_t c = p.send_counts[i];
+    C[i] = c;
+    if (c < 0) bad |= 1;
+  }
+  const int32_t base = p.signal[0];
+  const int nsig = P * p.B;
+  for (int j = tid; j < nsig; j += kCountThreads) {
+    const int r = j / p.B;
+    const int b = j - r * p.B;
+    if (p.signal[int64_t(r) * p.S + b] != base) bad |= 4;
+  }
+  if (bad) atomicOr(&flags, bad);
+  __syncthreads();
+
+  // Row sums (what each source sends) and column sums (what each destination
+  // receives), one wave per row or column.
+  for (int s = wave; s < P; s += kWaves) {
+    const int64_t v = lane < P ? int64_t(C[s * P + lane]) : 0;
+    const int64_t t = wave_inclusive_scan(v, lane);
+    if (lane == kWave - 1) rowsum[s] = t;
+  }
+  for (int d = wave; d < P; d += kWaves) {
+    const int64_t v = lane < P ? int64_t(C[lane * P + d]) : 0;
+    const int64_t t = wave_inclusive_scan(v, lane);
+    if (lane == kWave - 1) colsum[d] = t;
+  }
+  __syncthreads();
+  if (tid < P) {
+    if (rowsum[tid] * p.elem > p.in_slab || colsum[tid] * p.elem > p.tgt_slab)
+      atomicOr(&flags, 2);
+  }
+  __syncthreads();
+
+  const int f = flags;
+  if (f != 0) {
+    if (tid == 0) {
+      const int code = (f & 1) ? A2AV_ERR_INVALID_ARGS
+                     : (f & 2) ? A2AV_ERR_OVER_CAPACITY
+                               : A2AV_ERR_INVALID_ARGS;
+      atomicCAS(&p.ws.plan->error, 0, code);
+      p.ws.plan->valid = 0;
+    }
+    return;
+  }
+
+  // Flattened payload order is s-major: segment i = s*P + d.  Row bases are
+  // the exclusive scan of the row byte totals; lane 63 ends with T.
+  if (wave == 0) {
+    const int64_t v = lane < P ? rowsum[lane] * p.elem : 0;
+    const int64_t incl = wave_inclusive_scan(v, lane);
+    if (lane < P) rowbase[lane] = incl - v;
+    if (lane == kWave - 1) rowbase[kMaxP] = incl;
+  }
+  __syncthreads();
+
+  // Send side: exclusive scan along d of row s (input packed by destination).
+  for (int s = wave; s < P; s += kWaves) {
+    const int64_t v = lane < P ? int64_t(C[s * P + lane]) * p.elem : 0;
+    const int64_t ex = wave_inclusive_scan(v, lane) - v;
+    if (lane < P) {
+      p.ws.src_off[s * P + lane] = int64_t(s) * p.in_slab + ex;
+      p.ws.prefix[s * P + lane] = rowbase[s] + ex;
+    }
+  }
+  // Receive side: exclusive scan along s of column d (target packed by source).
+  for (int d = wave; d < P; d += kWaves) {
+    const int64_t v = lane < P ? int64_t(C[lane * P + d]) * p.elem : 0;
+    const int64_t ex = wave_inclusive_scan(v, lane) - v;
+    if (lane < P) p.ws.dst_off[lane * P + d] = int64_t(d) * p.tgt_slab + ex;
+  }
+  // recv_counts[d][s] = send_counts[s][d].
+  for (int i = tid; i < PP; i += kCountThreads) {
+    const int d = i / P;
+    const int s = i - d * P;
+    p.recv_counts[i] = C[s * P + d];
+  }
+  for (int b = tid; b < p.B; b += kCountThreads) p.ws.blk_cnt[b] = 0u;
+  if (tid == 0) {
+    p.ws.prefix[PP] = rowbase[kMaxP];
+    p.ws.plan->total_bytes = rowbase[kMaxP];
+    p.ws.plan->base_signal = base;
+    p.ws.plan->arrived = 0u;
+    p.ws.plan->valid = 1;
+  }
+}
+
+// ------------------------------------------------------------------ K2
+
+// Output word = bytes [phi, phi+16) of the 32 bytes a:b, phi = 4*Q + r.
+template <int Q>
+__device__ inline u32x4 funnel(u32x4 a, u32x4 b, uint32_t r) {
+  const uint32_t c[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  u32x4 o;
+  o.x = __builtin_amdgcn_alignbyte(c[Q + 1], c[Q + 0], r);
+  o.y = __builtin_amdgcn_alignbyte(c[Q + 2], c[Q + 1], r);
+  o.z = __builtin_amdgcn_alignbyte(c[Q + 3], c[Q + 2], r);
+  o.w = __builtin_amdgcn_alignbyte(c[Q + 4], c[Q + 3], r);
+  return o;
+}
+
+// Body with source and destination both 16-byte aligned: K words, one wave.
+__device__ inline void wave_copy_aligned(const u32x4* __restrict__ s, u32x4* __restrict__ d,
+                                         int64_t K, int lane) {
+  int64_t k0 = 0;
+  for (; k0 + kWave * kUnroll <= K; k0 += kWave * kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) v[j] = __builtin_nontemporal_load(s + k0 + j * kWave + lane);
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) __builtin_nontemporal_store(v[j], d + k0 + j * kWave + lane);
+  }
+  for (int64_t k = k0 + lane; k < K; k += kWave)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(s + k), d + k);
+}
+
+// Body whose source sits phi = 4*Q + r bytes (1..15) past a 16-byte boundary:
+// output word k is bytes [phi, phi+16) of aligned source words A[k], A[k+1].
+// Words A[0..K] all hold body bytes, so every load stays inside 16-byte words
+// that the segment touches.  The wave works on rows of 64 consecutive source
+// words that overlap by one: lane l of row q loads A[63q + l] and lanes 0..62
+// emit outputs 63q + l, taking the right neighbour's word from the wave's
+// LDS slot (1 KiB per wave, reused row after row).
+template <int Q>
+__device__ void wave_copy_realign(const u32x4* __restrict__ A, u32x4* __restrict__ D, int64_t K,
+                                  uint32_t r, u32x4* slot, int lane) {
+  constexpr int kRow = kWave - 1;
+  const int64_t nrows = (K + kRow - 1) / kRow;
+  for (int64_t r0 = 0; r0 < nrows; r0 += kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t k = (r0 + j) * kRow + lane;
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (r0 + j < nrows && k <= K) v[j] = __builtin_nontemporal_load(A + k);
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t k = (r0 + j) * kRow + lane;
+      slot[lane] = v[j];
+      // Lanes read a word another lane wrote: keep the compiler from moving
+      // LDS accesses across these points (a wave's LDS operations run in order).
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const u32x4 hi = slot[(lane + 1) & (kWave - 1)];
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if (r0 + j < nrows && lane < kRow && k < K)
+        __builtin_nontemporal_store(funnel<Q>(v[j], hi, r), D + k);
+    }
+  }
+}
+
+// Copy n bytes src -> dst (one piece of one segment) with one wave.  The
+// destination body is whole aligned 16-byte words; the at most 15 bytes on
+// either side are written one byte per lane, so no byte outside the piece is
+// ever stored.
+__device__ void wave_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int lane,
+                                u32x4* slot) {
+  const uintptr_t d0 = uintptr_t(dst);
+  const uintptr_t body_lo = (d0 + 15u) & ~uintptr_t(15);
+  const uintptr_t body_hi = (d0 + uintptr_t(n)) & ~uintptr_t(15);
+  if (body_lo >= body_hi) {
+    for (int64_t k = lane; k < n; k += kWave) dst[k] = src[k];
+    return;
+  }
+  const int64_t head = int64_t(body_lo - d0);
+  const int64_t tail_at = int64_t(body_hi - d0);
+  const int64_t tail = n - tail_at;
+  if (lane < head) dst[lane] = src[lane];
+  if (lane >= 16 && lane - 16 < tail) dst[tail_at + lane - 16] = src[tail_at + lane - 16];
+
+  // Pointers keep their provenance (no integer-to-pointer casts) so the
+  // compiler emits global, not flat, memory instructions.
+  const uint8_t* sb = src + head;
+  const int64_t K = int64_t(body_hi - body_lo) >> 4;
+  const uint32_t phi = uint32_t(uintptr_t(sb) & 15u);
+  u32x4* D = reinterpret_cast<u32x4*>(dst + head);
+  if (phi == 0) {
+    wave_copy_aligned(reinterpret_cast<const u32x4*>(sb), D, K, lane);
+    return;
+  }
+  const u32x4* A = reinterpret_cast<const u32x4*>(sb - phi);
+  const uint32_t r = phi & 3u;
+  switch (phi >> 2) {
+    case 0: wave_copy_realign<0>(A, D, K, r, slot, lane); break;
+    case 1: wave_copy_realign<1>(A, D, K, r, slot, lane); break;
+    case 2: wave_copy_realign<2>(A, D, K, r, slot, lane); break;
+    default: wave_copy_realign<3>(A, D, K, r, slot, lane); break;
+  }
+}
+
+// Segment tables of one run, staged in LDS by every workgroup.
+struct SegTables {
+  int64_t prefix[kMaxP * kMaxP + 1];
+  int64_t src[kMaxP * kMaxP];
+  int64_t dst[kMaxP * kMaxP];
+};
+
+// Largest segment i in [0, nseg) with prefix[i] <= x (prefix[0] = 0 <= x):
+// a 64-ary search, one LDS probe per lane per level (two levels for 4096).
+__device__ inline int seg_of(const int64_t* prefix, int nseg, int64_t x, int lane) {
+  int lo = 0;
+  int n = nseg;
+  while (n > 1) {
+    const int step = (n + kWave - 1) / kWave;
+    const int off = lane * step;
+    const bool ok = off < n && prefix[lo + off] <= x;
+    const int h = __popcll(__ballot(ok)) - 1;  // probes are monotone: lanes 0..h hold
+    lo += h * step;
+    n = min(step, n - h * step);
+  }
+  return lo;
+}
+
+// A tile boundary x moved forward (never past its segment's end or c_hi) so
+// that the destination byte it maps to starts a 128-byte line: neighbouring
+// tiles then never share a destination line inside a segment.  Monotone in x.
+__device__ inline int64_t align_boundary(const SegTables& t, int nseg, const uint8_t* target,
+                                         int64_t x, int64_t c_hi, int lane) {
+  const int i = seg_of(t.prefix, nseg, x, lane);
+  const uintptr_t a = uintptr_t(target) + uintptr_t(t.dst[i] + (x - t.prefix[i]));
+  int64_t y = x + int64_t((0u - a) & 127u);
+  if (y > t.prefix[i + 1]) y = t.prefix[i + 1];
+  if (y > c_hi) y = c_hi;
+  return y;
+}
+
+// One K2 launch copies the flattened payload bytes [c_lo, c_hi) of the run.
+// The range is cut into 16 KiB tiles dealt round-robin to every wave of the
+// grid, so at any moment all waves stream through one narrow window of the
+// source and of the destination (measured on gfx950: contiguous per-workgroup
+// ranges that fan out to destination slabs 1 GiB apart ran at ~4.1 TB/s, the
+// same bytes as interleaved tiles at ~5.6 TB/s).
+template <int NT>
+__global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
+  constexpr int NW = NT / kWave;
+  __shared__ SegTables tab;
+  __shared__ u32x4 slots[NW][kWave];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  RunPlan* plan = p.ws.plan;
+  if (plan->valid == 0) return;  // the run failed its device checks: write nothing
+
+  const int64_t T = plan->total_bytes;
+  const int64_t c_lo = p.chunk_lo < T ? p.chunk_lo : T;
+  const int64_t c_hi = p.chunk_hi < T ? p.chunk_hi : T;
+  const int nseg = p.nseg;
+  for (int i = tid; i <= nseg; i += NT) tab.prefix[i] = p.ws.prefix[i];
+  for (int i = tid; i < nseg; i += NT) {
+    tab.src[i] = p.ws.src_off[i];
+    tab.dst[i] = p.ws.dst_off[i];
+  }
+  __syncthreads();
+
+  const int64_t ntiles = (c_hi - c_lo + kTileBytes - 1) / kTileBytes;
+  const int64_t waves = int64_t(gridDim.x) * NW;
+  for (int64_t t = int64_t(blockIdx.x) * NW + wave; t < ntiles; t += waves) {
+    const int64_t x0 = c_lo + t * kTileBytes;
+    const int64_t x1 = x0 + kTileBytes < c_hi ? x0 + kTileBytes : c_hi;
+    const int64_t a = t == 0 ? c_lo : align_boundary(tab, nseg, p.target, x0, c_hi, lane);
+    const int64_t b = x1 >= c_hi ? c_hi : align_boundary(tab, nseg, p.target, x1, c_hi, lane);
+    int64_t x = a;
+    int i = x < b ? seg_of(tab.prefix, nseg, x, lane) : 0;
+    while (x < b) {
+      const int64_t seg_hi = tab.prefix[i + 1];
+      if (seg_hi > x) {
+        const int64_t pe = b < seg_hi ? b : seg_hi;
+        const int64_t off = x - tab.prefix[i];
+        wave_copy_piece(p.input + tab.src[i] + off, p.target + tab.dst[i] + off, pe - x, lane,
+                        slots[wave]);
+        x = pe;
+      }
+      ++i;
+    }
+  }
+
+  if (!p.last) return;
+
+  // Arrival.  Each wave waits until its own stores are acknowledged (in its
+  // XCD's L2); then one release per workgroup writes that L2 back so every
+  // XCD sees the payload, and the last workgroup of block b raises
+  // signal[r][b] for every rank r and counts the block as arrived.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const int b = int(blockIdx.x) / p.G;
+    const uint32_t done =
+        __hip_atomic_fetch_add(&p.ws.blk_cnt[b], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == uint32_t(p.G - 1)) {
+      // Release: a reader that acquires a flag sees the block's payload.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      for (int r = 0; r < p.P; ++r)
+        __hip_atomic_fetch_add(&p.signal[int64_t(r) * p.S + b], 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&plan->arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (p.wait) {
+      // All admitted blocks are co-resident (cooperative launch); wait until
+      // every one has arrived.  Polls are relaxed device-scope loads (no
+      // cache invalidation per poll); one acquire follows the wait.  The wait
+      // is bounded: a lost arrival latches TIMEOUT instead of hanging.
+      int spins = 0;
+      while (__hip_atomic_load(&plan->arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+             uint32_t(p.B)) {
+        if (++spins > p.spin_limit) {
+          int expected = 0;
+          __hip_atomic_compare_exchange_strong(&plan->error, &expected, int(A2AV_ERR_TIMEOUT),
+                                               __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+  }
+  __syncthreads();
+}
+
+}  // namespace
+
+hipError_t launch_count(const CountParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(count_kernel, dim3(1), dim3(kCountThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const CopyParams& p, int workgroups, bool cooperative, hipStream_t stream) {
+  if (cooperative) {
+    void* args[] = {const_cast<CopyParams*>(&p)};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&copy_kernel<kCopyThreads>),
+                                      dim3(workgroups), dim3(kCopyThreads), args, 0, stream);
+  }
+  hipLaunchKernelGGL(copy_kernel<kCopyThreads>, dim3(workgroups), dim3(kCopyThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t copy_occupancy(int* wgs_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      wgs_per_cu, reinterpret_cast<const void*>(&copy_kernel<kCopyThreads>), kCopyThreads, 0);
+}
+
+}  // namespace a2av

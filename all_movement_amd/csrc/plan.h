@@ -1,0 +1,46 @@
+// plan.h -- host-side planning for the all_to_all_v library: the block fold,
+// the argument checks that run before anything is enqueued, the chunk plan
+// and the workgroups-per-block choice.  Pure C++ (no HIP calls).
+#pragma once
+
+#include <cstdint>
+
+#include "a2av.h"
+
+namespace a2av {
+
+constexpr int32_t kMaxP = 64;
+constexpr int64_t kDefaultChunkLimit = int64_t(1) << 30;
+constexpr int64_t kInt32Max = 2147483647LL;
+
+// CalAllToAllVBlocks(P, L) ("Launch width" section of the PyPTO
+// LowerL2TensorCollectives page): L below P stays L, otherwise the largest
+// multiple of P that does not exceed L.  -1 on P < 1 or L < 1.
+int64_t fold_blocks(int64_t P, int64_t L);
+
+int64_t elem_bytes(int32_t dtype);
+
+// Geometry checks done once by a2av_create.
+int check_config(const a2av_config* cfg);
+
+// The host-side checks of a2av_run, in the documented order.
+int check_run_args(const a2av_config* cfg, int64_t capacity, const void* input,
+                   const void* target, const int32_t* signal, const int32_t* send_counts,
+                   const int32_t* recv_counts, int32_t P, int64_t core_num, int32_t dtype);
+
+// Upper bound of the payload of any valid run: every row fits its input slab
+// and every column its target slab, so T <= P * min(in_slab, tgt_slab).
+int64_t max_payload(const a2av_config* cfg);
+
+// K2 launches per run: enough chunks of `limit` bytes to cover max_payload.
+// The device skips the part of a chunk past the run's real payload.
+int32_t chunk_launches(const a2av_config* cfg, int64_t limit);
+
+// Workgroups that execute one admitted block.  `requested` > 0 is taken as
+// is (clamped to the capacity); 0 picks enough to cover `target_wgs`
+// workgroups without giving any workgroup less than `min_bytes_per_wg` of the
+// payload bound, and never more than capacity / B.
+int32_t wg_per_block(int64_t B, int64_t capacity, int64_t payload_bound, int32_t requested,
+                     int64_t target_wgs, int64_t min_bytes_per_wg);
+
+}  // namespace a2av

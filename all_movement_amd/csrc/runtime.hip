@@ -1,0 +1,307 @@
+// runtime.hip -- the C ABI of include/a2av.h: handle lifetime, host checks,
+// the chunk plan, and the K1 + K2 launch sequence of one exchange.
+//
+// One run enqueues, on the caller's stream and without synchronizing:
+//   K1  count_kernel            (1 workgroup)       device checks, recv_counts,
+//                                                   segment offsets, payload prefix
+//   K2  copy_kernel x launches  (B*G workgroups)    launch c copies payload bytes
+//                                                   [c*limit, (c+1)*limit) of the
+//                                                   s-major flattened order
+// The number of K2 launches comes from the slab geometry (the payload bound
+// P * min(in_slab, tgt_slab)), so the host never reads the counts back; a
+// launch whose range lies past the run's payload does no copying.  Only the
+// final launch raises the signal flags, and it is cooperative when B > 1.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "a2av.h"
+#include "kernels.h"
+#include "plan.h"
+
+struct a2av_handle {
+  a2av_config cfg{};
+  int device = 0;
+  int cus = 0;
+  int wgs_per_cu = 0;
+  int64_t capacity = 0;      // co-resident copy workgroups
+  int64_t chunk_limit = 0;
+  int32_t launches = 1;
+  int32_t spin_limit = 0;
+  void* ws_mem = nullptr;
+  a2av::Workspace ws{};
+  hipStream_t last_stream = nullptr;
+  bool profile = false;
+  // Event sets of the last kProfileRuns runs: per run [0] before K1, [1] after
+  // K1, [2+c] after K2 launch c.
+  std::vector<hipEvent_t> events;
+  int32_t events_per_run = 0;
+  int64_t profiled_runs = 0;  // runs recorded since the last a2av_profile_read
+  int64_t run_counter = 0;
+  std::string last_error;
+};
+
+namespace {
+
+constexpr int64_t kTargetWgsPerCu = 1;         // auto G aims at this many workgroups per CU
+constexpr int64_t kMinBytesPerWg = 256 * 1024; // ... but no fewer payload bytes per workgroup
+constexpr int32_t kDefaultSpinLimit = 1 << 22;
+constexpr int64_t kProfileRuns = 256;           // runs whose event sets are kept
+
+class DeviceGuard {
+ public:
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev_) != hipSuccess) prev_ = -1;
+    if (prev_ != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev_ >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev_) (void)hipSetDevice(prev_);
+  }
+
+ private:
+  int prev_ = -1;
+};
+
+int hip_fail(a2av_handle* h, hipError_t e, const char* what) {
+  if (h) {
+    h->last_error = std::string(what) + ": " + hipGetErrorString(e);
+  }
+  return A2AV_ERR_HIP;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t a2av_blocks(int64_t P, int64_t L) { return a2av::fold_blocks(P, L); }
+
+const char* a2av_status_string(int status) {
+  switch (status) {
+    case A2AV_OK: return "A2AV_OK";
+    case A2AV_ERR_NULLPTR: return "A2AV_ERR_NULLPTR";
+    case A2AV_ERR_INVALID_ARGS: return "A2AV_ERR_INVALID_ARGS";
+    case A2AV_ERR_UNSUPPORTED_DTYPE: return "A2AV_ERR_UNSUPPORTED_DTYPE";
+    case A2AV_ERR_OVER_CAPACITY: return "A2AV_ERR_OVER_CAPACITY";
+    case A2AV_ERR_LAUNCH_CAPACITY: return "A2AV_ERR_LAUNCH_CAPACITY";
+    case A2AV_ERR_HIP: return "A2AV_ERR_HIP";
+    case A2AV_ERR_TIMEOUT: return "A2AV_ERR_TIMEOUT";
+    default: return "A2AV_ERR_UNKNOWN";
+  }
+}
+
+int a2av_check_args(const a2av_config* cfg, int64_t capacity, const void* input,
+                    const void* target, const int32_t* signal, const int32_t* send_counts,
+                    const int32_t* recv_counts, int32_t P, int64_t core_num, int32_t dtype) {
+  return a2av::check_run_args(cfg, capacity, input, target, signal, send_counts, recv_counts, P,
+                              core_num, dtype);
+}
+
+int a2av_create(a2av_handle** out, const a2av_config* cfg) {
+  if (!out || !cfg) return A2AV_ERR_NULLPTR;
+  *out = nullptr;
+  const int st = a2av::check_config(cfg);
+  if (st != A2AV_OK) return st;
+
+  a2av_handle* h = new (std::nothrow) a2av_handle();
+  if (!h) return A2AV_ERR_HIP;
+  h->cfg = *cfg;
+  h->device = cfg->device;
+  DeviceGuard guard(h->device);
+
+  hipError_t e = hipSetDevice(h->device);
+  if (e != hipSuccess) { delete h; return A2AV_ERR_HIP; }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, h->device);
+  if (e != hipSuccess) { delete h; return A2AV_ERR_HIP; }
+  h->cus = prop.multiProcessorCount;
+  e = a2av::copy_occupancy(&h->wgs_per_cu);
+  if (e != hipSuccess) { delete h; return A2AV_ERR_HIP; }
+  h->capacity = cfg->capacity_override > 0 ? cfg->capacity_override
+                                           : int64_t(h->wgs_per_cu) * h->cus;
+  h->chunk_limit = cfg->chunk_limit_bytes > 0 ? cfg->chunk_limit_bytes : a2av::kDefaultChunkLimit;
+  h->launches = a2av::chunk_launches(cfg, h->chunk_limit);
+  h->spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
+
+  // Workspace: plan words, prefix[P*P+1], src_off[P*P], dst_off[P*P],
+  // blk_cnt[max(1, capacity)], each 256-byte aligned.
+  const size_t PP = size_t(cfg->P) * size_t(cfg->P);
+  const size_t max_blocks = size_t(h->capacity > 1 ? h->capacity : 1);
+  size_t off = 0;
+  const size_t o_plan = off; off = round_up(off + sizeof(a2av::RunPlan), 256);
+  const size_t o_prefix = off; off = round_up(off + (PP + 1) * sizeof(int64_t), 256);
+  const size_t o_src = off; off = round_up(off + PP * sizeof(int64_t), 256);
+  const size_t o_dst = off; off = round_up(off + PP * sizeof(int64_t), 256);
+  const size_t o_cnt = off; off = round_up(off + max_blocks * sizeof(uint32_t), 256);
+  e = hipMalloc(&h->ws_mem, off);
+  if (e != hipSuccess) { delete h; return A2AV_ERR_HIP; }
+  e = hipMemset(h->ws_mem, 0, off);
+  if (e != hipSuccess) { (void)hipFree(h->ws_mem); delete h; return A2AV_ERR_HIP; }
+  char* base = static_cast<char*>(h->ws_mem);
+  h->ws.plan = reinterpret_cast<a2av::RunPlan*>(base + o_plan);
+  h->ws.prefix = reinterpret_cast<int64_t*>(base + o_prefix);
+  h->ws.src_off = reinterpret_cast<int64_t*>(base + o_src);
+  h->ws.dst_off = reinterpret_cast<int64_t*>(base + o_dst);
+  h->ws.blk_cnt = reinterpret_cast<uint32_t*>(base + o_cnt);
+
+  h->profile = (cfg->flags & A2AV_FLAG_PROFILE) != 0;
+  if (h->profile) {
+    h->events_per_run = h->launches + 2;
+    h->events.resize(size_t(h->events_per_run) * kProfileRuns, nullptr);
+    for (auto& ev : h->events) {
+      e = hipEventCreate(&ev);
+      if (e != hipSuccess) { a2av_destroy(h); return A2AV_ERR_HIP; }
+    }
+  }
+  *out = h;
+  return A2AV_OK;
+}
+
+int a2av_destroy(a2av_handle* h) {
+  if (!h) return A2AV_OK;
+  DeviceGuard guard(h->device);
+  (void)hipDeviceSynchronize();
+  for (auto& ev : h->events)
+    if (ev) (void)hipEventDestroy(ev);
+  if (h->ws_mem) (void)hipFree(h->ws_mem);
+  delete h;
+  return A2AV_OK;
+}
+
+int a2av_launch_info_get(a2av_handle* h, int64_t core_num, a2av_launch_info* out) {
+  if (!h || !out) return A2AV_ERR_NULLPTR;
+  if (core_num < 1 || core_num > a2av::kInt32Max) return A2AV_ERR_INVALID_ARGS;
+  const int64_t B = a2av::fold_blocks(h->cfg.P, core_num);
+  if (B > 1 && B > h->capacity) return A2AV_ERR_LAUNCH_CAPACITY;
+  const int32_t G = a2av::wg_per_block(B, h->capacity, a2av::max_payload(&h->cfg),
+                                       h->cfg.wg_per_block, kTargetWgsPerCu * h->cus,
+                                       kMinBytesPerWg);
+  std::memset(out, 0, sizeof(*out));
+  out->blocks = B;
+  out->wg_per_block = G;
+  out->workgroups = int32_t(B * G);
+  out->threads_per_wg = a2av::kCopyThreads;
+  out->chunk_launches = h->launches;
+  out->chunk_limit_bytes = h->chunk_limit;
+  out->capacity = h->capacity;
+  out->cooperative = B > 1 ? 1 : 0;
+  return A2AV_OK;
+}
+
+int a2av_run(a2av_handle* h, const void* input, void* target, int32_t* signal,
+             const int32_t* send_counts, int32_t* recv_counts, int32_t P, int64_t core_num,
+             int32_t dtype, void* stream) {
+  if (!h) return A2AV_ERR_NULLPTR;
+  int st = a2av::check_run_args(&h->cfg, h->capacity, input, target, signal, send_counts,
+                                recv_counts, P, core_num, dtype);
+  if (st != A2AV_OK) return st;
+  a2av_launch_info li;
+  st = a2av_launch_info_get(h, core_num, &li);
+  if (st != A2AV_OK) return st;
+
+  DeviceGuard guard(h->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  h->last_stream = s;
+  hipError_t e;
+
+  a2av::CountParams cp{};
+  cp.send_counts = send_counts;
+  cp.recv_counts = recv_counts;
+  cp.signal = signal;
+  cp.ws = h->ws;
+  cp.in_slab = h->cfg.in_slab_bytes;
+  cp.tgt_slab = h->cfg.tgt_slab_bytes;
+  cp.P = P;
+  cp.S = h->cfg.S;
+  cp.B = int32_t(li.blocks);
+  cp.elem = int32_t(a2av::elem_bytes(dtype));
+
+  hipEvent_t* ev = nullptr;
+  if (h->profile)
+    ev = &h->events[size_t(h->run_counter % kProfileRuns) * size_t(h->events_per_run)];
+  if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+  if ((e = a2av::launch_count(cp, s)) != hipSuccess) return hip_fail(h, e, "count_kernel launch");
+  if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+
+  a2av::CopyParams kp{};
+  kp.input = static_cast<const uint8_t*>(input);
+  kp.target = static_cast<uint8_t*>(target);
+  kp.signal = signal;
+  kp.ws = h->ws;
+  kp.nseg = P * P;
+  kp.P = P;
+  kp.S = h->cfg.S;
+  kp.B = int32_t(li.blocks);
+  kp.G = li.wg_per_block;
+  kp.spin_limit = h->spin_limit;
+  for (int32_t c = 0; c < h->launches; ++c) {
+    const bool last = (c == h->launches - 1);
+    kp.chunk_lo = int64_t(c) * h->chunk_limit;
+    kp.chunk_hi = last ? INT64_MAX : int64_t(c + 1) * h->chunk_limit;
+    kp.last = last ? 1 : 0;
+    kp.wait = (last && li.blocks > 1) ? 1 : 0;
+    e = a2av::launch_copy(kp, li.workgroups, kp.wait != 0, s);
+    if (e != hipSuccess) return hip_fail(h, e, "copy_kernel launch");
+    if (ev && (e = hipEventRecord(ev[size_t(c) + 2], s)) != hipSuccess)
+      return hip_fail(h, e, "hipEventRecord");
+  }
+  if (ev) {
+    ++h->run_counter;
+    ++h->profiled_runs;
+  }
+  return A2AV_OK;
+}
+
+int a2av_query_error(a2av_handle* h) {
+  if (!h) return A2AV_ERR_NULLPTR;
+  DeviceGuard guard(h->device);
+  hipError_t e = hipStreamSynchronize(h->last_stream);
+  if (e != hipSuccess) return hip_fail(h, e, "hipStreamSynchronize");
+  int32_t err = 0;
+  e = hipMemcpy(&err, &h->ws.plan->error, sizeof(err), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(h, e, "hipMemcpy(error)");
+  if (err != 0) {
+    const int32_t zero = 0;
+    e = hipMemcpy(&h->ws.plan->error, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(h, e, "hipMemcpy(clear error)");
+  }
+  return err;
+}
+
+int a2av_profile_read(a2av_handle* h, double* k1_us, double* k2_us, int32_t* k2_launches,
+                      int32_t* runs) {
+  if (!h || !k1_us || !k2_us || !k2_launches || !runs) return A2AV_ERR_NULLPTR;
+  if (!h->profile) return A2AV_ERR_INVALID_ARGS;
+  DeviceGuard guard(h->device);
+  const int64_t n = h->profiled_runs < kProfileRuns ? h->profiled_runs : kProfileRuns;
+  double t1 = 0.0, t2 = 0.0;
+  for (int64_t k = 0; k < n; ++k) {
+    const int64_t run = h->run_counter - 1 - k;
+    hipEvent_t* ev = &h->events[size_t(run % kProfileRuns) * size_t(h->events_per_run)];
+    hipError_t e = hipEventSynchronize(ev[h->events_per_run - 1]);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventSynchronize");
+    float ms1 = 0.f, ms2 = 0.f;
+    if ((e = hipEventElapsedTime(&ms1, ev[0], ev[1])) != hipSuccess)
+      return hip_fail(h, e, "hipEventElapsedTime");
+    if ((e = hipEventElapsedTime(&ms2, ev[1], ev[h->events_per_run - 1])) != hipSuccess)
+      return hip_fail(h, e, "hipEventElapsedTime");
+    t1 += double(ms1) * 1e3;
+    t2 += double(ms2) * 1e3;
+  }
+  *k1_us = t1;
+  *k2_us = t2;
+  *k2_launches = int32_t(n * h->launches);
+  *runs = int32_t(n);
+  h->profiled_runs = 0;
+  return A2AV_OK;
+}
+
+const char* a2av_last_hip_error(a2av_handle* h) { return h ? h->last_error.c_str() : ""; }
+
+}  // extern "C"

@@ -1,0 +1,213 @@
+"""Benchmark of the all_to_all_v exchange on one MI355X.
+
+One step = one a2av_run (K1 count kernel + the K2 copy launches) over one
+seeded synthetic workload already resident in HBM.  Prints ONE JSON line with
+the whole-run throughput (payload bytes read + written per second), the
+roofline of the dominant kernel (K2, HBM-bound) from HIP events recorded by
+the library on the run's stream during the timed region, and the CPU oracle
+timed on a bounded sample of the same workload on the host.
+
+    python bench.py [--steps K] [--warmup W] [--workload c5] [--also c3,c4]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "all_to_all_v achieved HBM GB/s (read+write) and % of MI355X peak, 1 GPU"
+PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
+WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "copy_kernel_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ["kernels.hip", "kernels.h"]:
+        h.update(open(os.path.join(ROOT, "all_movement_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per K2 launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("kernel_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def run_gpu(k: int, steps: int, warmup: int):
+    import torch
+    from all_movement_amd import a2av
+    from all_movement_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    w = wl.workload(k)
+    log(f"[bench] {w.name}: payload {w.payload_bytes} B, generating inputs on the GPU")
+    inp = wl.input_tensor(w, dev)
+    tgt = torch.full((w.tgt_bytes,), wl.SENTINEL, dtype=torch.uint8, device=dev)
+    sig = torch.zeros((w.P, w.S), dtype=torch.int32, device=dev)
+    sc = torch.from_numpy(w.counts).to(dev)
+    rc = torch.zeros((w.P, w.P), dtype=torch.int32, device=dev)
+    ex = a2av.Exchange(w.P, w.in_slab, w.tgt_slab, w.S, device=0, profile=True)
+    info = ex.launch_info(w.core_num)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    for _ in range(warmup):
+        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream)
+    torch.cuda.synchronize()
+    if ex.query_error() != a2av.OK:
+        raise RuntimeError("warmup run reported a device-side error")
+    ex.profile()                           # drop the warmup tally
+
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if ex.query_error() != a2av.OK:
+        raise RuntimeError("timed run reported a device-side error")
+    k1_us, k2_us, k2_launches, runs = ex.profile()
+    ex.close()
+    sec = t1 - t0
+    moved = 2 * w.payload_bytes            # each payload byte read once, written once
+    res = {
+        "w": w, "info": info, "sec": sec, "steps": steps, "moved": moved,
+        "gbps": moved * steps / sec / 1e9, "ms_per_step": sec / steps * 1e3,
+        "k1_us": k1_us / max(runs, 1), "k2_us_per_run": k2_us / max(runs, 1),
+        "k2_launches_per_run": k2_launches / max(runs, 1), "runs_profiled": runs,
+    }
+    # The dominant kernel is K2; its launches share the payload.
+    res["k2_us_per_launch"] = res["k2_us_per_run"] / res["k2_launches_per_run"]
+    res["k2_gbps"] = moved / (res["k2_us_per_run"] * 1e-6) / 1e9
+    del inp, tgt
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(k: int, min_seconds: float = 10.0):
+    """The oracle (as it stands) on a bounded sample of workload k on the host."""
+    import numpy as np
+
+    import oracle
+    from all_movement_amd import workloads as wl
+
+    # Sample: the same workload shape at a reduced size (c5 at 1/8: P=8 equal
+    # counts of 2^22 fp32, 1 GiB of payload; c3/c4 at 1/4), run whole.
+    scale = {1: 1, 2: 1, 3: 4, 4: 4, 5: 8}[k]
+    w = wl.workload(k, scale=scale)
+    inp = wl.input_bytes_np(w)
+    tgt = np.full(w.tgt_bytes, wl.SENTINEL, np.uint8)
+    rc = np.zeros((w.P, w.P), np.int32)
+    times = []
+    t_end = time.perf_counter() + min_seconds
+    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 50):
+        sig = np.zeros((w.P, w.S), np.int32)
+        t0 = time.perf_counter()
+        st = oracle.run(inp, tgt, sig, w.counts, rc, P=w.P, S=w.S, in_slab=w.in_slab,
+                        tgt_slab=w.tgt_slab, core_num=w.core_num, dtype=w.dtype)
+        times.append(time.perf_counter() - t0)
+        assert st == oracle.OK
+    times.sort()
+    med = times[len(times) // 2]
+    return {
+        "value": round(2 * w.payload_bytes / med / 1e9, 3), "unit": "GB/s", "cores": 1,
+        "kind": "oracle",
+        "sample": f"{w.name} at 1/{scale} size ({w.payload_bytes} payload bytes), whole oracle "
+                  f"(checks + transpose + displacements + one memcpy per segment + signal), "
+                  f"single thread, median of {len(times)} runs",
+        "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
+    ap.add_argument("--also", default="c3,c4", help="other workloads reported beside it")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the exchange runs its P virtual ranks as slabs "
+              "of one GPU's memory; runs on more than one GPU are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    k = WORKLOADS[args.workload]
+    main_res = run_gpu(k, args.steps, args.warmup)
+    w, info = main_res["w"], main_res["info"]
+    log(f"[bench] {w.name}: {main_res['gbps']:.1f} GB/s whole run, K2 "
+        f"{main_res['k2_gbps']:.1f} GB/s, {main_res['ms_per_step']:.3f} ms/step")
+    also = {}
+    for name in [s for s in args.also.split(",") if s and s != args.workload]:
+        r = run_gpu(WORKLOADS[name], args.steps, args.warmup)
+        log(f"[bench] {r['w'].name}: {r['gbps']:.1f} GB/s whole run, K2 {r['k2_gbps']:.1f} GB/s")
+        also[r["w"].name] = {"value": round(r["gbps"], 1), "frac_of_peak": round(r["gbps"] / PEAK_GBPS, 4),
+                             "k2_gbps": round(r["k2_gbps"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+                             "blocks": r["info"].blocks, "workgroups": r["info"].workgroups}
+
+    traffic = measured_traffic(w.name)
+    per_launch_bytes = main_res["moved"] / main_res["k2_launches_per_run"]
+    roofline = {
+        "bound": "hbm", "kernel": "copy_kernel (K2)",
+        "achieved": round(per_launch_bytes / (main_res["k2_us_per_launch"] * 1e-6) / 1e9, 1),
+        "peak": PEAK_GBPS, "unit": "GB/s",
+        "frac": round(per_launch_bytes / (main_res["k2_us_per_launch"] * 1e-6) / 1e9 / PEAK_GBPS, 4),
+        "traffic": traffic,
+        "bytes_per_launch": int(per_launch_bytes),
+        "launches_per_step": main_res["k2_launches_per_run"],
+        "avg_launch_us": round(main_res["k2_us_per_launch"], 2),
+        "k1_us": round(main_res["k1_us"], 2),
+    }
+    out = {
+        "metric": METRIC, "value": round(main_res["gbps"], 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32" if w.dtype == 0 else "u8",
+        "data": "synthetic (seeded SplitMix64 payload, seeded count matrices)",
+        "config": {"workload": w.name, "P": w.P, "core_num": w.core_num,
+                   "blocks": info.blocks, "workgroups": info.workgroups,
+                   "chunk_launches": info.chunk_launches,
+                   "payload_bytes": w.payload_bytes, "parallelism": "1 GPU, P virtual ranks"},
+        "frac_of_peak": round(main_res["gbps"] / PEAK_GBPS, 4),
+        "roofline": roofline,
+        "also": also,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(k)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

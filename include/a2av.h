@@ -1,0 +1,180 @@
+/*
+ * a2av.h -- C ABI of the MI355X (gfx950) variable-count all-to-all exchange.
+ *
+ * The operation is the five-operand all_to_all_v of the PyPTO
+ * "LowerL2TensorCollectives Pass" page (section "Behavior": operands input,
+ * target, signal, send_counts, recv_counts with directions In, InOut, InOut,
+ * In, InOut, plus the launch request core_num).  On one GPU the P ranks are
+ * virtual: each owns one slab of a shared allocation, and the exchange is an
+ * on-device scatter/transpose of segments:
+ *
+ *   for every source s and destination d (element size e: fp32 4, int8 1)
+ *     target[d*tgt_slab + rdispl[d][s] .. + send_counts[s][d]*e) =
+ *     input [s*in_slab  + sdispl[s][d] .. + send_counts[s][d]*e)
+ *   with sdispl[s][d] = sum_{d'<d} send_counts[s][d']*e  (input packed by destination)
+ *   and  rdispl[d][s] = sum_{s'<s} send_counts[s'][d]*e  (target packed by source)
+ *   recv_counts[d][s] = send_counts[s][d]
+ *   signal[r][b] += 1 for every rank r < P and admitted block b < B
+ *
+ * Counts scale by the type size as in the ncclx ctranAllToAllvIbImpl
+ * pseudocode on the "vccl alltoallv dev log" page (section 5).  B is
+ * CalAllToAllVBlocks(P, core_num) ("Launch width" section of the PyPTO page).
+ * The create/run split mirrors the two-phase aclnn calling convention of the
+ * CANN BatchMatMulReduceScatterAllToAll page (section "Two-phase API"), and
+ * exchanges whose payload exceeds 1 GiB are issued as several launches of at
+ * most 1 GiB each, after the chunk rule of the vccl page (section 2).
+ *
+ * All device pointers are plain device addresses (hipMalloc or torch CUDA
+ * memory).  The library never allocates, copies or keeps payload buffers: it
+ * owns only a small workspace allocated by a2av_create.
+ *
+ * Thread safety: a handle is not thread-safe and its workspace is shared by
+ * all runs on it; runs on one handle must be ordered (one stream, or streams
+ * the caller orders).  Use one handle per concurrent stream.
+ */
+#ifndef A2AV_H
+#define A2AV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct a2av_handle a2av_handle;
+
+/* Payload element type.  Only FP32 and INT8 exist ("Constraints and
+ * diagnostics" section of the PyPTO page); payload moves as raw bits. */
+enum a2av_dtype { A2AV_FP32 = 0, A2AV_INT8 = 1 };
+
+/* Status codes.  NULLPTR is kept apart from INVALID_ARGS as in the aclnn
+ * error table (ACLNN_ERR_PARAM_NULLPTR vs ACLNN_ERR_PARAM_INVALID). */
+enum a2av_status {
+    A2AV_OK = 0,
+    A2AV_ERR_NULLPTR = 1,           /* a required pointer is NULL               */
+    A2AV_ERR_INVALID_ARGS = 2,      /* bad size, range, stride, alias or signal */
+    A2AV_ERR_UNSUPPORTED_DTYPE = 3, /* dtype not FP32 / INT8                    */
+    A2AV_ERR_OVER_CAPACITY = 4,     /* a row or column of counts overflows its slab */
+    A2AV_ERR_LAUNCH_CAPACITY = 5,   /* B > 1 blocks cannot all be co-resident   */
+    A2AV_ERR_HIP = 6,               /* a HIP runtime call failed                */
+    A2AV_ERR_TIMEOUT = 7            /* the block barrier's bounded wait expired */
+};
+
+/* a2av_config.flags */
+#define A2AV_FLAG_PROFILE 1u /* record HIP events around K1 and every K2 launch */
+
+typedef struct a2av_config {
+    int32_t device;            /* HIP device ordinal the handle binds to                 */
+    int32_t P;                 /* virtual ranks, 1..64 (NR of the [NR, S] signal)        */
+    int64_t in_slab_bytes;     /* byte stride between input slabs, >= 1                  */
+    int64_t tgt_slab_bytes;    /* byte stride between target slabs, >= 1                 */
+    int32_t S;                 /* signal row stride in int32 elements, >= 1              */
+    int32_t wg_per_block;      /* workgroups per admitted block; 0 = chosen at create    */
+    int64_t chunk_limit_bytes; /* payload bytes per K2 launch; 0 = 2^30 (1 GiB)          */
+    int64_t capacity_override; /* co-resident workgroup limit; 0 = query the device      */
+    uint32_t flags;            /* A2AV_FLAG_*                                            */
+    int32_t spin_limit;        /* barrier poll limit; 0 = default (about 1 s)            */
+} a2av_config;
+
+/* What one a2av_run with a given core_num launches (for logs and benches). */
+typedef struct a2av_launch_info {
+    int64_t blocks;            /* B = CalAllToAllVBlocks(P, core_num)                    */
+    int32_t wg_per_block;      /* G: workgroups that execute one admitted block          */
+    int32_t workgroups;        /* W = B * G workgroups per K2 launch                     */
+    int32_t threads_per_wg;    /* K2 workgroup size                                      */
+    int32_t chunk_launches;    /* K2 launches per run (host chunk plan)                  */
+    int64_t chunk_limit_bytes; /* payload bytes per K2 launch                            */
+    int64_t capacity;          /* co-resident K2 workgroups on the device                */
+    int32_t cooperative;       /* 1 when the last K2 launch is cooperative (B > 1)      */
+    int32_t reserved;
+} a2av_launch_info;
+
+/*
+ * Create a handle bound to cfg->device: checks the geometry (P in 1..64,
+ * slabs >= 1, S >= 1, chunk limit >= 0), queries the co-resident capacity of
+ * the copy kernel and allocates the workspace (displacement tables, plan
+ * words, block counters, the latched error word).
+ * Returns A2AV_OK and sets *out, or an error with *out left NULL.
+ * Errors: NULLPTR (out or cfg NULL), INVALID_ARGS (geometry), HIP.
+ */
+int a2av_create(a2av_handle **out, const a2av_config *cfg);
+
+/*
+ * Enqueue one exchange on `stream` (a hipStream_t; NULL = default stream).
+ *   input        device, P*in_slab bytes, read only
+ *   target       device, P*tgt_slab bytes; only the received prefix of each
+ *                slab is written, the rest keeps its bytes
+ *   signal       device int32 [P, S], row-major; entries (r < P, b < B) +1
+ *   send_counts  device int32 [P, P], row-major [s][d], element counts, read only
+ *   recv_counts  device int32 [P, P], row-major [d][s], overwritten
+ *   P            must equal the handle's P (the rank count is an explicit
+ *                argument here, where the page's kernel reads it from its
+ *                communication context)
+ *   core_num     requested block limit L, 1..INT32_MAX
+ *   dtype        A2AV_FP32 or A2AV_INT8
+ *
+ * Checked on the host before anything is enqueued, first failure wins:
+ *   NULLPTR (any operand) -> UNSUPPORTED_DTYPE -> INVALID_ARGS (P differs
+ *   from the handle, core_num out of range, S < B) -> LAUNCH_CAPACITY (B > 1
+ *   and B above the co-resident capacity: refused, never partially launched)
+ *   -> INVALID_ARGS (two operands share a byte; a slab size not a whole
+ *   number of elements).
+ * Checked on the device by the count kernel, in this order, before any
+ * operand is written: a negative count (INVALID_ARGS), a source row or
+ * destination column whose bytes exceed its slab (OVER_CAPACITY),
+ * signal[r][b] (r < P, b < B) not all equal (INVALID_ARGS).  A device-side
+ * failure writes nothing, is latched in the handle and is reported by
+ * a2av_query_error; a2av_run itself has already returned A2AV_OK.
+ * The call does not synchronize: results are visible to later work on
+ * `stream`.  Returns A2AV_ERR_HIP if a launch fails.
+ */
+int a2av_run(a2av_handle *h, const void *input, void *target, int32_t *signal,
+             const int32_t *send_counts, int32_t *recv_counts, int32_t P, int64_t core_num,
+             int32_t dtype, void *stream);
+
+/* Free the workspace and the handle (synchronizes the device first).
+ * NULL is accepted and ignored. */
+int a2av_destroy(a2av_handle *h);
+
+/* CalAllToAllVBlocks(P, L): L when L < P, else the largest multiple of P not
+ * exceeding L ("Launch width" section of the PyPTO page).  -1 if P < 1 or L < 1.
+ * Pure host function. */
+int64_t a2av_blocks(int64_t P, int64_t L);
+
+/* Host-side checks of a2av_run, as a pure host function that never touches
+ * device memory (usable without a GPU).  cfg gives P, slabs and S; `capacity`
+ * is the co-resident limit (<= 0: no limit); `P` is the run's argument.
+ * Returns the status a2av_run would return before enqueuing anything. */
+int a2av_check_args(const a2av_config *cfg, int64_t capacity, const void *input,
+                    const void *target, const int32_t *signal, const int32_t *send_counts,
+                    const int32_t *recv_counts, int32_t P, int64_t core_num, int32_t dtype);
+
+/* Wait for the handle's last stream, then return and clear the latched
+ * device-side status (A2AV_OK when every run since the last query was valid;
+ * otherwise the first failure: INVALID_ARGS, OVER_CAPACITY or TIMEOUT). */
+int a2av_query_error(a2av_handle *h);
+
+/* Fill *out with what a run with `core_num` would launch.  Errors: NULLPTR,
+ * INVALID_ARGS (core_num out of range), LAUNCH_CAPACITY. */
+int a2av_launch_info_get(a2av_handle *h, int64_t core_num, a2av_launch_info *out);
+
+/* With A2AV_FLAG_PROFILE: wait for the runs recorded since the last read (at
+ * most the last 256) and report, summed over them, the count kernel's time
+ * and the K2 time (end of K1 to end of the last K2 launch, so the gaps between
+ * a run's K2 launches are included) in microseconds, the number of K2
+ * launches and the number of runs; then start a new tally.
+ * Returns INVALID_ARGS when the handle was created without profiling. */
+int a2av_profile_read(a2av_handle *h, double *k1_us, double *k2_us, int32_t *k2_launches,
+                      int32_t *runs);
+
+/* Human-readable name of a status code (static storage). */
+const char *a2av_status_string(int status);
+
+/* Text of the last failing HIP call on this handle ("" if none). */
+const char *a2av_last_hip_error(a2av_handle *h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* A2AV_H */

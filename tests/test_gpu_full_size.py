@@ -1,0 +1,89 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (default Exchange settings, the workload's own core_num).
+
+c3 and c4 are compared with the whole C oracle on the host.  c5 (8 GiB of
+payload) is checked by a property that holds at any size -- with equal counts
+the exchange is the block transpose target[d][s] = input[s][d], compared on
+the GPU with torch slicing -- plus sampled bytes located one by one by the
+oracle's per-byte view from regenerated input bytes.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from all_movement_amd import a2av  # noqa: E402
+from all_movement_amd import workloads as wl  # noqa: E402
+from oracle import locate  # noqa: E402
+from tests.gpu_harness import DEV, Case, exchange_for, say  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _gpu_or_skip():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("k", [3, 4])
+def test_full_size_against_oracle(k):
+    w = wl.workload(k)
+    say("full size", w.name, "payload bytes", w.payload_bytes)
+    c = Case(w, host_input=False)          # input generated on the GPU by the workload module
+    ex = exchange_for(w)
+    try:
+        info = ex.launch_info(w.core_num)
+        say("launch", info.blocks, info.wg_per_block, info.workgroups, info.chunk_launches)
+        st = c.run_gpu(ex)
+        c.assert_matches(st, c.run_oracle())
+    finally:
+        ex.close()
+
+
+def test_c4_with_small_chunks_against_oracle():
+    # The chunked path the c4 text intends: 256 MiB per launch (about 4 launches).
+    w = wl.workload(4)
+    c = Case(w, host_input=False)
+    ex = exchange_for(w, chunk_limit_bytes=256 << 20)
+    try:
+        assert ex.launch_info(w.core_num).chunk_launches == 8
+        c.assert_matches(c.run_gpu(ex), c.run_oracle())
+    finally:
+        ex.close()
+
+
+def test_c5_full_size_block_transpose_and_samples():
+    w = wl.workload(5)
+    P = w.P
+    n = int(w.counts[0, 0]) * 4
+    say("full size", w.name, "payload bytes", w.payload_bytes)
+    c = Case(w, host_input=False)
+    ex = exchange_for(w)
+    try:
+        info = ex.launch_info(w.core_num)
+        assert info.chunk_launches == 8 and info.blocks == 256
+        assert c.run_gpu(ex) == a2av.OK
+        inp = c.input.view(P, P, n)
+        tgt = c.target.view(P, P, n)
+        for d in range(P):
+            for s in range(P):
+                assert torch.equal(tgt[d, s], inp[s, d]), (d, s)
+        assert (c.signal.cpu().numpy() == 1).all()
+        np.testing.assert_array_equal(c.recv.cpu().numpy(), w.counts.T)
+        # Sampled bytes, located by the oracle and regenerated from the seed.
+        rng = np.random.default_rng(55)
+        d_idx = rng.integers(0, P, 4000)
+        offs = rng.integers(0, w.tgt_slab, 4000)
+        offs[:8] = [0, 1, 15, 16, n - 1, n, w.tgt_slab - 1, w.tgt_slab - 16]
+        got = c.target.view(P, w.tgt_slab)[torch.as_tensor(d_idx, device=DEV),
+                                           torch.as_tensor(offs, device=DEV)].cpu().numpy()
+        for j in range(len(d_idx)):
+            src = locate.source_of(w.counts, int(d_idx[j]), int(offs[j]), 4, w.in_slab)
+            want = wl.SENTINEL if src is None else wl.random_bytes_np(w.payload_seed, src, 1)[0]
+            assert got[j] == want, (int(d_idx[j]), int(offs[j]))
+    finally:
+        ex.close()
