@@ -6,13 +6,13 @@
 // with wave64 exclusive scans (send side along d, receive side along s, and
 // the flattened s-major payload prefix that K2 partitions).
 //
-// K2 (copy_kernel, W = B * G workgroups): each workgroup copies one
-// contiguous share of the flattened payload.  Inside a segment the copy is
+// K2 (copy_kernel, W = B * G workgroups): the flattened payload is cut into
+// 128 KiB tiles dealt round-robin to the workgroups.  Inside a segment the copy is
 // destination-aligned: 128-bit nontemporal loads and stores in the body,
 // byte stores for the at most 15 bytes at either end, so no byte outside a
 // segment is ever written.  When source and destination are not congruent
-// mod 16 the body is realigned through LDS: each wave stages 64 aligned
-// source words plus one, then every lane funnels its word and its
+// mod 16 the body is realigned through LDS: each wave stages a row of 64
+// aligned source words, then every lane funnels its word and its right
 // neighbour's with v_alignbyte.  On the run's final launch every admitted
 // block raises its flag in every rank's signal row, and when B > 1 (a
 // cooperative launch) every workgroup waits, with a bounded spin, until all
@@ -31,8 +31,9 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kUnroll = 8;          // 16-byte words in flight per lane
-constexpr int64_t kTileBytes = 16384; // flattened payload bytes per wave task
+constexpr int kUnroll = 8;          // 16-byte words in flight per lane, aligned body
+constexpr int kRealignUnroll = 4;   // 64-word rows in flight per wave, realigned body
+constexpr int64_t kTileBytes = 131072; // flattened payload bytes per workgroup tile
 
 // ------------------------------------------------------------------ K1
 
@@ -166,74 +167,84 @@ __device__ inline u32x4 funnel(u32x4 a, u32x4 b, uint32_t r) {
   return o;
 }
 
-// Body with source and destination both 16-byte aligned: K words, one wave.
-__device__ inline void wave_copy_aligned(const u32x4* __restrict__ s, u32x4* __restrict__ d,
-                                         int64_t K, int lane) {
+// Body with source and destination both 16-byte aligned: K words, copied by
+// the whole workgroup.  Thread t moves words t, t + NT, ... : each load
+// instruction of a wave covers 1 KiB, and a thread's kUnroll loads in flight
+// are NT words (16 KiB) apart.
+__device__ inline void wg_copy_aligned(const u32x4* __restrict__ s, u32x4* __restrict__ d,
+                                       int64_t K, int tid) {
+  constexpr int NT = kCopyThreads;
   int64_t k0 = 0;
-  for (; k0 + kWave * kUnroll <= K; k0 += kWave * kUnroll) {
+  for (; k0 + int64_t(NT) * kUnroll <= K; k0 += int64_t(NT) * kUnroll) {
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) v[j] = __builtin_nontemporal_load(s + k0 + j * kWave + lane);
+    for (int j = 0; j < kUnroll; ++j) v[j] = __builtin_nontemporal_load(s + k0 + j * NT + tid);
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) __builtin_nontemporal_store(v[j], d + k0 + j * kWave + lane);
+    for (int j = 0; j < kUnroll; ++j) __builtin_nontemporal_store(v[j], d + k0 + j * NT + tid);
   }
-  for (int64_t k = k0 + lane; k < K; k += kWave)
+  for (int64_t k = k0 + tid; k < K; k += NT)
     __builtin_nontemporal_store(__builtin_nontemporal_load(s + k), d + k);
 }
 
 // Body whose source sits phi = 4*Q + r bytes (1..15) past a 16-byte boundary:
 // output word k is bytes [phi, phi+16) of aligned source words A[k], A[k+1].
 // Words A[0..K] all hold body bytes, so every load stays inside 16-byte words
-// that the segment touches.  The wave works on rows of 64 consecutive source
-// words that overlap by one: lane l of row q loads A[63q + l] and lanes 0..62
-// emit outputs 63q + l, taking the right neighbour's word from the wave's
-// LDS slot (1 KiB per wave, reused row after row).
+// that the segment touches.  Rows of 64 output words go to the waves in turn;
+// lane l of row q loads A[64q + l], takes A[64q + l + 1] from its right
+// neighbour through the wave's LDS slot (1 KiB, reused row after row), and
+// lane 63 uses A[64q + 64], which the whole wave loads as one broadcast word.
 template <int Q>
-__device__ void wave_copy_realign(const u32x4* __restrict__ A, u32x4* __restrict__ D, int64_t K,
-                                  uint32_t r, u32x4* slot, int lane) {
-  constexpr int kRow = kWave - 1;
-  const int64_t nrows = (K + kRow - 1) / kRow;
-  for (int64_t r0 = 0; r0 < nrows; r0 += kUnroll) {
-    u32x4 v[kUnroll];
+__device__ void wg_copy_realign(const u32x4* __restrict__ A, u32x4* __restrict__ D, int64_t K,
+                                uint32_t r, u32x4* slot, int lane, int wave) {
+  constexpr int NW = kCopyThreads / kWave;
+  const int64_t nrows = (K + kWave - 1) / kWave;
+  for (int64_t r0 = 0; r0 < nrows; r0 += int64_t(kRealignUnroll) * NW) {
+    u32x4 v[kRealignUnroll];
+    u32x4 x[kRealignUnroll];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t k = (r0 + j) * kRow + lane;
+    for (int j = 0; j < kRealignUnroll; ++j) {
+      const int64_t row = r0 + int64_t(j) * NW + wave;
+      const int64_t k = row * kWave + lane;
+      const int64_t next = row * kWave + kWave;
       v[j] = u32x4{0u, 0u, 0u, 0u};
-      if (r0 + j < nrows && k <= K) v[j] = __builtin_nontemporal_load(A + k);
+      x[j] = u32x4{0u, 0u, 0u, 0u};
+      if (row < nrows && k <= K) v[j] = __builtin_nontemporal_load(A + k);
+      if (row < nrows && next <= K) x[j] = __builtin_nontemporal_load(A + next);
     }
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t k = (r0 + j) * kRow + lane;
+    for (int j = 0; j < kRealignUnroll; ++j) {
+      const int64_t row = r0 + int64_t(j) * NW + wave;
+      const int64_t k = row * kWave + lane;
       slot[lane] = v[j];
       // Lanes read a word another lane wrote: keep the compiler from moving
       // LDS accesses across these points (a wave's LDS operations run in order).
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      const u32x4 hi = slot[(lane + 1) & (kWave - 1)];
+      u32x4 hi = slot[(lane + 1) & (kWave - 1)];
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      if (r0 + j < nrows && lane < kRow && k < K)
-        __builtin_nontemporal_store(funnel<Q>(v[j], hi, r), D + k);
+      if (lane == kWave - 1) hi = x[j];
+      if (row < nrows && k < K) __builtin_nontemporal_store(funnel<Q>(v[j], hi, r), D + k);
     }
   }
 }
 
-// Copy n bytes src -> dst (one piece of one segment) with one wave.  The
-// destination body is whole aligned 16-byte words; the at most 15 bytes on
-// either side are written one byte per lane, so no byte outside the piece is
-// ever stored.
-__device__ void wave_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int lane,
-                                u32x4* slot) {
+// Copy n bytes src -> dst (one piece of one segment) with the whole
+// workgroup.  The destination body is whole aligned 16-byte words; the at
+// most 15 bytes on either side are written one byte per thread, so no byte
+// outside the piece is ever stored.
+__device__ void wg_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int tid, int lane,
+                              int wave, u32x4* slot) {
   const uintptr_t d0 = uintptr_t(dst);
   const uintptr_t body_lo = (d0 + 15u) & ~uintptr_t(15);
   const uintptr_t body_hi = (d0 + uintptr_t(n)) & ~uintptr_t(15);
   if (body_lo >= body_hi) {
-    for (int64_t k = lane; k < n; k += kWave) dst[k] = src[k];
+    for (int64_t k = tid; k < n; k += kCopyThreads) dst[k] = src[k];
     return;
   }
   const int64_t head = int64_t(body_lo - d0);
   const int64_t tail_at = int64_t(body_hi - d0);
   const int64_t tail = n - tail_at;
-  if (lane < head) dst[lane] = src[lane];
-  if (lane >= 16 && lane - 16 < tail) dst[tail_at + lane - 16] = src[tail_at + lane - 16];
+  if (tid < head) dst[tid] = src[tid];
+  if (tid >= 16 && tid - 16 < tail) dst[tail_at + tid - 16] = src[tail_at + tid - 16];
 
   // Pointers keep their provenance (no integer-to-pointer casts) so the
   // compiler emits global, not flat, memory instructions.
@@ -242,16 +253,16 @@ __device__ void wave_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int
   const uint32_t phi = uint32_t(uintptr_t(sb) & 15u);
   u32x4* D = reinterpret_cast<u32x4*>(dst + head);
   if (phi == 0) {
-    wave_copy_aligned(reinterpret_cast<const u32x4*>(sb), D, K, lane);
+    wg_copy_aligned(reinterpret_cast<const u32x4*>(sb), D, K, tid);
     return;
   }
   const u32x4* A = reinterpret_cast<const u32x4*>(sb - phi);
   const uint32_t r = phi & 3u;
   switch (phi >> 2) {
-    case 0: wave_copy_realign<0>(A, D, K, r, slot, lane); break;
-    case 1: wave_copy_realign<1>(A, D, K, r, slot, lane); break;
-    case 2: wave_copy_realign<2>(A, D, K, r, slot, lane); break;
-    default: wave_copy_realign<3>(A, D, K, r, slot, lane); break;
+    case 0: wg_copy_realign<0>(A, D, K, r, slot, lane, wave); break;
+    case 1: wg_copy_realign<1>(A, D, K, r, slot, lane, wave); break;
+    case 2: wg_copy_realign<2>(A, D, K, r, slot, lane, wave); break;
+    default: wg_copy_realign<3>(A, D, K, r, slot, lane, wave); break;
   }
 }
 
@@ -292,11 +303,12 @@ __device__ inline int64_t align_boundary(const SegTables& t, int nseg, const uin
 }
 
 // One K2 launch copies the flattened payload bytes [c_lo, c_hi) of the run.
-// The range is cut into 16 KiB tiles dealt round-robin to every wave of the
-// grid, so at any moment all waves stream through one narrow window of the
-// source and of the destination (measured on gfx950: contiguous per-workgroup
-// ranges that fan out to destination slabs 1 GiB apart ran at ~4.1 TB/s, the
-// same bytes as interleaved tiles at ~5.6 TB/s).
+// The range is cut into 128 KiB tiles dealt round-robin to the workgroups, so
+// at any moment the grid streams through one narrow window of the source and
+// of the destination (measured on gfx950: contiguous per-workgroup ranges that
+// fan out to destination slabs 1 GiB apart ran at ~4.1 TB/s, the same bytes as
+// interleaved tiles at ~5.6 TB/s).  Every wave derives the same tile bounds
+// and pieces from the LDS tables, so tiles need no workgroup barrier.
 template <int NT>
 __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   constexpr int NW = NT / kWave;
@@ -321,8 +333,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   __syncthreads();
 
   const int64_t ntiles = (c_hi - c_lo + kTileBytes - 1) / kTileBytes;
-  const int64_t waves = int64_t(gridDim.x) * NW;
-  for (int64_t t = int64_t(blockIdx.x) * NW + wave; t < ntiles; t += waves) {
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t x0 = c_lo + t * kTileBytes;
     const int64_t x1 = x0 + kTileBytes < c_hi ? x0 + kTileBytes : c_hi;
     const int64_t a = t == 0 ? c_lo : align_boundary(tab, nseg, p.target, x0, c_hi, lane);
@@ -334,8 +345,8 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
       if (seg_hi > x) {
         const int64_t pe = b < seg_hi ? b : seg_hi;
         const int64_t off = x - tab.prefix[i];
-        wave_copy_piece(p.input + tab.src[i] + off, p.target + tab.dst[i] + off, pe - x, lane,
-                        slots[wave]);
+        wg_copy_piece(p.input + tab.src[i] + off, p.target + tab.dst[i] + off, pe - x, tid, lane,
+                      wave, slots[wave]);
         x = pe;
       }
       ++i;
