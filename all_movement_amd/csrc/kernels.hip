@@ -8,7 +8,8 @@
 //
 // K2 (copy_kernel, W = B * G workgroups): the flattened payload is cut into
 // 128 KiB tiles dealt round-robin to the workgroups.  Inside a segment the copy is
-// destination-aligned: 128-bit nontemporal loads and stores in the body,
+// destination-aligned: 128-bit streaming buffer loads and device-scope
+// streaming buffer stores in the body,
 // byte stores for the at most 15 bytes at either end, so no byte outside a
 // segment is ever written.  When source and destination are not congruent
 // mod 16 the body is realigned through LDS: each wave stages a row of 64
@@ -34,6 +35,18 @@ constexpr int kWave = 64;
 constexpr int kUnroll = 8;          // 16-byte words in flight per lane, aligned body
 constexpr int kRealignUnroll = 4;   // 64-word rows in flight per wave, realigned body
 constexpr int64_t kTileBytes = 131072; // flattened payload bytes per workgroup tile
+
+// Buffer resources: word 3 of a raw (untyped, stride 0) buffer descriptor on
+// the gfx9 family; num_records is in bytes and the hardware drops any access
+// past it (loads read 0, stores are discarded), so a piece's descriptor also
+// fences its accesses to the piece.
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy bits of buffer instructions on gfx950: nt = 2 (streaming),
+// sc1 = 16 (device scope).  Payload loads stream; payload stores stream and
+// are device-scope, so a store is visible to every XCD once acknowledged and
+// the arrival below needs no L2 writeback.
+constexpr int kLoadPolicy = 2;
+constexpr int kStorePolicy = 2 | 16;
 
 // ------------------------------------------------------------------ K1
 
@@ -65,18 +78,21 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
 
   // Load the counts; note negatives (bit 0) and a signal that is not uniform
   // over the admitted entries (bit 2).
+  // The loops are unrolled so each thread issues its loads back to back.
   int bad = 0;
+#pragma unroll 4
   for (int i = tid; i < PP; i += kCountThreads) {
     const int32_t c = p.send_counts[i];
     C[i] = c;
-    if (c < 0) bad |= 1;
+    bad |= c < 0 ? 1 : 0;
   }
   const int32_t base = p.signal[0];
   const int nsig = P * p.B;
+#pragma unroll 8
   for (int j = tid; j < nsig; j += kCountThreads) {
     const int r = j / p.B;
     const int b = j - r * p.B;
-    if (p.signal[int64_t(r) * p.S + b] != base) bad |= 4;
+    bad |= p.signal[int64_t(r) * p.S + b] != base ? 4 : 0;
   }
   if (bad) atomicOr(&flags, bad);
   __syncthreads();
@@ -155,6 +171,18 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
 
 // ------------------------------------------------------------------ K2
 
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3);
+}
+
+__device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, int64_t word) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, int(word * 16), 0, kLoadPolicy);
+}
+
+__device__ inline void store16(__amdgpu_buffer_rsrc_t r, int64_t word, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, int(word * 16), 0, kStorePolicy);
+}
+
 // Output word = bytes [phi, phi+16) of the 32 bytes a:b, phi = 4*Q + r.
 template <int Q>
 __device__ inline u32x4 funnel(u32x4 a, u32x4 b, uint32_t r) {
@@ -171,19 +199,34 @@ __device__ inline u32x4 funnel(u32x4 a, u32x4 b, uint32_t r) {
 // the whole workgroup.  Thread t moves words t, t + NT, ... : each load
 // instruction of a wave covers 1 KiB, and a thread's kUnroll loads in flight
 // are NT words (16 KiB) apart.
-__device__ inline void wg_copy_aligned(const u32x4* __restrict__ s, u32x4* __restrict__ d,
-                                       int64_t K, int tid) {
+__device__ inline void wg_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int tid) {
   constexpr int NT = kCopyThreads;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, K * 16);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(d, K * 16);
   int64_t k0 = 0;
   for (; k0 + int64_t(NT) * kUnroll <= K; k0 += int64_t(NT) * kUnroll) {
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) v[j] = __builtin_nontemporal_load(s + k0 + j * NT + tid);
+    for (int j = 0; j < kUnroll; ++j) v[j] = load16(rs, k0 + j * NT + tid);
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) __builtin_nontemporal_store(v[j], d + k0 + j * NT + tid);
+    for (int j = 0; j < kUnroll; ++j) store16(rd, k0 + j * NT + tid, v[j]);
   }
-  for (int64_t k = k0 + tid; k < K; k += NT)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(s + k), d + k);
+  // The remainder (under NT * kUnroll words) in one predicated pass, so short
+  // pieces keep kUnroll loads in flight too.
+  if (k0 < K) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t k = k0 + j * NT + tid;
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (k < K) v[j] = load16(rs, k);
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t k = k0 + j * NT + tid;
+      if (k < K) store16(rd, k, v[j]);
+    }
+  }
 }
 
 // Body whose source sits phi = 4*Q + r bytes (1..15) past a 16-byte boundary:
@@ -194,9 +237,11 @@ __device__ inline void wg_copy_aligned(const u32x4* __restrict__ s, u32x4* __res
 // neighbour through the wave's LDS slot (1 KiB, reused row after row), and
 // lane 63 uses A[64q + 64], which the whole wave loads as one broadcast word.
 template <int Q>
-__device__ void wg_copy_realign(const u32x4* __restrict__ A, u32x4* __restrict__ D, int64_t K,
-                                uint32_t r, u32x4* slot, int lane, int wave) {
+__device__ void wg_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r, u32x4* slot,
+                                int lane, int wave) {
   constexpr int NW = kCopyThreads / kWave;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(A, (K + 1) * 16);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(D, K * 16);
   const int64_t nrows = (K + kWave - 1) / kWave;
   for (int64_t r0 = 0; r0 < nrows; r0 += int64_t(kRealignUnroll) * NW) {
     u32x4 v[kRealignUnroll];
@@ -208,8 +253,8 @@ __device__ void wg_copy_realign(const u32x4* __restrict__ A, u32x4* __restrict__
       const int64_t next = row * kWave + kWave;
       v[j] = u32x4{0u, 0u, 0u, 0u};
       x[j] = u32x4{0u, 0u, 0u, 0u};
-      if (row < nrows && k <= K) v[j] = __builtin_nontemporal_load(A + k);
-      if (row < nrows && next <= K) x[j] = __builtin_nontemporal_load(A + next);
+      if (row < nrows && k <= K) v[j] = load16(rs, k);
+      if (row < nrows && next <= K) x[j] = load16(rs, next);
     }
 #pragma unroll
     for (int j = 0; j < kRealignUnroll; ++j) {
@@ -222,7 +267,7 @@ __device__ void wg_copy_realign(const u32x4* __restrict__ A, u32x4* __restrict__
       u32x4 hi = slot[(lane + 1) & (kWave - 1)];
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       if (lane == kWave - 1) hi = x[j];
-      if (row < nrows && k < K) __builtin_nontemporal_store(funnel<Q>(v[j], hi, r), D + k);
+      if (row < nrows && k < K) store16(rd, k, funnel<Q>(v[j], hi, r));
     }
   }
 }
@@ -236,18 +281,21 @@ __device__ void wg_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int t
   const uintptr_t d0 = uintptr_t(dst);
   const uintptr_t body_lo = (d0 + 15u) & ~uintptr_t(15);
   const uintptr_t body_hi = (d0 + uintptr_t(n)) & ~uintptr_t(15);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(dst, n);
   if (body_lo >= body_hi) {
-    for (int64_t k = tid; k < n; k += kCopyThreads) dst[k] = src[k];
+    for (int64_t k = tid; k < n; k += kCopyThreads)
+      __builtin_amdgcn_raw_buffer_store_b8(src[k], rb, int(k), 0, kStorePolicy);
     return;
   }
   const int64_t head = int64_t(body_lo - d0);
   const int64_t tail_at = int64_t(body_hi - d0);
   const int64_t tail = n - tail_at;
-  if (tid < head) dst[tid] = src[tid];
-  if (tid >= 16 && tid - 16 < tail) dst[tail_at + tid - 16] = src[tail_at + tid - 16];
+  if (tid < head) __builtin_amdgcn_raw_buffer_store_b8(src[tid], rb, tid, 0, kStorePolicy);
+  if (tid >= 16 && tid - 16 < tail) {
+    const int64_t k = tail_at + tid - 16;
+    __builtin_amdgcn_raw_buffer_store_b8(src[k], rb, int(k), 0, kStorePolicy);
+  }
 
-  // Pointers keep their provenance (no integer-to-pointer casts) so the
-  // compiler emits global, not flat, memory instructions.
   const uint8_t* sb = src + head;
   const int64_t K = int64_t(body_hi - body_lo) >> 4;
   const uint32_t phi = uint32_t(uintptr_t(sb) & 15u);
@@ -355,29 +403,28 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
 
   if (!p.last) return;
 
-  // Arrival.  Each wave waits until its own stores are acknowledged (in its
-  // XCD's L2); then one release per workgroup writes that L2 back so every
-  // XCD sees the payload, and the last workgroup of block b raises
-  // signal[r][b] for every rank r and counts the block as arrived.
+  // Arrival.  Every payload store is device-scope, so once a wave's stores are
+  // acknowledged (vmcnt 0) they are visible to every XCD: that wait is the
+  // release.  Then the last workgroup of block b raises signal[r][b] for
+  // every rank r and counts the block as arrived; the asm's memory clobber
+  // and the barrier keep the compiler from hoisting the atomics above it.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
     const int b = int(blockIdx.x) / p.G;
     const uint32_t done =
-        __hip_atomic_fetch_add(&p.ws.blk_cnt[b], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&p.ws.blk_cnt[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done == uint32_t(p.G - 1)) {
-      // Release: a reader that acquires a flag sees the block's payload.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       for (int r = 0; r < p.P; ++r)
         __hip_atomic_fetch_add(&p.signal[int64_t(r) * p.S + b], 1, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&plan->arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&plan->arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (p.wait) {
       // All admitted blocks are co-resident (cooperative launch); wait until
       // every one has arrived.  Polls are relaxed device-scope loads (no
-      // cache invalidation per poll); one acquire follows the wait.  The wait
-      // is bounded: a lost arrival latches TIMEOUT instead of hanging.
+      // cache invalidation per poll); nothing is read after the wait.  The
+      // wait is bounded: a lost arrival latches TIMEOUT instead of hanging.
       int spins = 0;
       while (__hip_atomic_load(&plan->arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
              uint32_t(p.B)) {
@@ -390,7 +437,6 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
         }
         __builtin_amdgcn_s_sleep(2);
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
   }
   __syncthreads();

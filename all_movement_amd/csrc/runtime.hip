@@ -9,8 +9,9 @@
 //                                                   s-major flattened order
 // The number of K2 launches comes from the slab geometry (the payload bound
 // P * min(in_slab, tgt_slab)), so the host never reads the counts back; a
-// launch whose range lies past the run's payload does no copying.  Only the
-// final launch raises the signal flags, and it is cooperative when B > 1.
+// launch whose range lies past the run's payload does no copying.  Launches
+// go from the highest chunk down to chunk 0; only the final one (chunk 0)
+// raises the signal flags, and it is cooperative when B > 1.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -37,7 +38,7 @@ struct a2av_handle {
   hipStream_t last_stream = nullptr;
   bool profile = false;
   // Event sets of the last kProfileRuns runs: per run [0] before K1, [1] after
-  // K1, [2+c] after K2 launch c.
+  // K1, [2+n] after the n-th K2 launch.
   std::vector<hipEvent_t> events;
   int32_t events_per_run = 0;
   int64_t profiled_runs = 0;  // runs recorded since the last a2av_profile_read
@@ -240,15 +241,20 @@ int a2av_run(a2av_handle* h, const void* input, void* target, int32_t* signal,
   kp.B = int32_t(li.blocks);
   kp.G = li.wg_per_block;
   kp.spin_limit = h->spin_limit;
-  for (int32_t c = 0; c < h->launches; ++c) {
-    const bool last = (c == h->launches - 1);
+  // Chunks are issued from the highest to chunk 0.  Chunks past the run's
+  // payload cost only a plain launch that exits at once, and the final launch
+  // (the one that raises the flags, cooperative when B > 1) is chunk 0, which
+  // holds payload whenever the run has any.
+  for (int32_t n = 0; n < h->launches; ++n) {
+    const int32_t c = h->launches - 1 - n;
+    const bool last = (c == 0);
     kp.chunk_lo = int64_t(c) * h->chunk_limit;
-    kp.chunk_hi = last ? INT64_MAX : int64_t(c + 1) * h->chunk_limit;
+    kp.chunk_hi = (c == h->launches - 1) ? INT64_MAX : int64_t(c + 1) * h->chunk_limit;
     kp.last = last ? 1 : 0;
     kp.wait = (last && li.blocks > 1) ? 1 : 0;
     e = a2av::launch_copy(kp, li.workgroups, kp.wait != 0, s);
     if (e != hipSuccess) return hip_fail(h, e, "copy_kernel launch");
-    if (ev && (e = hipEventRecord(ev[size_t(c) + 2], s)) != hipSuccess)
+    if (ev && (e = hipEventRecord(ev[size_t(n) + 2], s)) != hipSuccess)
       return hip_fail(h, e, "hipEventRecord");
   }
   if (ev) {
