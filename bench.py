@@ -103,6 +103,21 @@ def run_gpu(k: int, steps: int, warmup: int):
     return res
 
 
+def copy_probe(nbytes: int, steps: int) -> None:
+    """A plain device-to-device copy of a known size (torch's copy kernel):
+    reads and writes exactly nbytes per launch, the reference that scales the
+    HBM byte counters of the exchange's kernels."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": steps}), flush=True)
+
+
 def cpu_baseline(k: int, min_seconds: float = 10.0):
     """The oracle (as it stands) on a bounded sample of workload k on the host."""
     import numpy as np
@@ -157,6 +172,9 @@ def main():
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
     ap.add_argument("--also", default="c3,c4", help="other workloads reported beside it")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain torch device copy of MIB MiB --steps times (the "
+                         "known-size reference for HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the exchange runs its P virtual ranks as slabs "
@@ -164,6 +182,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_probe:
+        copy_probe(args.copy_probe << 20, args.steps)
+        return
     k = WORKLOADS[args.workload]
     main_res = run_gpu(k, args.steps, args.warmup)
     w, info = main_res["w"], main_res["info"]
