@@ -87,12 +87,10 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     bad |= c < 0 ? 1 : 0;
   }
   const int32_t base = p.signal[0];
-  const int nsig = P * p.B;
-#pragma unroll 8
-  for (int j = tid; j < nsig; j += kCountThreads) {
-    const int r = j / p.B;
-    const int b = j - r * p.B;
-    bad |= p.signal[int64_t(r) * p.S + b] != base ? 4 : 0;
+  for (int r = wave; r < P; r += kWaves) {
+    const int32_t* row = p.signal + int64_t(r) * p.S;
+#pragma unroll 4
+    for (int b = lane; b < p.B; b += kWave) bad |= row[b] != base ? 4 : 0;
   }
   if (bad) atomicOr(&flags, bad);
   __syncthreads();
@@ -321,18 +319,14 @@ struct SegTables {
   int64_t dst[kMaxP * kMaxP];
 };
 
-// Largest segment i in [0, nseg) with prefix[i] <= x (prefix[0] = 0 <= x):
-// a 64-ary search, one LDS probe per lane per level (two levels for 4096).
-__device__ inline int seg_of(const int64_t* prefix, int nseg, int64_t x, int lane) {
+// Largest segment i in [0, nseg) with prefix[i] <= x (prefix[0] = 0 <= x),
+// by one lane on its own (binary search over the LDS prefix).
+__device__ inline int seg_of(const int64_t* prefix, int nseg, int64_t x) {
   int lo = 0;
-  int n = nseg;
-  while (n > 1) {
-    const int step = (n + kWave - 1) / kWave;
-    const int off = lane * step;
-    const bool ok = off < n && prefix[lo + off] <= x;
-    const int h = __popcll(__ballot(ok)) - 1;  // probes are monotone: lanes 0..h hold
-    lo += h * step;
-    n = min(step, n - h * step);
+  int hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= x) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -341,13 +335,19 @@ __device__ inline int seg_of(const int64_t* prefix, int nseg, int64_t x, int lan
 // that the destination byte it maps to starts a 128-byte line: neighbouring
 // tiles then never share a destination line inside a segment.  Monotone in x.
 __device__ inline int64_t align_boundary(const SegTables& t, int nseg, const uint8_t* target,
-                                         int64_t x, int64_t c_hi, int lane) {
-  const int i = seg_of(t.prefix, nseg, x, lane);
+                                         int64_t x, int64_t c_hi) {
+  const int i = seg_of(t.prefix, nseg, x);
   const uintptr_t a = uintptr_t(target) + uintptr_t(t.dst[i] + (x - t.prefix[i]));
   int64_t y = x + int64_t((0u - a) & 127u);
   if (y > t.prefix[i + 1]) y = t.prefix[i + 1];
   if (y > c_hi) y = c_hi;
   return y;
+}
+
+__device__ inline int64_t readlane64(int64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(uint64_t(v)), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(uint64_t(v) >> 32), lane);
+  return int64_t((uint64_t(hi) << 32) | lo);
 }
 
 // One K2 launch copies the flattened payload bytes [c_lo, c_hi) of the run.
@@ -380,24 +380,43 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   }
   __syncthreads();
 
-  const int64_t ntiles = (c_hi - c_lo + kTileBytes - 1) / kTileBytes;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t x0 = c_lo + t * kTileBytes;
-    const int64_t x1 = x0 + kTileBytes < c_hi ? x0 + kTileBytes : c_hi;
-    const int64_t a = t == 0 ? c_lo : align_boundary(tab, nseg, p.target, x0, c_hi, lane);
-    const int64_t b = x1 >= c_hi ? c_hi : align_boundary(tab, nseg, p.target, x1, c_hi, lane);
-    int64_t x = a;
-    int i = x < b ? seg_of(tab.prefix, nseg, x, lane) : 0;
-    while (x < b) {
-      const int64_t seg_hi = tab.prefix[i + 1];
-      if (seg_hi > x) {
-        const int64_t pe = b < seg_hi ? b : seg_hi;
-        const int64_t off = x - tab.prefix[i];
-        wg_copy_piece(p.input + tab.src[i] + off, p.target + tab.dst[i] + off, pe - x, tid, lane,
-                      wave, slots[wave]);
-        x = pe;
+  // Tile size: at most kTileBytes, chosen so every workgroup gets the same
+  // number of tiles (no workgroup is left with one extra tile at the end).
+  const int64_t len = c_hi - c_lo;
+  const int64_t W = gridDim.x;
+  const int64_t rounds = (len + W * kTileBytes - 1) / (W * kTileBytes);
+  const int64_t tile = rounds > 0 ? ((len + W * rounds - 1) / (W * rounds) + 15) & ~int64_t(15) : 1;
+  const int64_t ntiles = (len + tile - 1) / tile;
+  // A wave works through its workgroup's tiles (blockIdx.x, + W, ...) 64 at a
+  // time: lane l first finds the bounds and first segment of the l-th tile of
+  // the batch, then the wave walks the batch, reading them with readlane.
+  for (int64_t t0 = blockIdx.x; t0 < ntiles; t0 += int64_t(kWave) * W) {
+    const int64_t tl = t0 + int64_t(lane) * W;
+    int64_t la = 0;
+    int64_t lb = 0;
+    int li = 0;
+    if (tl < ntiles) {
+      const int64_t x0 = c_lo + tl * tile;
+      const int64_t x1 = x0 + tile < c_hi ? x0 + tile : c_hi;
+      la = tl == 0 ? c_lo : align_boundary(tab, nseg, p.target, x0, c_hi);
+      lb = x1 >= c_hi ? c_hi : align_boundary(tab, nseg, p.target, x1, c_hi);
+      li = la < lb ? seg_of(tab.prefix, nseg, la) : 0;
+    }
+    for (int j = 0; j < kWave && t0 + int64_t(j) * W < ntiles; ++j) {
+      int64_t x = readlane64(la, j);
+      const int64_t b = readlane64(lb, j);
+      int i = __builtin_amdgcn_readlane(li, j);
+      while (x < b) {
+        const int64_t seg_hi = tab.prefix[i + 1];
+        if (seg_hi > x) {
+          const int64_t pe = b < seg_hi ? b : seg_hi;
+          const int64_t off = x - tab.prefix[i];
+          wg_copy_piece(p.input + tab.src[i] + off, p.target + tab.dst[i] + off, pe - x, tid,
+                        lane, wave, slots[wave]);
+          x = pe;
+        }
+        ++i;
       }
-      ++i;
     }
   }
 
