@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.a2av_oracle_run.restype = ctypes.c_int
         L.a2av_oracle_check.argtypes = run_args
         L.a2av_oracle_check.restype = ctypes.c_int
+        L.a2av_oracle_run_blocked.argtypes = run_args + [i32]
+        L.a2av_oracle_run_blocked.restype = ctypes.c_int
         L.a2av_oracle_displacements.argtypes = [vp, i32, i32, vp, vp]
         L.a2av_oracle_displacements.restype = None
         L.a2av_oracle_move.argtypes = [vp, vp, vp, i32, i32, i64, i64]
@@ -109,6 +111,22 @@ def run(input_bytes: np.ndarray, target_bytes: np.ndarray, signal: np.ndarray,
     return int(lib().a2av_oracle_run(
         _ptr(input_bytes), _ptr(target_bytes), _ptr(signal), _ptr(send_counts),
         _ptr(recv_counts), P, S, in_slab, tgt_slab, core_num, dtype, capacity))
+
+
+def run_blocked(input_bytes: np.ndarray, target_bytes: np.ndarray, signal: np.ndarray,
+                send_counts: np.ndarray, recv_counts: np.ndarray, *, P: int, S: int,
+                in_slab: int, tgt_slab: int, core_num: int, dtype: int, nblk: int,
+                capacity: int = 0) -> int:
+    """The blocked exchange (each segment is nblk sub-blocks read from the
+    source's block-rows); nblk = 1 is :func:`run`.  Same buffers as run."""
+    for a, n in ((input_bytes, P * in_slab), (target_bytes, P * tgt_slab)):
+        assert a.dtype == np.uint8 and a.size == n
+    assert signal.dtype == np.int32 and signal.size == P * S
+    assert send_counts.dtype == np.int32 and send_counts.size == P * P
+    assert recv_counts.dtype == np.int32 and recv_counts.size == P * P
+    return int(lib().a2av_oracle_run_blocked(
+        _ptr(input_bytes), _ptr(target_bytes), _ptr(signal), _ptr(send_counts),
+        _ptr(recv_counts), P, S, in_slab, tgt_slab, core_num, dtype, capacity, nblk))
 
 
 def check(input_ptr, target_ptr, signal_ptr, send_ptr, recv_ptr, *, P, S, in_slab,

@@ -97,6 +97,8 @@ static int ranges_overlap(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb)
  *      rule of "Current limitations")                   -> INVALID_ARGS
  *   8. a slab size that is not a whole number of elements -> INVALID_ARGS
  *   9. a negative count                                 -> INVALID_ARGS
+ *  9b. (blocked exchange only) a count that nblk does not divide
+ *                                                       -> INVALID_ARGS
  *  10. a source row or destination column whose bytes exceed its slab
  *                                                       -> OVER_CAPACITY
  *  11. signal[r][b] (r < P, b < B) not all equal        -> INVALID_ARGS
@@ -107,13 +109,13 @@ static int ranges_overlap(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb)
 static int check_args(const void *input, const void *target, const int32_t *signal,
                       const int32_t *send_counts, const int32_t *recv_counts,
                       int32_t P, int32_t S, int64_t in_slab, int64_t tgt_slab,
-                      int64_t core_num, int32_t dtype, int64_t capacity)
+                      int64_t core_num, int32_t dtype, int64_t capacity, int32_t nblk)
 {
     if (!input || !target || !signal || !send_counts || !recv_counts)
         return OR_ERR_NULLPTR;
     if (dtype != OR_DTYPE_FP32 && dtype != OR_DTYPE_INT8)
         return OR_ERR_UNSUPPORTED_DTYPE;
-    if (P < 1 || P > OR_MAX_P || S < 1 || in_slab < 1 || tgt_slab < 1)
+    if (P < 1 || P > OR_MAX_P || S < 1 || in_slab < 1 || tgt_slab < 1 || nblk < 1)
         return OR_ERR_INVALID_ARGS;
     if (core_num < 1 || core_num > OR_INT32_MAX)
         return OR_ERR_INVALID_ARGS;
@@ -140,6 +142,10 @@ static int check_args(const void *input, const void *target, const int32_t *sign
     for (int32_t s = 0; s < P; ++s)
         for (int32_t d = 0; d < P; ++d)
             if (send_counts[s * P + d] < 0)
+                return OR_ERR_INVALID_ARGS;
+    for (int32_t s = 0; s < P; ++s)
+        for (int32_t d = 0; d < P; ++d)
+            if (send_counts[s * P + d] % nblk != 0)
                 return OR_ERR_INVALID_ARGS;
 
     for (int32_t s = 0; s < P; ++s) {
@@ -172,7 +178,7 @@ int a2av_oracle_check(const void *input, const void *target, const int32_t *sign
                       int64_t core_num, int32_t dtype, int64_t capacity)
 {
     return check_args(input, target, signal, send_counts, recv_counts, P, S, in_slab,
-                      tgt_slab, core_num, dtype, capacity);
+                      tgt_slab, core_num, dtype, capacity, 1);
 }
 
 /*
@@ -263,7 +269,7 @@ int a2av_oracle_run(const void *input, void *target, int32_t *signal,
                     int64_t core_num, int32_t dtype, int64_t capacity)
 {
     int st = check_args(input, target, signal, send_counts, recv_counts, P, S, in_slab,
-                        tgt_slab, core_num, dtype, capacity);
+                        tgt_slab, core_num, dtype, capacity, 1);
     if (st != OR_OK)
         return st;
     int64_t e = elem_size(dtype);
@@ -274,6 +280,64 @@ int a2av_oracle_run(const void *input, void *target, int32_t *signal,
     displacements(send_counts, P, e, sdispl, rdispl);
     move_segments((const uint8_t *)input, (uint8_t *)target, send_counts, P, e, in_slab,
                   tgt_slab, sdispl, rdispl);
+    arrive(signal, P, S, B);
+    return OR_OK;
+}
+
+/*
+ * The blocked exchange: the AllToAll at the end of the CANN
+ * BatchMatMulReduceScatterAllToAll op ("Function and computation flow",
+ * "Constraints": per rank temp3 is (E/ep, ep*C, H/tp) and y is (E, C, H/tp)),
+ * taken on the source's own layout instead of after a pack into
+ * destination order.  Source slab s is nblk block-rows; block-row a holds,
+ * for d = 0..P-1 in order, the a-th of the nblk equal sub-blocks of the
+ * segment s -> d (send_counts[s][d] / nblk elements each).  Destination
+ * slab d receives segment s -> d at rdispl[d][s] as before, its sub-blocks
+ * in order a = 0..nblk-1:
+ *   target[d*tgt_slab + rdispl[d][s] + a*sub .. + sub) =
+ *   input [s*in_slab + a*row_s/nblk + sdispl[s][d]/nblk .. + sub)
+ * with sub = send_counts[s][d]*e/nblk and row_s the bytes source s sends.
+ * With E/ep experts per rank, ep ranks, C tokens per expert and H/tp
+ * hidden: nblk = E/ep and every count is C*H/tp*nblk, so block-row a is
+ * expert a's (ep*C, H/tp) slice and sub-block d of it is rows d*C..d*C+C.
+ * nblk = 1 is the plain exchange.  nblk < 1 is INVALID_ARGS among the
+ * geometry checks; a count that nblk does not divide is INVALID_ARGS right
+ * after the negative-count check (check 9b).
+ * Pinned by: nblk = 1 equals a2av_oracle_run; the CANN layout relation
+ * checked against numpy's transpose of (P, A, P, Q) to (P, P, A, Q); brute
+ * force for tiny P in the tests.
+ */
+int a2av_oracle_run_blocked(const void *input, void *target, int32_t *signal,
+                            const int32_t *send_counts, int32_t *recv_counts, int32_t P,
+                            int32_t S, int64_t in_slab, int64_t tgt_slab, int64_t core_num,
+                            int32_t dtype, int64_t capacity, int32_t nblk)
+{
+    int st = check_args(input, target, signal, send_counts, recv_counts, P, S, in_slab,
+                        tgt_slab, core_num, dtype, capacity, nblk);
+    if (st != OR_OK)
+        return st;
+
+    int64_t e = elem_size(dtype);
+    int64_t B = a2av_oracle_blocks(P, core_num);
+    int64_t sdispl[OR_MAX_P * OR_MAX_P];
+    int64_t rdispl[OR_MAX_P * OR_MAX_P];
+    transpose_counts(send_counts, recv_counts, P);
+    displacements(send_counts, P, e, sdispl, rdispl);
+    for (int32_t s = 0; s < P; ++s) {
+        int64_t row = 0;
+        for (int32_t d = 0; d < P; ++d)
+            row += (int64_t)send_counts[s * P + d] * e;
+        for (int32_t d = 0; d < P; ++d) {
+            int64_t sub = (int64_t)send_counts[s * P + d] * e / nblk;
+            if (sub == 0)
+                continue;
+            for (int32_t a = 0; a < nblk; ++a)
+                memcpy((uint8_t *)target + (int64_t)d * tgt_slab + rdispl[d * P + s] + a * sub,
+                       (const uint8_t *)input + (int64_t)s * in_slab + a * (row / nblk) +
+                           sdispl[s * P + d] / nblk,
+                       (size_t)sub);
+        }
+    }
     arrive(signal, P, S, B);
     return OR_OK;
 }

@@ -31,6 +31,37 @@ def exchange(input_slabs: list[bytes], target_slabs: list[bytes],
     return out
 
 
+def exchange_blocked(input_slabs: list[bytes], target_slabs: list[bytes],
+                     counts: list[list[int]], elem_size: int, nblk: int) -> list[bytes]:
+    """The blocked exchange by byte concatenation.
+
+    Source slab s is read as nblk equal block-rows; each block-row lists the
+    sub-blocks for destinations 0..P-1 in order, sub-block d being
+    counts[s][d] / nblk elements.  Destination d receives, for s ascending,
+    the nblk sub-blocks of s's segment in block-row order.
+    """
+    P = len(input_slabs)
+    pieces: dict[tuple[int, int], bytes] = {}
+    for s in range(P):
+        subs = [counts[s][d] * elem_size // nblk for d in range(P)]
+        row = sum(subs)                      # bytes per block-row
+        parts = {d: b"" for d in range(P)}
+        for a in range(nblk):
+            block = input_slabs[s][a * row:(a + 1) * row]
+            pos = 0
+            for d in range(P):
+                parts[d] += block[pos:pos + subs[d]]
+                pos += subs[d]
+        for d in range(P):
+            pieces[(s, d)] = parts[d]
+    out = []
+    for d in range(P):
+        received = b"".join(pieces[(s, d)] for s in range(P))
+        old = target_slabs[d]
+        out.append(received + old[len(received):])
+    return out
+
+
 def transpose(counts: list[list[int]]) -> list[list[int]]:
     P = len(counts)
     return [[counts[s][d] for s in range(P)] for d in range(P)]

@@ -392,3 +392,110 @@ def test_workload_shapes():
     assert (w4.counts == 0).sum() >= 205 and w4.counts.max() <= 2**19
     w2 = wl.workload(2)
     assert (w2.counts == 0).sum() >= 6
+
+
+# ------------------------------------------------------------------- blocked exchange
+
+def _run_blocked(C, P, dtype, in_slab, tgt_slab, nblk, core_num=1, seed=4):
+    C = np.ascontiguousarray(C, np.int32)
+    S = max(1, oracle.blocks(P, core_num))
+    inp = wl.random_bytes_np(seed, 0, P * in_slab)
+    tgt = np.full(P * tgt_slab, wl.SENTINEL, np.uint8)
+    sig = np.zeros((P, S), np.int32)
+    rc = np.full((P, P), -7, np.int32)
+    st = oracle.run_blocked(inp, tgt, sig, C, rc, P=P, S=S, in_slab=in_slab, tgt_slab=tgt_slab,
+                            core_num=core_num, dtype=dtype, nblk=nblk)
+    return st, inp, tgt, sig, rc
+
+
+@pytest.mark.parametrize("dtype", [wl.FP32, wl.INT8])
+def test_blocked_with_one_block_is_the_plain_exchange(dtype):
+    rng = np.random.default_rng(31)
+    P = 6
+    e = wl.ELEM_SIZE[dtype]
+    C = rng.integers(0, 50, size=(P, P)).astype(np.int32)
+    slab = 50 * P * e + 24
+    a = _run(C, P, dtype, slab, slab, core_num=4)
+    b = _run_blocked(C, P, dtype, slab, slab, 1, core_num=4, seed=3)
+    assert a[0] == b[0] == oracle.OK
+    for x, y in zip(a[1:], b[1:]):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("P,A,Q", [(2, 3, 5), (4, 2, 8), (3, 4, 1), (8, 8, 3)])
+def test_blocked_equal_counts_is_numpy_transpose(P, A, Q):
+    # Source slab s viewed as (A, P, Q): expert block a, destination rows d.
+    C = np.full((P, P), A * Q, np.int32)
+    slab = P * A * Q * 4
+    st, inp, tgt, _, _ = _run_blocked(C, P, wl.FP32, slab, slab, A)
+    assert st == oracle.OK
+    src = inp.view(np.int32).reshape(P, A, P, Q)
+    want = src.transpose(2, 0, 1, 3).reshape(-1)
+    np.testing.assert_array_equal(tgt.view(np.int32), want)
+
+
+def test_blocked_cann_example_layout():
+    g = json.load(open(os.path.join(GOLDEN, "bmm_rs_a2a_example.json")))
+    ep, tp, E, Cc, H = g["EP"], g["TP"], g["E"], g["C"], g["H"]
+    Eop, Hot = E // ep, H // tp
+    P = ep
+    # temp3 on source p in its own layout (E/ep, ep*C, H/tp), values encode (p, e, row, h).
+    vals = np.zeros((P, Eop, ep * Cc, Hot), np.int64)
+    for p_, e_, r_, h_ in itertools.product(range(P), range(Eop), range(ep * Cc), range(Hot)):
+        vals[p_, e_, r_, h_] = ((p_ * Eop + e_) * ep * Cc + r_) * Hot + h_
+    inp = vals.astype(np.int32).view(np.uint8).reshape(-1).copy()
+    n = Eop * Cc * Hot
+    slab = P * n * 4
+    tgt = np.zeros(P * slab, np.uint8)
+    sig = np.zeros((P, 1), np.int32)
+    rc = np.zeros((P, P), np.int32)
+    C = np.full((P, P), n, np.int32)
+    assert oracle.run_blocked(inp, tgt, sig, C, rc, P=P, S=1, in_slab=slab, tgt_slab=slab,
+                              core_num=1, dtype=wl.FP32, nblk=Eop) == oracle.OK
+    y = tgt.view(np.int32).reshape(P, E, Cc, Hot)          # y on rank j: (E, C, H/tp)
+    for j, p_, e_ in itertools.product(range(P), range(P), range(Eop)):
+        want = vals[p_, e_, j * Cc:(j + 1) * Cc, :].astype(np.int32)
+        np.testing.assert_array_equal(y[j, p_ * Eop + e_], want)
+
+
+@pytest.mark.parametrize("dtype", [wl.FP32, wl.INT8])
+@pytest.mark.parametrize("nblk", [2, 3])
+def test_blocked_brute_force(dtype, nblk):
+    rng = np.random.default_rng(nblk * 10 + dtype)
+    e = wl.ELEM_SIZE[dtype]
+    for P in (2, 3, 4):
+        for _ in range(15):
+            C = (rng.integers(0, 6, size=(P, P)) * nblk).astype(np.int32)
+            in_slab = 6 * nblk * P * e + 3 * e
+            tgt_slab = 6 * nblk * P * e + 5 * e
+            st, inp, tgt, _, rc = _run_blocked(C, P, dtype, in_slab, tgt_slab, nblk,
+                                               seed=int(rng.integers(1 << 30)))
+            assert st == oracle.OK
+            in_slabs = [bytes(inp[s * in_slab:(s + 1) * in_slab]) for s in range(P)]
+            old = [bytes([wl.SENTINEL]) * tgt_slab for _ in range(P)]
+            want = brute.exchange_blocked(in_slabs, old, C.tolist(), e, nblk)
+            got = [bytes(tgt[d * tgt_slab:(d + 1) * tgt_slab]) for d in range(P)]
+            assert got == want, (P, C.tolist())
+            np.testing.assert_array_equal(rc, C.T)
+
+
+def test_blocked_diagnostics():
+    P = 4
+    C = np.full((P, P), 6, np.int32)
+    st, _, tgt, sig, rc = _run_blocked(C, P, wl.INT8, 64, 64, 4)     # 6 % 4 != 0
+    assert st == oracle.ERR_INVALID_ARGS
+    assert (tgt == wl.SENTINEL).all() and (sig == 0).all() and (rc == -7).all()
+    st, *_ = _run_blocked(C, P, wl.INT8, 64, 64, 0)                   # nblk < 1
+    assert st == oracle.ERR_INVALID_ARGS
+    st, *_ = _run_blocked(C, P, wl.INT8, 64, 64, 3)                   # divides: fine
+    assert st == oracle.OK
+    C2 = C.copy()
+    C2[0, 0] = -3                                                     # negative wins
+    st, *_ = _run_blocked(C2, P, wl.INT8, 64, 64, 4)
+    assert st == oracle.ERR_INVALID_ARGS
+    C3 = np.full((P, P), 7, np.int32)                                 # 7 % 2 and over capacity
+    st, *_ = _run_blocked(C3, P, wl.INT8, 16, 16, 2)
+    assert st == oracle.ERR_INVALID_ARGS                              # divisibility first
+    C4 = np.full((P, P), 8, np.int32)
+    st, *_ = _run_blocked(C4, P, wl.INT8, 16, 16, 2)
+    assert st == oracle.ERR_OVER_CAPACITY
