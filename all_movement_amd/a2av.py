@@ -32,7 +32,7 @@ INT8 = 1
 ELEM_SIZE = {FP32: 4, INT8: 1}
 FLAG_PROFILE = 1
 
-EXPORTS = ["a2av_create", "a2av_run", "a2av_destroy", "a2av_blocks", "a2av_check_args",
+EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_destroy", "a2av_blocks", "a2av_check_args",
            "a2av_query_error", "a2av_launch_info_get", "a2av_profile_read",
            "a2av_status_string", "a2av_last_hip_error"]
 
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.a2av_create.restype = ctypes.c_int
     L.a2av_run.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, vp]
     L.a2av_run.restype = ctypes.c_int
+    L.a2av_run_blocked.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
+    L.a2av_run_blocked.restype = ctypes.c_int
     L.a2av_destroy.argtypes = [vp]
     L.a2av_destroy.restype = ctypes.c_int
     L.a2av_blocks.argtypes = [i64, i64]
@@ -105,6 +107,12 @@ def a2av_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dt
              stream) -> int:
     return lib().a2av_run(h, input, target, signal, send_counts, recv_counts, P, core_num,
                           dtype, stream)
+
+
+def a2av_run_blocked(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype,
+                     nblk, stream) -> int:
+    return lib().a2av_run_blocked(h, input, target, signal, send_counts, recv_counts, P,
+                                  core_num, dtype, nblk, stream)
 
 
 def a2av_destroy(h) -> int:
@@ -216,7 +224,8 @@ class Exchange:
         return t.data_ptr()
 
     def run(self, input, target, signal, send_counts, recv_counts, core_num: int, dtype: int,
-            stream=None) -> None:
+            stream=None, nblk: int = 1) -> None:
+        """One exchange; ``nblk`` > 1 runs the blocked exchange (a2av_run_blocked)."""
         import torch
         c = self.cfg
         P = c.P
@@ -227,7 +236,11 @@ class Exchange:
         rcp = self._check(recv_counts, P * P * 4, "recv_counts", torch.int32)
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
-        st = a2av_run(self.h, ip, tp, sp, scp, rcp, P, core_num, dtype, stream.cuda_stream)
+        if nblk == 1:
+            st = a2av_run(self.h, ip, tp, sp, scp, rcp, P, core_num, dtype, stream.cuda_stream)
+        else:
+            st = a2av_run_blocked(self.h, ip, tp, sp, scp, rcp, P, core_num, dtype, nblk,
+                                  stream.cuda_stream)
         _raise(st, "a2av_run", self.h)
 
     def query_error(self) -> int:

@@ -24,6 +24,7 @@ struct Workspace {
   int64_t* src_off;  // [P*P] byte offset of segment (s, d) inside `input`
   int64_t* dst_off;  // [P*P] byte offset of segment (s, d) inside `target`
   uint32_t* blk_cnt; // [max blocks] workgroups of each block that finished copying
+  int64_t* sstride;  // [P] bytes per source block-row (blocked exchange)
 };
 
 struct CountParams {
@@ -37,6 +38,7 @@ struct CountParams {
   int32_t S;
   int32_t B;
   int32_t elem;
+  int32_t nblk;       // sub-blocks per segment (1 = plain exchange)
 };
 
 struct CopyParams {
@@ -51,6 +53,7 @@ struct CopyParams {
   int32_t S;
   int32_t B;
   int32_t G;          // workgroups per admitted block
+  int32_t nblk;       // sub-blocks per segment (1 = plain exchange)
   int32_t last;       // 1 on the run's final launch: raise the block flags
   int32_t wait;       // 1 when the final launch is cooperative (B > 1): wait for all blocks
   int32_t spin_limit;

@@ -76,8 +76,8 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   if (tid == 0) flags = 0;
   __syncthreads();
 
-  // Load the counts; note negatives (bit 0) and a signal that is not uniform
-  // over the admitted entries (bit 2).
+  // Load the counts; note negatives (bit 0), counts nblk does not divide
+  // (bit 3) and a signal that is not uniform over the admitted entries (bit 2).
   // The loops are unrolled so each thread issues its loads back to back.
   int bad = 0;
 #pragma unroll 4
@@ -85,6 +85,7 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     const int32_t c = p.send_counts[i];
     C[i] = c;
     bad |= c < 0 ? 1 : 0;
+    bad |= c % p.nblk != 0 ? 8 : 0;
   }
   const int32_t base = p.signal[0];
   for (int r = wave; r < P; r += kWaves) {
@@ -117,7 +118,10 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   const int f = flags;
   if (f != 0) {
     if (tid == 0) {
+      // Order: negative count, count not divisible by nblk, over-capacity,
+      // unequal signal.
       const int code = (f & 1) ? A2AV_ERR_INVALID_ARGS
+                     : (f & 8) ? A2AV_ERR_INVALID_ARGS
                      : (f & 2) ? A2AV_ERR_OVER_CAPACITY
                                : A2AV_ERR_INVALID_ARGS;
       atomicCAS(&p.ws.plan->error, 0, code);
@@ -137,13 +141,19 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   __syncthreads();
 
   // Send side: exclusive scan along d of row s (input packed by destination).
+  // The blocked exchange scans the sub-block sizes instead: segment s -> d
+  // starts at its sub-block's offset inside block-row 0 of source s, and the
+  // following block-rows are sstride[s] bytes apart.
   for (int s = wave; s < P; s += kWaves) {
     const int64_t v = lane < P ? int64_t(C[s * P + lane]) * p.elem : 0;
-    const int64_t ex = wave_inclusive_scan(v, lane) - v;
+    const int64_t incl = wave_inclusive_scan(v, lane);
+    const int64_t sub = v / p.nblk;
+    const int64_t sub_ex = wave_inclusive_scan(sub, lane) - sub;
     if (lane < P) {
-      p.ws.src_off[s * P + lane] = int64_t(s) * p.in_slab + ex;
-      p.ws.prefix[s * P + lane] = rowbase[s] + ex;
+      p.ws.src_off[s * P + lane] = int64_t(s) * p.in_slab + sub_ex;
+      p.ws.prefix[s * P + lane] = rowbase[s] + (incl - v);
     }
+    if (lane == kWave - 1) p.ws.sstride[s] = incl / p.nblk;
   }
   // Receive side: exclusive scan along s of column d (target packed by source).
   for (int d = wave; d < P; d += kWaves) {
@@ -317,6 +327,7 @@ struct SegTables {
   int64_t prefix[kMaxP * kMaxP + 1];
   int64_t src[kMaxP * kMaxP];
   int64_t dst[kMaxP * kMaxP];
+  int64_t sstride[kMaxP];  // bytes per source block-row (blocked exchange)
 };
 
 // Largest segment i in [0, nseg) with prefix[i] <= x (prefix[0] = 0 <= x),
@@ -350,6 +361,39 @@ __device__ inline int64_t readlane64(int64_t v, int lane) {
   return int64_t((uint64_t(hi) << 32) | lo);
 }
 
+// Copy the flattened bytes [x, b) that start in segment i, piece by piece.
+// The target side of a segment is contiguous.  In the blocked exchange the
+// source side is nblk sub-blocks, sub-block a at tab.src[i] + a * sstride[s],
+// so a piece is also cut where a sub-block ends.
+__device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int64_t x, int64_t b,
+                                  int i, int tid, int lane, int wave, u32x4* slot) {
+  while (x < b) {
+    const int64_t seg_lo = tab.prefix[i];
+    const int64_t seg_hi = tab.prefix[i + 1];
+    if (seg_hi > x) {
+      const int64_t pe = b < seg_hi ? b : seg_hi;
+      if (p.nblk == 1) {
+        const int64_t off = x - seg_lo;
+        wg_copy_piece(p.input + tab.src[i] + off, p.target + tab.dst[i] + off, pe - x, tid,
+                      lane, wave, slot);
+      } else {
+        const int64_t sub = (seg_hi - seg_lo) / p.nblk;
+        const int64_t stride = tab.sstride[i / p.P];
+        for (int64_t off = x - seg_lo; off < pe - seg_lo;) {
+          const int64_t a = off / sub;
+          const int64_t w = off - a * sub;
+          const int64_t end = (a + 1) * sub < pe - seg_lo ? (a + 1) * sub : pe - seg_lo;
+          wg_copy_piece(p.input + tab.src[i] + a * stride + w, p.target + tab.dst[i] + off,
+                        end - off, tid, lane, wave, slot);
+          off = end;
+        }
+      }
+      x = pe;
+    }
+    ++i;
+  }
+}
+
 // One K2 launch copies the flattened payload bytes [c_lo, c_hi) of the run.
 // The range is cut into 128 KiB tiles dealt round-robin to the workgroups, so
 // at any moment the grid streams through one narrow window of the source and
@@ -378,6 +422,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
     tab.src[i] = p.ws.src_off[i];
     tab.dst[i] = p.ws.dst_off[i];
   }
+  if (tid < p.P) tab.sstride[tid] = p.ws.sstride[tid];
   __syncthreads();
 
   // Tile size: at most kTileBytes, chosen so every workgroup gets the same
@@ -403,20 +448,8 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
       li = la < lb ? seg_of(tab.prefix, nseg, la) : 0;
     }
     for (int j = 0; j < kWave && t0 + int64_t(j) * W < ntiles; ++j) {
-      int64_t x = readlane64(la, j);
-      const int64_t b = readlane64(lb, j);
-      int i = __builtin_amdgcn_readlane(li, j);
-      while (x < b) {
-        const int64_t seg_hi = tab.prefix[i + 1];
-        if (seg_hi > x) {
-          const int64_t pe = b < seg_hi ? b : seg_hi;
-          const int64_t off = x - tab.prefix[i];
-          wg_copy_piece(p.input + tab.src[i] + off, p.target + tab.dst[i] + off, pe - x, tid,
-                        lane, wave, slots[wave]);
-          x = pe;
-        }
-        ++i;
-      }
+      copy_range(p, tab, readlane64(la, j), readlane64(lb, j), __builtin_amdgcn_readlane(li, j),
+                 tid, lane, wave, slots[wave]);
     }
   }
 

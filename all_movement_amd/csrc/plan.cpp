@@ -42,12 +42,13 @@ bool overlap(const Range& a, const Range& b) {
 
 int check_run_args(const a2av_config* cfg, int64_t capacity, const void* input,
                    const void* target, const int32_t* signal, const int32_t* send_counts,
-                   const int32_t* recv_counts, int32_t P, int64_t core_num, int32_t dtype) {
+                   const int32_t* recv_counts, int32_t P, int64_t core_num, int32_t dtype,
+                   int32_t nblk) {
   if (!cfg || !input || !target || !signal || !send_counts || !recv_counts)
     return A2AV_ERR_NULLPTR;
   if (dtype != A2AV_FP32 && dtype != A2AV_INT8) return A2AV_ERR_UNSUPPORTED_DTYPE;
   if (check_config(cfg) != A2AV_OK) return A2AV_ERR_INVALID_ARGS;
-  if (P != cfg->P) return A2AV_ERR_INVALID_ARGS;
+  if (P != cfg->P || nblk < 1) return A2AV_ERR_INVALID_ARGS;
   if (core_num < 1 || core_num > kInt32Max) return A2AV_ERR_INVALID_ARGS;
   const int64_t B = fold_blocks(P, core_num);
   if (int64_t(cfg->S) < B) return A2AV_ERR_INVALID_ARGS;

@@ -23,10 +23,12 @@ int64_t elem_bytes(int32_t dtype);
 // Geometry checks done once by a2av_create.
 int check_config(const a2av_config* cfg);
 
-// The host-side checks of a2av_run, in the documented order.
+// The host-side checks of a2av_run / a2av_run_blocked, in the documented
+// order (nblk = 1 for a2av_run).
 int check_run_args(const a2av_config* cfg, int64_t capacity, const void* input,
                    const void* target, const int32_t* signal, const int32_t* send_counts,
-                   const int32_t* recv_counts, int32_t P, int64_t core_num, int32_t dtype);
+                   const int32_t* recv_counts, int32_t P, int64_t core_num, int32_t dtype,
+                   int32_t nblk = 1);
 
 // Upper bound of the payload of any valid run: every row fits its input slab
 // and every column its target slab, so T <= P * min(in_slab, tgt_slab).

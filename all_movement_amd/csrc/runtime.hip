@@ -131,7 +131,7 @@ int a2av_create(a2av_handle** out, const a2av_config* cfg) {
   h->spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
 
   // Workspace: plan words, prefix[P*P+1], src_off[P*P], dst_off[P*P],
-  // blk_cnt[max(1, capacity)], each 256-byte aligned.
+  // blk_cnt[max(1, capacity)], sstride[P], each 256-byte aligned.
   const size_t PP = size_t(cfg->P) * size_t(cfg->P);
   const size_t max_blocks = size_t(h->capacity > 1 ? h->capacity : 1);
   size_t off = 0;
@@ -140,6 +140,7 @@ int a2av_create(a2av_handle** out, const a2av_config* cfg) {
   const size_t o_src = off; off = round_up(off + PP * sizeof(int64_t), 256);
   const size_t o_dst = off; off = round_up(off + PP * sizeof(int64_t), 256);
   const size_t o_cnt = off; off = round_up(off + max_blocks * sizeof(uint32_t), 256);
+  const size_t o_str = off; off = round_up(off + size_t(cfg->P) * sizeof(int64_t), 256);
   e = hipMalloc(&h->ws_mem, off);
   if (e != hipSuccess) { delete h; return A2AV_ERR_HIP; }
   e = hipMemset(h->ws_mem, 0, off);
@@ -150,6 +151,7 @@ int a2av_create(a2av_handle** out, const a2av_config* cfg) {
   h->ws.src_off = reinterpret_cast<int64_t*>(base + o_src);
   h->ws.dst_off = reinterpret_cast<int64_t*>(base + o_dst);
   h->ws.blk_cnt = reinterpret_cast<uint32_t*>(base + o_cnt);
+  h->ws.sstride = reinterpret_cast<int64_t*>(base + o_str);
 
   h->profile = (cfg->flags & A2AV_FLAG_PROFILE) != 0;
   if (h->profile) {
@@ -195,12 +197,12 @@ int a2av_launch_info_get(a2av_handle* h, int64_t core_num, a2av_launch_info* out
   return A2AV_OK;
 }
 
-int a2av_run(a2av_handle* h, const void* input, void* target, int32_t* signal,
-             const int32_t* send_counts, int32_t* recv_counts, int32_t P, int64_t core_num,
-             int32_t dtype, void* stream) {
+int a2av_run_blocked(a2av_handle* h, const void* input, void* target, int32_t* signal,
+                     const int32_t* send_counts, int32_t* recv_counts, int32_t P,
+                     int64_t core_num, int32_t dtype, int32_t nblk, void* stream) {
   if (!h) return A2AV_ERR_NULLPTR;
   int st = a2av::check_run_args(&h->cfg, h->capacity, input, target, signal, send_counts,
-                                recv_counts, P, core_num, dtype);
+                                recv_counts, P, core_num, dtype, nblk);
   if (st != A2AV_OK) return st;
   a2av_launch_info li;
   st = a2av_launch_info_get(h, core_num, &li);
@@ -222,6 +224,7 @@ int a2av_run(a2av_handle* h, const void* input, void* target, int32_t* signal,
   cp.S = h->cfg.S;
   cp.B = int32_t(li.blocks);
   cp.elem = int32_t(a2av::elem_bytes(dtype));
+  cp.nblk = nblk;
 
   hipEvent_t* ev = nullptr;
   if (h->profile)
@@ -240,6 +243,7 @@ int a2av_run(a2av_handle* h, const void* input, void* target, int32_t* signal,
   kp.S = h->cfg.S;
   kp.B = int32_t(li.blocks);
   kp.G = li.wg_per_block;
+  kp.nblk = nblk;
   kp.spin_limit = h->spin_limit;
   // Chunks are issued from the highest to chunk 0.  Chunks past the run's
   // payload cost only a plain launch that exits at once, and the final launch
@@ -262,6 +266,13 @@ int a2av_run(a2av_handle* h, const void* input, void* target, int32_t* signal,
     ++h->profiled_runs;
   }
   return A2AV_OK;
+}
+
+int a2av_run(a2av_handle* h, const void* input, void* target, int32_t* signal,
+             const int32_t* send_counts, int32_t* recv_counts, int32_t P, int64_t core_num,
+             int32_t dtype, void* stream) {
+  return a2av_run_blocked(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype,
+                          1, stream);
 }
 
 int a2av_query_error(a2av_handle* h) {

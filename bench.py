@@ -25,7 +25,11 @@ if ROOT not in sys.path:
 
 METRIC = "all_to_all_v achieved HBM GB/s (read+write) and % of MI355X peak, 1 GPU"
 PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
-WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
+# name -> (workload index, sub-blocks per segment).  c5u is c5's exchange taken
+# on the source's own temp3 layout (E/ep, ep*C, H/tp): the blocked exchange
+# with nblk = E/ep = 8.
+WORKLOADS = {"c1": (1, 1), "c2": (2, 1), "c3": (3, 1), "c4": (4, 1), "c5": (5, 1),
+             "c5u": (5, 8)}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "copy_kernel_traffic.json")
 
 
@@ -53,13 +57,15 @@ def measured_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
-def run_gpu(k: int, steps: int, warmup: int):
+def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
     import torch
     from all_movement_amd import a2av
     from all_movement_amd import workloads as wl
 
     dev = torch.device("cuda:0")
     w = wl.workload(k)
+    if nblk > 1:
+        w.name += f"_temp3_layout_nblk{nblk}"
     log(f"[bench] {w.name}: payload {w.payload_bytes} B, generating inputs on the GPU")
     inp = wl.input_tensor(w, dev)
     tgt = torch.full((w.tgt_bytes,), wl.SENTINEL, dtype=torch.uint8, device=dev)
@@ -72,7 +78,7 @@ def run_gpu(k: int, steps: int, warmup: int):
     torch.cuda.synchronize()
 
     for _ in range(warmup):
-        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream)
+        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, nblk=nblk)
     torch.cuda.synchronize()
     if ex.query_error() != a2av.OK:
         raise RuntimeError("warmup run reported a device-side error")
@@ -80,7 +86,7 @@ def run_gpu(k: int, steps: int, warmup: int):
 
     t0 = time.perf_counter()
     for _ in range(steps):
-        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream)
+        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, nblk=nblk)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if ex.query_error() != a2av.OK:
@@ -170,7 +176,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="c3,c4", help="other workloads reported beside it")
+    ap.add_argument("--also", default="c3,c4,c5u", help="other workloads reported beside it")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain torch device copy of MIB MiB --steps times (the "
@@ -185,14 +191,14 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe << 20, args.steps)
         return
-    k = WORKLOADS[args.workload]
-    main_res = run_gpu(k, args.steps, args.warmup)
+    k, nblk = WORKLOADS[args.workload]
+    main_res = run_gpu(k, args.steps, args.warmup, nblk)
     w, info = main_res["w"], main_res["info"]
     log(f"[bench] {w.name}: {main_res['gbps']:.1f} GB/s whole run, K2 "
         f"{main_res['k2_gbps']:.1f} GB/s, {main_res['ms_per_step']:.3f} ms/step")
     also = {}
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
-        r = run_gpu(WORKLOADS[name], args.steps, args.warmup)
+        r = run_gpu(*WORKLOADS[name][:1], args.steps, args.warmup, WORKLOADS[name][1])
         log(f"[bench] {r['w'].name}: {r['gbps']:.1f} GB/s whole run, K2 {r['k2_gbps']:.1f} GB/s")
         also[r["w"].name] = {"value": round(r["gbps"], 1), "frac_of_peak": round(r["gbps"] / PEAK_GBPS, 4),
                              "k2_gbps": round(r["k2_gbps"], 1), "ms_per_step": round(r["ms_per_step"], 4),

@@ -132,6 +132,28 @@ int a2av_run(a2av_handle *h, const void *input, void *target, int32_t *signal,
              const int32_t *send_counts, int32_t *recv_counts, int32_t P, int64_t core_num,
              int32_t dtype, void *stream);
 
+/*
+ * The blocked exchange: a2av_run where each segment s -> d is read from the
+ * source as nblk equal sub-blocks instead of one contiguous run.  Source slab
+ * s is nblk block-rows of row_s/nblk bytes (row_s = the bytes s sends); each
+ * block-row lists the sub-blocks for destinations 0..P-1 in order, sub-block
+ * d being send_counts[s][d]/nblk elements.  The target is as in a2av_run:
+ * segment s -> d lands at rdispl[d][s], its sub-blocks in block-row order.
+ * This is the AllToAll at the end of the CANN
+ * BatchMatMulReduceScatterAllToAll op taken on the source's own layout
+ * ("Function and computation flow", "Constraints": per rank temp3 is
+ * (E/ep, ep*C, H/tp), y is (E, C, H/tp)): with nblk = E/ep and every count
+ * C*H/tp*nblk, block-row a is expert a's (ep*C, H/tp) slice, so the pack
+ * into destination order that would precede a2av_run is fused away.
+ * nblk = 1 is exactly a2av_run.
+ * Errors: as a2av_run; in addition nblk < 1 is INVALID_ARGS (host, with the
+ * P check), and a count that nblk does not divide is INVALID_ARGS on the
+ * device (right after the negative-count check, latched like the others).
+ */
+int a2av_run_blocked(a2av_handle *h, const void *input, void *target, int32_t *signal,
+                     const int32_t *send_counts, int32_t *recv_counts, int32_t P,
+                     int64_t core_num, int32_t dtype, int32_t nblk, void *stream);
+
 /* Free the workspace and the handle (synchronizes the device first).
  * NULL is accepted and ignored. */
 int a2av_destroy(a2av_handle *h);

@@ -51,25 +51,30 @@ class Case:
         self.send = upload(w.counts)
         self.recv = torch.full((P, P), -7, dtype=torch.int32, device=DEV)
 
-    def run_gpu(self, ex: a2av.Exchange, core_num: int | None = None, sync: bool = True) -> int:
+    def run_gpu(self, ex: a2av.Exchange, core_num: int | None = None, sync: bool = True,
+                nblk: int = 1) -> int:
         w = self.w
         ex.run(self.input, self.target, self.signal, self.send, self.recv,
-               w.core_num if core_num is None else core_num, w.dtype)
+               w.core_num if core_num is None else core_num, w.dtype, nblk=nblk)
         if sync:
             torch.cuda.synchronize()
             return ex.query_error()
         return a2av.OK
 
-    def run_oracle(self, core_num: int | None = None, capacity: int = 0):
+    def run_oracle(self, core_num: int | None = None, capacity: int = 0, nblk: int = 1):
         w = self.w
         inp = self.input_np if self.input_np is not None else self.input.cpu().numpy()
         tgt = np.full(w.tgt_bytes, wl.SENTINEL, np.uint8)
         sig = self.signal_np0.copy()
         rc = np.full((w.P, w.P), -7, np.int32)
-        st = oracle.run(inp, tgt, sig, np.ascontiguousarray(w.counts, np.int32), rc, P=w.P, S=w.S,
-                        in_slab=w.in_slab, tgt_slab=w.tgt_slab,
-                        core_num=w.core_num if core_num is None else core_num, dtype=w.dtype,
-                        capacity=capacity)
+        kw = dict(P=w.P, S=w.S, in_slab=w.in_slab, tgt_slab=w.tgt_slab,
+                  core_num=w.core_num if core_num is None else core_num, dtype=w.dtype,
+                  capacity=capacity)
+        C = np.ascontiguousarray(w.counts, np.int32)
+        if nblk == 1:
+            st = oracle.run(inp, tgt, sig, C, rc, **kw)
+        else:
+            st = oracle.run_blocked(inp, tgt, sig, C, rc, nblk=nblk, **kw)
         return st, tgt, sig, rc
 
     def assert_matches(self, st_gpu, expect):
@@ -89,16 +94,16 @@ def exchange_for(w: wl.Workload, **kw) -> a2av.Exchange:
     return a2av.Exchange(w.P, w.in_slab, w.tgt_slab, w.S, device=0, **kw)
 
 
-def check_case(w: wl.Workload, core_num: int | None = None, runs: int = 1, **kw):
+def check_case(w: wl.Workload, core_num: int | None = None, runs: int = 1, nblk: int = 1, **kw):
     """Run the GPU path ``runs`` times and the oracle as often; compare everything."""
     c = Case(w)
     ex = exchange_for(w, **kw)
     try:
         for _ in range(runs):
-            st = c.run_gpu(ex, core_num)
+            st = c.run_gpu(ex, core_num, nblk=nblk)
         exp = None
         for _ in range(runs):
-            exp = c.run_oracle(core_num)
+            exp = c.run_oracle(core_num, nblk=nblk)
             if runs > 1:
                 c.signal_np0 = exp[2].copy()
         c.assert_matches(st, exp)
