@@ -36,7 +36,9 @@ import numpy as np
 
 FP32 = 0
 INT8 = 1
-ELEM_SIZE = {FP32: 4, INT8: 1}
+FP16 = 2
+BF16 = 3
+ELEM_SIZE = {FP32: 4, INT8: 1, FP16: 2, BF16: 2}
 SENTINEL = 0xA5
 
 _GOLDEN = 0x9E3779B97F4A7C15
@@ -95,6 +97,33 @@ def fill_random_(t, seed: int, chunk_words: int = 1 << 24) -> None:
         b = z.view(torch.uint8)
         lo, hi = w0 * 8, min(n, w1 * 8)
         t[lo:hi].copy_(b[: hi - lo])
+
+
+def finite16_from_words(words: np.ndarray, dtype: int) -> np.ndarray:
+    """Map random 16-bit words to finite, moderate 16-bit floats (as uint16 bits).
+
+    Random sign and mantissa; the exponent field is folded into a middle
+    range (bf16: 2^-27 .. 2^27, fp16: 2^-10 .. 2^10), so no NaN, infinity or
+    overflow can arise in the payload or in a sum with a moderate bias.
+    """
+    w = words.astype(np.uint32)
+    sign = w & 0x8000
+    if dtype == BF16:
+        exp = 100 + (w >> 7) % 55                       # biased 100..154
+        return (sign | (exp << 7) | (w & 0x7F)).astype(np.uint16)
+    exp = 5 + (w >> 10) % 21                            # biased 5..25
+    return (sign | (exp << 10) | (w & 0x3FF)).astype(np.uint16)
+
+
+def bias_values(seed: int, P: int, nblk: int, hidden: int, dtype: int) -> np.ndarray:
+    """Bias [P, nblk, hidden]: float32 for BF16 payloads, binary16 bits for FP16."""
+    n = P * nblk * hidden
+    if dtype == BF16:
+        u = random_bytes_np(seed, 0, 4 * n).view(np.uint32)
+        v = ((u >> 9).astype(np.float64) / float(1 << 23) - 0.5) * 64.0   # in [-32, 32)
+        return v.astype(np.float32).reshape(P, nblk, hidden)
+    w = random_bytes_np(seed, 0, 2 * n).view(np.uint16)
+    return finite16_from_words(w, FP16).reshape(P, nblk, hidden)
 
 
 # ---------------------------------------------------------------- count matrices

@@ -40,7 +40,9 @@ ERR_LAUNCH_CAPACITY = 5
 
 FP32 = 0
 INT8 = 1
-ELEM_SIZE = {FP32: 4, INT8: 1}
+FP16 = 2
+BF16 = 3
+ELEM_SIZE = {FP32: 4, INT8: 1, FP16: 2, BF16: 2}
 
 
 def build(force: bool = True) -> str:
@@ -73,6 +75,16 @@ def lib() -> ctypes.CDLL:
         L.a2av_oracle_check.restype = ctypes.c_int
         L.a2av_oracle_run_blocked.argtypes = run_args + [i32]
         L.a2av_oracle_run_blocked.restype = ctypes.c_int
+        L.a2av_oracle_run_bias.argtypes = run_args + [i32, vp, i32]
+        L.a2av_oracle_run_bias.restype = ctypes.c_int
+        L.a2av_oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.a2av_oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.a2av_oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.a2av_oracle_bf16_to_f32.restype = ctypes.c_float
+        L.a2av_oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        L.a2av_oracle_f32_to_f16.restype = ctypes.c_uint16
+        L.a2av_oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.a2av_oracle_f16_to_f32.restype = ctypes.c_float
         L.a2av_oracle_displacements.argtypes = [vp, i32, i32, vp, vp]
         L.a2av_oracle_displacements.restype = None
         L.a2av_oracle_move.argtypes = [vp, vp, vp, i32, i32, i64, i64]
@@ -127,6 +139,39 @@ def run_blocked(input_bytes: np.ndarray, target_bytes: np.ndarray, signal: np.nd
     return int(lib().a2av_oracle_run_blocked(
         _ptr(input_bytes), _ptr(target_bytes), _ptr(signal), _ptr(send_counts),
         _ptr(recv_counts), P, S, in_slab, tgt_slab, core_num, dtype, capacity, nblk))
+
+
+def run_bias(input_bytes: np.ndarray, target_bytes: np.ndarray, signal: np.ndarray,
+             send_counts: np.ndarray, recv_counts: np.ndarray, bias: np.ndarray | None, *,
+             P: int, S: int, in_slab: int, tgt_slab: int, core_num: int, dtype: int, nblk: int,
+             hidden: int, capacity: int = 0) -> int:
+    """The exchange with the bias Add fused in front (16-bit payloads): the
+    blocked exchange of (input + bias broadcast over rows), each sum formed in
+    binary32 and rounded to nearest even.  ``bias`` is float32 [P, nblk, hidden]
+    for BF16 payloads, uint16 (binary16 bits) for FP16."""
+    for a, n in ((input_bytes, P * in_slab), (target_bytes, P * tgt_slab)):
+        assert a.dtype == np.uint8 and a.size == n
+    assert signal.dtype == np.int32 and signal.size == P * S
+    return int(lib().a2av_oracle_run_bias(
+        _ptr(input_bytes), _ptr(target_bytes), _ptr(signal), _ptr(send_counts),
+        _ptr(recv_counts), P, S, in_slab, tgt_slab, core_num, dtype, capacity, nblk,
+        _ptr(bias), hidden))
+
+
+def f32_to_bf16(x: float) -> int:
+    return int(lib().a2av_oracle_f32_to_bf16(x))
+
+
+def bf16_to_f32(h: int) -> float:
+    return float(lib().a2av_oracle_bf16_to_f32(h))
+
+
+def f32_to_f16(x: float) -> int:
+    return int(lib().a2av_oracle_f32_to_f16(x))
+
+
+def f16_to_f32(h: int) -> float:
+    return float(lib().a2av_oracle_f16_to_f32(h))
 
 
 def check(input_ptr, target_ptr, signal_ptr, send_ptr, recv_ptr, *, P, S, in_slab,

@@ -28,6 +28,7 @@
  * Parity status of every function here is recorded at its definition.  There
  * is no floating-point arithmetic: payload moves as raw bytes.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stddef.h>
 #include <string.h>
@@ -42,6 +43,8 @@
 
 #define OR_DTYPE_FP32 0
 #define OR_DTYPE_INT8 1
+#define OR_DTYPE_FP16 2
+#define OR_DTYPE_BF16 3
 
 #define OR_MAX_P 64
 #define OR_INT32_MAX 2147483647LL
@@ -69,7 +72,7 @@ int64_t a2av_oracle_blocks(int64_t P, int64_t L)
 
 static int64_t elem_size(int32_t dtype)
 {
-    return dtype == OR_DTYPE_FP32 ? 4 : 1;
+    return dtype == OR_DTYPE_FP32 ? 4 : dtype == OR_DTYPE_INT8 ? 1 : 2;
 }
 
 /* Half-open byte ranges [a, a+na) and [b, b+nb) share at least one byte. */
@@ -97,8 +100,8 @@ static int ranges_overlap(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb)
  *      rule of "Current limitations")                   -> INVALID_ARGS
  *   8. a slab size that is not a whole number of elements -> INVALID_ARGS
  *   9. a negative count                                 -> INVALID_ARGS
- *  9b. (blocked exchange only) a count that nblk does not divide
- *                                                       -> INVALID_ARGS
+ *  9b. a count that nblk (times the row length, with a bias) does not
+ *      divide (blocked and fused-bias exchanges only)   -> INVALID_ARGS
  *  10. a source row or destination column whose bytes exceed its slab
  *                                                       -> OVER_CAPACITY
  *  11. signal[r][b] (r < P, b < B) not all equal        -> INVALID_ARGS
@@ -109,13 +112,18 @@ static int ranges_overlap(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb)
 static int check_args(const void *input, const void *target, const int32_t *signal,
                       const int32_t *send_counts, const int32_t *recv_counts,
                       int32_t P, int32_t S, int64_t in_slab, int64_t tgt_slab,
-                      int64_t core_num, int32_t dtype, int64_t capacity, int32_t nblk)
+                      int64_t core_num, int32_t dtype, int64_t capacity, int32_t nblk,
+                      const void *bias, int32_t hidden)
 {
+    /* bias != NULL selects the fused-bias exchange: 16-bit payloads and a
+     * sixth operand of P*nblk*hidden bias values. */
+    const int with_bias = bias != NULL;
     if (!input || !target || !signal || !send_counts || !recv_counts)
         return OR_ERR_NULLPTR;
-    if (dtype != OR_DTYPE_FP32 && dtype != OR_DTYPE_INT8)
+    if (with_bias ? (dtype != OR_DTYPE_FP16 && dtype != OR_DTYPE_BF16)
+                  : (dtype != OR_DTYPE_FP32 && dtype != OR_DTYPE_INT8))
         return OR_ERR_UNSUPPORTED_DTYPE;
-    if (P < 1 || P > OR_MAX_P || S < 1 || in_slab < 1 || tgt_slab < 1 || nblk < 1)
+    if (P < 1 || P > OR_MAX_P || S < 1 || in_slab < 1 || tgt_slab < 1 || nblk < 1 || hidden < 1)
         return OR_ERR_INVALID_ARGS;
     if (core_num < 1 || core_num > OR_INT32_MAX)
         return OR_ERR_INVALID_ARGS;
@@ -125,13 +133,16 @@ static int check_args(const void *input, const void *target, const int32_t *sign
     if (B > 1 && capacity > 0 && B > capacity)
         return OR_ERR_LAUNCH_CAPACITY;
 
-    uintptr_t base[5] = {(uintptr_t)input, (uintptr_t)target, (uintptr_t)signal,
-                         (uintptr_t)send_counts, (uintptr_t)recv_counts};
-    uint64_t len[5] = {(uint64_t)P * (uint64_t)in_slab, (uint64_t)P * (uint64_t)tgt_slab,
+    int64_t bias_e = dtype == OR_DTYPE_BF16 ? 4 : 2;
+    uintptr_t base[6] = {(uintptr_t)input, (uintptr_t)target, (uintptr_t)signal,
+                         (uintptr_t)send_counts, (uintptr_t)recv_counts, (uintptr_t)bias};
+    uint64_t len[6] = {(uint64_t)P * (uint64_t)in_slab, (uint64_t)P * (uint64_t)tgt_slab,
                        (uint64_t)P * (uint64_t)S * 4u, (uint64_t)P * (uint64_t)P * 4u,
-                       (uint64_t)P * (uint64_t)P * 4u};
-    for (int i = 0; i < 5; ++i)
-        for (int j = i + 1; j < 5; ++j)
+                       (uint64_t)P * (uint64_t)P * 4u,
+                       with_bias ? (uint64_t)P * (uint64_t)nblk * (uint64_t)hidden * (uint64_t)bias_e
+                                 : 0u};
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j)
             if (ranges_overlap(base[i], len[i], base[j], len[j]))
                 return OR_ERR_INVALID_ARGS;
 
@@ -143,9 +154,10 @@ static int check_args(const void *input, const void *target, const int32_t *sign
         for (int32_t d = 0; d < P; ++d)
             if (send_counts[s * P + d] < 0)
                 return OR_ERR_INVALID_ARGS;
+    int64_t unit = (int64_t)nblk * hidden;
     for (int32_t s = 0; s < P; ++s)
         for (int32_t d = 0; d < P; ++d)
-            if (send_counts[s * P + d] % nblk != 0)
+            if (send_counts[s * P + d] % unit != 0)
                 return OR_ERR_INVALID_ARGS;
 
     for (int32_t s = 0; s < P; ++s) {
@@ -178,7 +190,7 @@ int a2av_oracle_check(const void *input, const void *target, const int32_t *sign
                       int64_t core_num, int32_t dtype, int64_t capacity)
 {
     return check_args(input, target, signal, send_counts, recv_counts, P, S, in_slab,
-                      tgt_slab, core_num, dtype, capacity, 1);
+                      tgt_slab, core_num, dtype, capacity, 1, NULL, 1);
 }
 
 /*
@@ -269,7 +281,7 @@ int a2av_oracle_run(const void *input, void *target, int32_t *signal,
                     int64_t core_num, int32_t dtype, int64_t capacity)
 {
     int st = check_args(input, target, signal, send_counts, recv_counts, P, S, in_slab,
-                        tgt_slab, core_num, dtype, capacity, 1);
+                        tgt_slab, core_num, dtype, capacity, 1, NULL, 1);
     if (st != OR_OK)
         return st;
     int64_t e = elem_size(dtype);
@@ -313,7 +325,7 @@ int a2av_oracle_run_blocked(const void *input, void *target, int32_t *signal,
                             int32_t dtype, int64_t capacity, int32_t nblk)
 {
     int st = check_args(input, target, signal, send_counts, recv_counts, P, S, in_slab,
-                        tgt_slab, core_num, dtype, capacity, nblk);
+                        tgt_slab, core_num, dtype, capacity, nblk, NULL, 1);
     if (st != OR_OK)
         return st;
 
@@ -336,6 +348,154 @@ int a2av_oracle_run_blocked(const void *input, void *target, int32_t *signal,
                        (const uint8_t *)input + (int64_t)s * in_slab + a * (row / nblk) +
                            sdispl[s * P + d] / nblk,
                        (size_t)sub);
+        }
+    }
+    arrive(signal, P, S, B);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------ 16-bit payload */
+
+/* IEEE binary32 bits <-> float without aliasing tricks. */
+static float f32_from_bits(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static uint32_t bits_from_f32(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return u;
+}
+
+/* bfloat16 is the upper half of a binary32: widening appends 16 zero bits. */
+float a2av_oracle_bf16_to_f32(uint16_t h)
+{
+    return f32_from_bits((uint32_t)h << 16);
+}
+
+/* binary32 -> bfloat16, round to nearest, ties to even: add half an ulp of
+ * the kept part (minus one when the kept part is even), then truncate.
+ * Finite inputs only (the payloads here are finite).
+ * Pinned by: torch's CPU float32 -> bfloat16 conversion on every test value. */
+uint16_t a2av_oracle_f32_to_bf16(float f)
+{
+    uint32_t u = bits_from_f32(f);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* binary16 -> binary32, exact (normal, subnormal, zero; finite inputs). */
+float a2av_oracle_f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) & 1u;
+    uint32_t exp = (uint32_t)(h >> 10) & 0x1Fu;
+    uint32_t man = (uint32_t)h & 0x3FFu;
+    float mag;
+    if (exp == 0)
+        mag = (float)man * (1.0f / 16777216.0f); /* man * 2^-24 */
+    else
+        mag = f32_from_bits(((exp + 112u) << 23) | (man << 13)); /* rebias 15 -> 127 */
+    return sign ? -mag : mag;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even, from the definition:
+ * scale into the binary16 grid of the value's binade (the subnormal grid
+ * below 2^-14), round the scaled value to an integer with ties to even, and
+ * assemble the fields.  Finite inputs whose result is finite.
+ * Pinned by: numpy's float32 -> float16 conversion on every test value. */
+uint16_t a2av_oracle_f32_to_f16(float f)
+{
+    uint32_t u = bits_from_f32(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    double a = fabs((double)f);
+    if (a == 0.0)
+        return sign;
+    int e = (int)((u >> 23) & 0xFFu) - 127;            /* binade of |f| */
+    if (e < -14)
+        e = -14;                                       /* subnormal grid */
+    double step = ldexp(1.0, e - 10);                  /* ulp in that binade */
+    double q = a / step;                               /* exact: a power-of-2 scale */
+    double r = floor(q);
+    double frac = q - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) == 1.0))
+        r += 1.0;
+    /* r in [0, 2048]; 2048 means the value rounded up into the next binade. */
+    int64_t m = (int64_t)r;
+    int64_t biased = (int64_t)e + 15;
+    if (m >= 2048) {
+        m >>= 1;
+        biased += 1;
+    }
+    if (m < 1024)                                      /* subnormal result */
+        return (uint16_t)(sign | (uint16_t)m);
+    return (uint16_t)(sign | (uint16_t)(biased << 10) | (uint16_t)(m & 0x3FF));
+}
+
+/*
+ * The exchange with the bias Add fused in front of it: the tail of the CANN
+ * BatchMatMulReduceScatterAllToAll op ("Function and computation flow":
+ * temp3 = temp2 + bias, y = AllToAll(temp3); "Parameters": for FLOAT16 x the
+ * bias is FLOAT16, for BFLOAT16 x it is FLOAT32 and the add is done in FP32
+ * and cast back; "Constraints", yShardType 0: bias (E/ep, 1, H/tp) broadcast
+ * over the C rows).  Layout as in a2av_oracle_run_blocked with nblk = E/ep:
+ * source s's block-row a is expert a; every element belongs to a row of
+ * `hidden` (= H/tp) elements; element h of a row in block-row a of source s
+ * gets bias[(s * nblk + a) * hidden + h].  Each sum is formed in binary32
+ * (the FLOAT16 case widened the same way, a reading) and rounded once, to
+ * nearest even, back to 16 bits.  Payload and bias are finite.
+ * The checks are check_args's with: bias a sixth operand (NULLPTR when
+ * missing, in the pairwise-distinct rule with P*nblk*hidden values), dtype
+ * FP16 or BF16 only, hidden >= 1 with the geometry, and every count a
+ * multiple of hidden * nblk (whole rows of every sub-block; check 9b).
+ * Pinned by: the conversion pins above; a zero bias reduces it to the
+ * blocked exchange; the CANN layout relation against numpy / torch adds.
+ */
+int a2av_oracle_run_bias(const void *input, void *target, int32_t *signal,
+                         const int32_t *send_counts, int32_t *recv_counts, int32_t P, int32_t S,
+                         int64_t in_slab, int64_t tgt_slab, int64_t core_num, int32_t dtype,
+                         int64_t capacity, int32_t nblk, const void *bias, int32_t hidden)
+{
+    if (!bias)
+        return OR_ERR_NULLPTR;
+    int st = check_args(input, target, signal, send_counts, recv_counts, P, S, in_slab,
+                        tgt_slab, core_num, dtype, capacity, nblk, bias, hidden);
+    if (st != OR_OK)
+        return st;
+
+    int64_t B = a2av_oracle_blocks(P, core_num);
+    int64_t sdispl[OR_MAX_P * OR_MAX_P];
+    int64_t rdispl[OR_MAX_P * OR_MAX_P];
+    transpose_counts(send_counts, recv_counts, P);
+    displacements(send_counts, P, 2, sdispl, rdispl);
+    const uint16_t *x = (const uint16_t *)input;
+    uint16_t *y = (uint16_t *)target;
+    for (int32_t s = 0; s < P; ++s) {
+        int64_t row = 0; /* bytes source s sends */
+        for (int32_t d = 0; d < P; ++d)
+            row += (int64_t)send_counts[s * P + d] * 2;
+        for (int32_t d = 0; d < P; ++d) {
+            int64_t sub = (int64_t)send_counts[s * P + d] / nblk; /* elements */
+            for (int32_t a = 0; a < nblk; ++a) {
+                int64_t src = ((int64_t)s * in_slab + a * (row / nblk) + sdispl[s * P + d] / nblk) / 2;
+                int64_t dst = ((int64_t)d * tgt_slab + rdispl[d * P + s]) / 2 + a * sub;
+                for (int64_t k = 0; k < sub; ++k) {
+                    int64_t h = k % hidden;
+                    int64_t bi = ((int64_t)s * nblk + a) * hidden + h;
+                    float sum;
+                    if (dtype == OR_DTYPE_BF16) {
+                        sum = a2av_oracle_bf16_to_f32(x[src + k]) + ((const float *)bias)[bi];
+                        y[dst + k] = a2av_oracle_f32_to_bf16(sum);
+                    } else {
+                        sum = a2av_oracle_f16_to_f32(x[src + k]) +
+                              a2av_oracle_f16_to_f32(((const uint16_t *)bias)[bi]);
+                        y[dst + k] = a2av_oracle_f32_to_f16(sum);
+                    }
+                }
+            }
         }
     }
     arrive(signal, P, S, B);

@@ -499,3 +499,136 @@ def test_blocked_diagnostics():
     C4 = np.full((P, P), 8, np.int32)
     st, *_ = _run_blocked(C4, P, wl.INT8, 16, 16, 2)
     assert st == oracle.ERR_OVER_CAPACITY
+
+
+# ------------------------------------------------------------------- fused bias Add
+
+def test_bf16_conversions_match_torch():
+    import torch
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 4000),
+        # exact ties: kept part even and odd
+        (np.arange(1, 200, dtype=np.uint32) << 16 | 0x8000).view(np.float32),
+        ((np.arange(1, 200, dtype=np.uint32) << 16) | 0x18000).view(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, 1e-40, -1e-40], np.float32),
+    ]).astype(np.float32)
+    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.f32_to_bf16(float(v)) for v in vals], np.uint16)
+    np.testing.assert_array_equal(got, want)
+    back = torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().numpy()
+    got_back = np.array([oracle.bf16_to_f32(int(h)) for h in want], np.float32)
+    np.testing.assert_array_equal(got_back.view(np.uint32), back.view(np.uint32))
+
+
+def test_f16_conversions_match_numpy():
+    rng = np.random.default_rng(6)
+    vals = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32) * 2.0 ** rng.integers(-26, 15, 4000),
+        # exact ties in the normal and subnormal ranges
+        (np.arange(1, 300, dtype=np.float64) + 0.5).astype(np.float32) * np.float32(2.0 ** -24),
+        (np.arange(1024, 1400, dtype=np.float64) + 0.5).astype(np.float32),
+        np.array([0.0, -0.0, 65504.0, 6.1e-5, 5.96e-8, 2.98e-8, 65519.0], np.float32),
+    ]).astype(np.float32)
+    want = vals.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f32_to_f16(float(v)) for v in vals], np.uint16)
+    np.testing.assert_array_equal(got, want)
+    halves = np.concatenate([np.arange(0, 0x7C00, 7, dtype=np.uint16),
+                             np.arange(0x8000, 0xFC00, 13, dtype=np.uint16)])
+    back = np.array([oracle.f16_to_f32(int(h)) for h in halves], np.float32)
+    np.testing.assert_array_equal(back.view(np.uint32),
+                                  halves.view(np.float16).astype(np.float32).view(np.uint32))
+
+
+def _bias_case(P, nblk, hidden, rows, dtype, seed=3, bias=None, pad=32):
+    rng = np.random.default_rng(seed)
+    C = (rng.integers(0, rows + 1, size=(P, P)) * nblk * hidden).astype(np.int32)
+    e = 2
+    in_slab = int(C.sum(axis=1).max(initial=0)) * e + pad
+    tgt_slab = int(C.sum(axis=0).max(initial=0)) * e + pad
+    words = wl.random_bytes_np(seed + 100, 0, P * in_slab).view(np.uint16)
+    inp = wl.finite16_from_words(words, dtype).view(np.uint8).copy()
+    if bias is None:
+        bias = wl.bias_values(seed + 200, P, nblk, hidden, dtype)
+    return C, in_slab, tgt_slab, inp, np.ascontiguousarray(bias)
+
+
+def _run_bias(C, P, in_slab, tgt_slab, inp, bias, dtype, nblk, hidden, core_num=1):
+    S = max(1, oracle.blocks(P, core_num))
+    tgt = np.full(P * tgt_slab, wl.SENTINEL, np.uint8)
+    sig = np.zeros((P, S), np.int32)
+    rc = np.full((P, P), -7, np.int32)
+    st = oracle.run_bias(inp, tgt, sig, np.ascontiguousarray(C, np.int32), rc, bias, P=P, S=S,
+                         in_slab=in_slab, tgt_slab=tgt_slab, core_num=core_num, dtype=dtype,
+                         nblk=nblk, hidden=hidden)
+    return st, tgt, sig, rc
+
+
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP16])
+def test_bias_of_negative_zero_is_the_blocked_exchange(dtype):
+    # x + (-0) == x for every finite x, so the result is the blocked exchange
+    # of the same bytes (an int8 exchange with counts doubled).
+    P, nblk, hidden = 4, 3, 8
+    negz = np.full((P, nblk, hidden), -0.0, np.float32) if dtype == oracle.BF16 else \
+        np.full((P, nblk, hidden), 0x8000, np.uint16)
+    C, in_slab, tgt_slab, inp, bias = _bias_case(P, nblk, hidden, 5, dtype, bias=negz)
+    st, tgt, sig, rc = _run_bias(C, P, in_slab, tgt_slab, inp, bias, dtype, nblk, hidden)
+    assert st == oracle.OK
+    tgt2 = np.full(P * tgt_slab, wl.SENTINEL, np.uint8)
+    sig2 = np.zeros((P, 1), np.int32)
+    rc2 = np.full((P, P), -7, np.int32)
+    st2 = oracle.run_blocked(inp, tgt2, sig2, (C * 2).astype(np.int32), rc2, P=P, S=1,
+                             in_slab=in_slab, tgt_slab=tgt_slab, core_num=1, dtype=oracle.INT8,
+                             nblk=nblk)
+    assert st2 == oracle.OK
+    np.testing.assert_array_equal(tgt, tgt2)
+    np.testing.assert_array_equal(rc, C.T)
+
+
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP16])
+def test_bias_cann_flow_against_torch(dtype):
+    # Equal counts: temp2 per source is (A, P*Cr, Hd); temp3 = temp2 + bias[s, a, None, :]
+    # in fp32, rounded to the payload type by torch; y = permute to (P, P, A, Cr*Hd).
+    import torch
+    P, A, Cr, Hd = 4, 2, 3, 16
+    C = np.full((P, P), A * Cr * Hd, np.int32)
+    slab = P * A * Cr * Hd * 2
+    words = wl.random_bytes_np(77, 0, P * slab).view(np.uint16)
+    x16 = wl.finite16_from_words(words, dtype)
+    bias = wl.bias_values(78, P, A, Hd, dtype)
+    st, tgt, _, _ = _run_bias(C, P, slab, slab, x16.view(np.uint8).copy(), bias, dtype, A, Hd)
+    assert st == oracle.OK
+    tdt = torch.bfloat16 if dtype == oracle.BF16 else torch.float16
+    x = torch.from_numpy(x16.view(np.int16)).view(tdt).float().view(P, A, P * Cr, Hd)
+    if dtype == oracle.BF16:
+        b = torch.from_numpy(bias)
+    else:
+        b = torch.from_numpy(bias.view(np.int16)).view(torch.float16).float()
+    temp3 = (x + b.view(P, A, 1, Hd)).to(tdt)                    # (P, A, P*Cr, Hd)
+    y = temp3.view(P, A, P, Cr * Hd).permute(2, 0, 1, 3).contiguous()
+    want = y.view(torch.int16).numpy().reshape(-1).view(np.uint8)
+    np.testing.assert_array_equal(tgt, want)
+
+
+def test_bias_diagnostics():
+    P, nblk, hidden = 2, 2, 8
+    C, in_slab, tgt_slab, inp, bias = _bias_case(P, nblk, hidden, 3, oracle.BF16, seed=9)
+    st, *_ = _run_bias(C, P, in_slab, tgt_slab, inp, None, oracle.BF16, nblk, hidden)
+    assert st == oracle.ERR_NULLPTR
+    st, *_ = _run_bias(C, P, in_slab, tgt_slab, inp, bias, oracle.FP32, nblk, hidden)
+    assert st == oracle.ERR_UNSUPPORTED_DTYPE
+    st, *_ = _run_bias(C, P, in_slab, tgt_slab, inp, bias, oracle.BF16, nblk, 0)
+    assert st == oracle.ERR_INVALID_ARGS
+    C2 = C.copy()
+    C2[0, 1] += nblk                                   # not whole rows of every sub-block
+    st, tgt, sig, rc = _run_bias(C2, P, in_slab + 64, tgt_slab + 64,
+                                 np.zeros(P * (in_slab + 64), np.uint8), bias, oracle.BF16,
+                                 nblk, hidden)
+    assert st == oracle.ERR_INVALID_ARGS
+    assert (tgt == wl.SENTINEL).all() and (sig == 0).all() and (rc == -7).all()
+    # The bias may not overlap another operand.
+    st = oracle.run_bias(inp, np.zeros(P * tgt_slab, np.uint8), np.zeros((P, 1), np.int32),
+                         C, np.zeros((P, P), np.int32), inp, P=P, S=1, in_slab=in_slab,
+                         tgt_slab=tgt_slab, core_num=1, dtype=oracle.BF16, nblk=nblk,
+                         hidden=hidden)
+    assert st == oracle.ERR_INVALID_ARGS
