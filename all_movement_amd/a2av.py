@@ -29,11 +29,13 @@ ERR_TIMEOUT = 7
 
 FP32 = 0
 INT8 = 1
-ELEM_SIZE = {FP32: 4, INT8: 1}
+FP16 = 2
+BF16 = 3
+ELEM_SIZE = {FP32: 4, INT8: 1, FP16: 2, BF16: 2}
 FLAG_PROFILE = 1
 
-EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_destroy", "a2av_blocks", "a2av_check_args",
-           "a2av_query_error", "a2av_launch_info_get", "a2av_profile_read",
+EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_run_bias", "a2av_destroy",
+           "a2av_blocks", "a2av_check_args", "a2av_query_error", "a2av_launch_info_get", "a2av_profile_read",
            "a2av_status_string", "a2av_last_hip_error"]
 
 
@@ -73,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.a2av_run.restype = ctypes.c_int
     L.a2av_run_blocked.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
     L.a2av_run_blocked.restype = ctypes.c_int
+    L.a2av_run_bias.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp]
+    L.a2av_run_bias.restype = ctypes.c_int
     L.a2av_destroy.argtypes = [vp]
     L.a2av_destroy.restype = ctypes.c_int
     L.a2av_blocks.argtypes = [i64, i64]
@@ -113,6 +117,12 @@ def a2av_run_blocked(h, input, target, signal, send_counts, recv_counts, P, core
                      nblk, stream) -> int:
     return lib().a2av_run_blocked(h, input, target, signal, send_counts, recv_counts, P,
                                   core_num, dtype, nblk, stream)
+
+
+def a2av_run_bias(h, input, target, signal, send_counts, recv_counts, bias, P, core_num, dtype,
+                  nblk, hidden, stream) -> int:
+    return lib().a2av_run_bias(h, input, target, signal, send_counts, recv_counts, bias, P,
+                               core_num, dtype, nblk, hidden, stream)
 
 
 def a2av_destroy(h) -> int:
@@ -224,8 +234,11 @@ class Exchange:
         return t.data_ptr()
 
     def run(self, input, target, signal, send_counts, recv_counts, core_num: int, dtype: int,
-            stream=None, nblk: int = 1) -> None:
-        """One exchange; ``nblk`` > 1 runs the blocked exchange (a2av_run_blocked)."""
+            stream=None, nblk: int = 1, bias=None, hidden: int = 0) -> None:
+        """One exchange; ``nblk`` > 1 runs the blocked exchange (a2av_run_blocked);
+        a ``bias`` tensor (float32 for BF16 payloads, float16 for FP16, [P, nblk,
+        hidden] elements) runs the exchange with the bias Add fused in
+        (a2av_run_bias)."""
         import torch
         c = self.cfg
         P = c.P
@@ -236,7 +249,15 @@ class Exchange:
         rcp = self._check(recv_counts, P * P * 4, "recv_counts", torch.int32)
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
-        if nblk == 1:
+        if bias is not None:
+            be = {BF16: (torch.float32, 4), FP16: (torch.float16, 2)}.get(dtype)
+            if be is None:  # the library reports the unsupported dtype
+                bp = self._check(bias, bias.numel() * bias.element_size(), "bias")
+            else:
+                bp = self._check(bias, P * nblk * hidden * be[1], "bias", be[0])
+            st = a2av_run_bias(self.h, ip, tp, sp, scp, rcp, bp, P, core_num, dtype, nblk, hidden,
+                               stream.cuda_stream)
+        elif nblk == 1:
             st = a2av_run(self.h, ip, tp, sp, scp, rcp, P, core_num, dtype, stream.cuda_stream)
         else:
             st = a2av_run_blocked(self.h, ip, tp, sp, scp, rcp, P, core_num, dtype, nblk,

@@ -39,6 +39,7 @@ struct CountParams {
   int32_t B;
   int32_t elem;
   int32_t nblk;       // sub-blocks per segment (1 = plain exchange)
+  int64_t unit;       // every count must be a multiple of this (nblk, or nblk * hidden)
 };
 
 struct CopyParams {
@@ -54,6 +55,9 @@ struct CopyParams {
   int32_t B;
   int32_t G;          // workgroups per admitted block
   int32_t nblk;       // sub-blocks per segment (1 = plain exchange)
+  int32_t mode;       // 0: move bytes; 1: BF16 + FP32 bias; 2: FP16 + FP16 bias
+  int32_t hidden;     // elements per row (bias modes)
+  const void* bias;   // [P, nblk, hidden] (bias modes)
   int32_t last;       // 1 on the run's final launch: raise the block flags
   int32_t wait;       // 1 when the final launch is cooperative (B > 1): wait for all blocks
   int32_t spin_limit;

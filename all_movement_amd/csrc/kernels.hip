@@ -76,8 +76,8 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   if (tid == 0) flags = 0;
   __syncthreads();
 
-  // Load the counts; note negatives (bit 0), counts nblk does not divide
-  // (bit 3) and a signal that is not uniform over the admitted entries (bit 2).
+  // Load the counts; note negatives (bit 0), counts that are not whole
+  // sub-blocks (bit 3: nblk, or nblk rows of the bias path, does not divide) and a signal that is not uniform over the admitted entries (bit 2).
   // The loops are unrolled so each thread issues its loads back to back.
   int bad = 0;
 #pragma unroll 4
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     const int32_t c = p.send_counts[i];
     C[i] = c;
     bad |= c < 0 ? 1 : 0;
-    bad |= c % p.nblk != 0 ? 8 : 0;
+    bad |= int64_t(c) % p.unit != 0 ? 8 : 0;
   }
   const int32_t base = p.signal[0];
   for (int r = wave; r < P; r += kWaves) {
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   const int f = flags;
   if (f != 0) {
     if (tid == 0) {
-      // Order: negative count, count not divisible by nblk, over-capacity,
+      // Order: negative count, count not whole sub-blocks, over-capacity,
       // unequal signal.
       const int code = (f & 1) ? A2AV_ERR_INVALID_ARGS
                      : (f & 8) ? A2AV_ERR_INVALID_ARGS
@@ -322,6 +322,156 @@ __device__ void wg_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int t
   }
 }
 
+// ------------------------------------------------ K2, fused bias Add path
+//
+// BF16 payload with an FP32 bias (MODE 1) or FP16 with an FP16 bias (MODE 2),
+// as in the CANN BatchMatMulReduceScatterAllToAll op ("Parameters": the BF16
+// case adds in FP32).  Each sum is formed in binary32 and rounded once to
+// nearest even by the conversion instruction (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32 under the default round-to-nearest-even mode).  For FP16
+// the compiler may form the sum with a packed half add instead: binary32
+// carries 24 >= 2 * 11 + 2 significand bits, so rounding the binary32 sum to
+// binary16 gives the correctly rounded half sum and both forms agree bit for
+// bit.
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBiasUnroll = 4;  // 16-byte payload words in flight per lane
+
+// Reinterpret through a scalar argument: applied directly to an element of an
+// ext_vector_type value (b.y), this compiler's __builtin_bit_cast reads
+// element 0 whatever the index (seen in the gfx950 code it emits).
+__device__ inline float f32_bits(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// A value every lane of the wave holds, moved to scalar registers (the
+// compiler cannot see that values read from LDS at a uniform index are
+// uniform, and would otherwise loop over lanes for every buffer access).
+__device__ inline int64_t wave_uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+template <typename T>
+__device__ inline T* wave_uniform(T* p) {
+  return reinterpret_cast<T*>(wave_uniform(int64_t(reinterpret_cast<uintptr_t>(p))));
+}
+
+__device__ inline uint32_t add_bf16x2(uint32_t x, float b0, float b1) {
+  // bf16 -> f32 is exact: the bits move to the high half.
+  f32x2 v;
+  v.x = __builtin_bit_cast(float, x << 16) + b0;
+  v.y = __builtin_bit_cast(float, x & 0xFFFF0000u) + b1;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ inline uint32_t add_f16x2(uint32_t x, uint32_t b) {
+  const f32x2 v = __builtin_convertvector(__builtin_bit_cast(f16x2, x), f32x2) +
+                  __builtin_convertvector(__builtin_bit_cast(f16x2, b), f32x2);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// One 16-byte payload word (8 elements of one row) plus the 8 bias values of
+// its columns: two 16-byte bias words for FP32, one for FP16.
+template <int MODE>
+__device__ inline u32x4 add_bias_word(u32x4 x, u32x4 b0, u32x4 b1) {
+  u32x4 o;
+  if constexpr (MODE == 1) {
+    o.x = add_bf16x2(x.x, f32_bits(b0.x), f32_bits(b0.y));
+    o.y = add_bf16x2(x.y, f32_bits(b0.z), f32_bits(b0.w));
+    o.z = add_bf16x2(x.z, f32_bits(b1.x), f32_bits(b1.y));
+    o.w = add_bf16x2(x.w, f32_bits(b1.z), f32_bits(b1.w));
+  } else {
+    o.x = add_f16x2(x.x, b0.x);
+    o.y = add_f16x2(x.y, b0.y);
+    o.z = add_f16x2(x.z, b0.z);
+    o.w = add_f16x2(x.w, b0.w);
+  }
+  return o;
+}
+
+// A piece of n bytes (whole 16-byte words, source and destination 16-byte
+// aligned: the host checks and the device count check guarantee it) inside
+// one sub-block.  Its first element is element e0 of the sub-block, whose
+// rows are `hidden` elements long (hidden a multiple of 8, so a word never
+// straddles two rows); brow is the sub-block's bias row.
+//
+// Rows of Hw = hidden / 8 words.  When Hw <= NT the workgroup steps through
+// the piece NTe = (NT / Hw) * Hw words at a time (the last NT - NTe threads
+// idle), so every thread meets the same column on every step and loads its 8
+// bias values once per piece.  Longer rows step NT words at a time and each
+// word loads its own bias values; the column then advances by 8 * NT
+// (mod hidden) per step.
+template <int MODE>
+__device__ void wg_bias_piece(const uint8_t* src, uint8_t* dst, int64_t n, const uint8_t* brow,
+                              int64_t e0, int32_t hidden, int tid) {
+  constexpr int NT = kCopyThreads;
+  constexpr int BE = MODE == 1 ? 4 : 2;  // bias bytes per element
+  src = wave_uniform(src);
+  dst = wave_uniform(dst);
+  brow = wave_uniform(brow);
+  n = wave_uniform(n);
+  e0 = wave_uniform(e0);
+  const int64_t K = n >> 4;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, n);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst, n);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(brow, int64_t(hidden) * BE);
+  const uint32_t H = uint32_t(hidden);
+  const uint32_t Hw = H / 8u;
+  uint32_t h = uint32_t((e0 + 8 * int64_t(tid)) % int64_t(H));
+
+  if (Hw <= uint32_t(NT)) {
+    const int NTe = int((uint32_t(NT) / Hw) * Hw);
+    if (tid >= NTe) return;
+    const u32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, int(h * BE), 0, 0);
+    u32x4 b1 = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (MODE == 1) b1 = __builtin_amdgcn_raw_buffer_load_b128(rb, int(h * BE + 16), 0, 0);
+    for (int64_t k0 = 0; k0 < K; k0 += int64_t(NTe) * kBiasUnroll) {
+      u32x4 v[kBiasUnroll];
+#pragma unroll
+      for (int j = 0; j < kBiasUnroll; ++j) {
+        const int64_t k = k0 + int64_t(j) * NTe + tid;
+        v[j] = u32x4{0u, 0u, 0u, 0u};
+        if (k < K) v[j] = load16(rs, k);
+      }
+#pragma unroll
+      for (int j = 0; j < kBiasUnroll; ++j) {
+        const int64_t k = k0 + int64_t(j) * NTe + tid;
+        if (k < K) store16(rd, k, add_bias_word<MODE>(v[j], b0, b1));
+      }
+    }
+    return;
+  }
+
+  const uint32_t inc = uint32_t((8u * NT) % H);
+  for (int64_t k0 = 0; k0 < K; k0 += int64_t(NT) * kBiasUnroll) {
+    u32x4 v[kBiasUnroll];
+    u32x4 b0[kBiasUnroll];
+    u32x4 b1[kBiasUnroll];
+#pragma unroll
+    for (int j = 0; j < kBiasUnroll; ++j) {
+      const int64_t k = k0 + j * NT + tid;
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      b0[j] = u32x4{0u, 0u, 0u, 0u};
+      b1[j] = u32x4{0u, 0u, 0u, 0u};
+      if (k < K) {
+        v[j] = load16(rs, k);
+        b0[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, int(h * BE), 0, 0);
+        if constexpr (MODE == 1) b1[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, int(h * BE + 16), 0, 0);
+      }
+      h += inc;
+      if (h >= H) h -= H;
+    }
+#pragma unroll
+    for (int j = 0; j < kBiasUnroll; ++j) {
+      const int64_t k = k0 + j * NT + tid;
+      if (k < K) store16(rd, k, add_bias_word<MODE>(v[j], b0[j], b1[j]));
+    }
+  }
+}
+
 // Segment tables of one run, staged in LDS by every workgroup.
 struct SegTables {
   int64_t prefix[kMaxP * kMaxP + 1];
@@ -365,6 +515,7 @@ __device__ inline int64_t readlane64(int64_t v, int lane) {
 // The target side of a segment is contiguous.  In the blocked exchange the
 // source side is nblk sub-blocks, sub-block a at tab.src[i] + a * sstride[s],
 // so a piece is also cut where a sub-block ends.
+template <int MODE>
 __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int64_t x, int64_t b,
                                   int i, int tid, int lane, int wave, u32x4* slot) {
   while (x < b) {
@@ -372,7 +523,25 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
     const int64_t seg_hi = tab.prefix[i + 1];
     if (seg_hi > x) {
       const int64_t pe = b < seg_hi ? b : seg_hi;
-      if (p.nblk == 1) {
+      if constexpr (MODE != 0) {
+        // Fused bias Add: pieces end at sub-block ends; sub-block a of source
+        // s takes bias row (s, a).
+        const int64_t sub = (seg_hi - seg_lo) / p.nblk;
+        const int s = i / p.P;
+        const int64_t stride = tab.sstride[s];
+        constexpr int be = MODE == 1 ? 4 : 2;
+        for (int64_t off = x - seg_lo; off < pe - seg_lo;) {
+          const int64_t a = off / sub;
+          const int64_t w = off - a * sub;
+          const int64_t end = (a + 1) * sub < pe - seg_lo ? (a + 1) * sub : pe - seg_lo;
+          const uint8_t* brow = static_cast<const uint8_t*>(p.bias) +
+                                (int64_t(s) * p.nblk + a) * p.hidden * be;
+          const uint8_t* src = p.input + tab.src[i] + a * stride + w;
+          uint8_t* dst = p.target + tab.dst[i] + off;
+          wg_bias_piece<MODE>(src, dst, end - off, brow, w >> 1, p.hidden, tid);
+          off = end;
+        }
+      } else if (p.nblk == 1) {
         const int64_t off = x - seg_lo;
         wg_copy_piece(p.input + tab.src[i] + off, p.target + tab.dst[i] + off, pe - x, tid,
                       lane, wave, slot);
@@ -401,7 +570,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
 // fan out to destination slabs 1 GiB apart ran at ~4.1 TB/s, the same bytes as
 // interleaved tiles at ~5.6 TB/s).  Every wave derives the same tile bounds
 // and pieces from the LDS tables, so tiles need no workgroup barrier.
-template <int NT>
+template <int NT, int MODE>
 __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   constexpr int NW = NT / kWave;
   __shared__ SegTables tab;
@@ -448,7 +617,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
       li = la < lb ? seg_of(tab.prefix, nseg, la) : 0;
     }
     for (int j = 0; j < kWave && t0 + int64_t(j) * W < ntiles; ++j) {
-      copy_range(p, tab, readlane64(la, j), readlane64(lb, j), __builtin_amdgcn_readlane(li, j),
+      copy_range<MODE>(p, tab, readlane64(la, j), readlane64(lb, j), __builtin_amdgcn_readlane(li, j),
                  tid, lane, wave, slots[wave]);
     }
   }
@@ -501,19 +670,40 @@ hipError_t launch_count(const CountParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_copy(const CopyParams& p, int workgroups, bool cooperative, hipStream_t stream) {
-  if (cooperative) {
-    void* args[] = {const_cast<CopyParams*>(&p)};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&copy_kernel<kCopyThreads>),
-                                      dim3(workgroups), dim3(kCopyThreads), args, 0, stream);
+namespace {
+
+// One instantiation per body, so the plain kernel carries no bias code.
+const void* copy_kernel_for(int mode) {
+  switch (mode) {
+    case 1: return reinterpret_cast<const void*>(&copy_kernel<kCopyThreads, 1>);
+    case 2: return reinterpret_cast<const void*>(&copy_kernel<kCopyThreads, 2>);
+    default: return reinterpret_cast<const void*>(&copy_kernel<kCopyThreads, 0>);
   }
-  hipLaunchKernelGGL(copy_kernel<kCopyThreads>, dim3(workgroups), dim3(kCopyThreads), 0, stream, p);
-  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_copy(const CopyParams& p, int workgroups, bool cooperative, hipStream_t stream) {
+  void* args[] = {const_cast<CopyParams*>(&p)};
+  const void* f = copy_kernel_for(p.mode);
+  if (cooperative)
+    return hipLaunchCooperativeKernel(f, dim3(workgroups), dim3(kCopyThreads), args, 0, stream);
+  return hipLaunchKernel(f, dim3(workgroups), dim3(kCopyThreads), args, 0, stream);
 }
 
 hipError_t copy_occupancy(int* wgs_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      wgs_per_cu, reinterpret_cast<const void*>(&copy_kernel<kCopyThreads>), kCopyThreads, 0);
+  // The largest of the three instantiations decides (they share the LDS
+  // footprint; register counts differ).
+  int best = 1 << 30;
+  for (int mode = 0; mode < 3; ++mode) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, copy_kernel_for(mode),
+                                                                      kCopyThreads, 0);
+    if (e != hipSuccess) return e;
+    if (n < best) best = n;
+  }
+  *wgs_per_cu = best;
+  return hipSuccess;
 }
 
 }  // namespace a2av

@@ -11,7 +11,9 @@ int64_t fold_blocks(int64_t P, int64_t L) {
   return L < P ? L : (L / P) * P;
 }
 
-int64_t elem_bytes(int32_t dtype) { return dtype == A2AV_FP32 ? 4 : 1; }
+int64_t elem_bytes(int32_t dtype) {
+  return dtype == A2AV_FP32 ? 4 : dtype == A2AV_INT8 ? 1 : 2;
+}
 
 int check_config(const a2av_config* cfg) {
   if (!cfg) return A2AV_ERR_NULLPTR;
@@ -68,6 +70,44 @@ int check_run_args(const a2av_config* cfg, int64_t capacity, const void* input,
 
   const int64_t e = elem_bytes(dtype);
   if (cfg->in_slab_bytes % e != 0 || cfg->tgt_slab_bytes % e != 0) return A2AV_ERR_INVALID_ARGS;
+  return A2AV_OK;
+}
+
+int check_bias_args(const a2av_config* cfg, int64_t capacity, int64_t chunk_limit,
+                    const void* input, const void* target, const int32_t* signal,
+                    const int32_t* send_counts, const int32_t* recv_counts, const void* bias,
+                    int32_t P, int64_t core_num, int32_t dtype, int32_t nblk, int32_t hidden) {
+  if (!cfg || !input || !target || !signal || !send_counts || !recv_counts || !bias)
+    return A2AV_ERR_NULLPTR;
+  if (dtype != A2AV_FP16 && dtype != A2AV_BF16) return A2AV_ERR_UNSUPPORTED_DTYPE;
+  if (check_config(cfg) != A2AV_OK) return A2AV_ERR_INVALID_ARGS;
+  if (P != cfg->P || nblk < 1 || hidden < 1) return A2AV_ERR_INVALID_ARGS;
+  if (core_num < 1 || core_num > kInt32Max) return A2AV_ERR_INVALID_ARGS;
+  const int64_t B = fold_blocks(P, core_num);
+  if (int64_t(cfg->S) < B) return A2AV_ERR_INVALID_ARGS;
+  if (B > 1 && capacity > 0 && B > capacity) return A2AV_ERR_LAUNCH_CAPACITY;
+
+  const uint64_t p = uint64_t(P);
+  const uint64_t bias_e = dtype == A2AV_BF16 ? 4u : 2u;
+  const Range r[6] = {
+      {uintptr_t(input), p * uint64_t(cfg->in_slab_bytes)},
+      {uintptr_t(target), p * uint64_t(cfg->tgt_slab_bytes)},
+      {uintptr_t(signal), p * uint64_t(cfg->S) * 4u},
+      {uintptr_t(send_counts), p * p * 4u},
+      {uintptr_t(recv_counts), p * p * 4u},
+      {uintptr_t(bias), p * uint64_t(nblk) * uint64_t(hidden) * bias_e},
+  };
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(r[i], r[j])) return A2AV_ERR_INVALID_ARGS;
+  if (cfg->in_slab_bytes % 2 != 0 || cfg->tgt_slab_bytes % 2 != 0) return A2AV_ERR_INVALID_ARGS;
+  // Limits of the GPU path: 16-byte rows and 16-byte aligned operands, so
+  // every piece is whole 16-byte words of one row.
+  if (hidden % 8 != 0 || hidden > kMaxHidden) return A2AV_ERR_INVALID_ARGS;
+  if (((uintptr_t(input) | uintptr_t(target) | uintptr_t(bias)) & 15u) != 0)
+    return A2AV_ERR_INVALID_ARGS;
+  if (cfg->in_slab_bytes % 16 != 0 || cfg->tgt_slab_bytes % 16 != 0 || chunk_limit % 16 != 0)
+    return A2AV_ERR_INVALID_ARGS;
   return A2AV_OK;
 }
 

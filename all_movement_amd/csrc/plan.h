@@ -12,6 +12,9 @@ namespace a2av {
 constexpr int32_t kMaxP = 64;
 constexpr int64_t kDefaultChunkLimit = int64_t(1) << 30;
 constexpr int64_t kInt32Max = 2147483647LL;
+// Longest bias row of a2av_run_bias: the row's bytes must stay a 32-bit
+// buffer offset.
+constexpr int32_t kMaxHidden = int32_t(1) << 28;
 
 // CalAllToAllVBlocks(P, L) ("Launch width" section of the PyPTO
 // LowerL2TensorCollectives page): L below P stays L, otherwise the largest
@@ -29,6 +32,13 @@ int check_run_args(const a2av_config* cfg, int64_t capacity, const void* input,
                    const void* target, const int32_t* signal, const int32_t* send_counts,
                    const int32_t* recv_counts, int32_t P, int64_t core_num, int32_t dtype,
                    int32_t nblk = 1);
+
+// The host-side checks of a2av_run_bias (fused bias Add, 16-bit payloads),
+// in the documented order; chunk_limit is the handle's bytes per launch.
+int check_bias_args(const a2av_config* cfg, int64_t capacity, int64_t chunk_limit,
+                    const void* input, const void* target, const int32_t* signal,
+                    const int32_t* send_counts, const int32_t* recv_counts, const void* bias,
+                    int32_t P, int64_t core_num, int32_t dtype, int32_t nblk, int32_t hidden);
 
 // Upper bound of the payload of any valid run: every row fits its input slab
 // and every column its target slab, so T <= P * min(in_slab, tgt_slab).

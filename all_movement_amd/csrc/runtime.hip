@@ -197,15 +197,19 @@ int a2av_launch_info_get(a2av_handle* h, int64_t core_num, a2av_launch_info* out
   return A2AV_OK;
 }
 
-int a2av_run_blocked(a2av_handle* h, const void* input, void* target, int32_t* signal,
-                     const int32_t* send_counts, int32_t* recv_counts, int32_t P,
-                     int64_t core_num, int32_t dtype, int32_t nblk, void* stream) {
-  if (!h) return A2AV_ERR_NULLPTR;
-  int st = a2av::check_run_args(&h->cfg, h->capacity, input, target, signal, send_counts,
-                                recv_counts, P, core_num, dtype, nblk);
-  if (st != A2AV_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Enqueue one run whose arguments passed the host checks: K1, then the K2
+// launches.  mode selects the body of K2 (0: move bytes; 1 and 2: the fused
+// bias Add for BF16 and FP16 payloads).
+int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal,
+                const int32_t* send_counts, int32_t* recv_counts, int32_t P, int64_t core_num,
+                int32_t dtype, int32_t nblk, const void* bias, int32_t hidden, int32_t mode,
+                void* stream) {
   a2av_launch_info li;
-  st = a2av_launch_info_get(h, core_num, &li);
+  int st = a2av_launch_info_get(h, core_num, &li);
   if (st != A2AV_OK) return st;
 
   DeviceGuard guard(h->device);
@@ -225,6 +229,7 @@ int a2av_run_blocked(a2av_handle* h, const void* input, void* target, int32_t* s
   cp.B = int32_t(li.blocks);
   cp.elem = int32_t(a2av::elem_bytes(dtype));
   cp.nblk = nblk;
+  cp.unit = int64_t(nblk) * (mode != 0 ? hidden : 1);
 
   hipEvent_t* ev = nullptr;
   if (h->profile)
@@ -244,6 +249,9 @@ int a2av_run_blocked(a2av_handle* h, const void* input, void* target, int32_t* s
   kp.B = int32_t(li.blocks);
   kp.G = li.wg_per_block;
   kp.nblk = nblk;
+  kp.mode = mode;
+  kp.hidden = hidden;
+  kp.bias = bias;
   kp.spin_limit = h->spin_limit;
   // Chunks are issued from the highest to chunk 0.  Chunks past the run's
   // payload cost only a plain launch that exits at once, and the final launch
@@ -266,6 +274,33 @@ int a2av_run_blocked(a2av_handle* h, const void* input, void* target, int32_t* s
     ++h->profiled_runs;
   }
   return A2AV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int a2av_run_blocked(a2av_handle* h, const void* input, void* target, int32_t* signal,
+                     const int32_t* send_counts, int32_t* recv_counts, int32_t P,
+                     int64_t core_num, int32_t dtype, int32_t nblk, void* stream) {
+  if (!h) return A2AV_ERR_NULLPTR;
+  const int st = a2av::check_run_args(&h->cfg, h->capacity, input, target, signal, send_counts,
+                                      recv_counts, P, core_num, dtype, nblk);
+  if (st != A2AV_OK) return st;
+  return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, nblk,
+                     nullptr, 0, 0, stream);
+}
+
+int a2av_run_bias(a2av_handle* h, const void* input, void* target, int32_t* signal,
+                  const int32_t* send_counts, int32_t* recv_counts, const void* bias, int32_t P,
+                  int64_t core_num, int32_t dtype, int32_t nblk, int32_t hidden, void* stream) {
+  if (!h) return A2AV_ERR_NULLPTR;
+  const int st = a2av::check_bias_args(&h->cfg, h->capacity, h->chunk_limit, input, target,
+                                       signal, send_counts, recv_counts, bias, P, core_num, dtype,
+                                       nblk, hidden);
+  if (st != A2AV_OK) return st;
+  return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, nblk,
+                     bias, hidden, dtype == A2AV_BF16 ? 1 : 2, stream);
 }
 
 int a2av_run(a2av_handle* h, const void* input, void* target, int32_t* signal,

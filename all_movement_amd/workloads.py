@@ -39,6 +39,7 @@ INT8 = 1
 FP16 = 2
 BF16 = 3
 ELEM_SIZE = {FP32: 4, INT8: 1, FP16: 2, BF16: 2}
+DTYPE_NAME = {FP32: "fp32", INT8: "int8", FP16: "fp16", BF16: "bf16"}
 SENTINEL = 0xA5
 
 _GOLDEN = 0x9E3779B97F4A7C15
@@ -113,6 +114,22 @@ def finite16_from_words(words: np.ndarray, dtype: int) -> np.ndarray:
         return (sign | (exp << 7) | (w & 0x7F)).astype(np.uint16)
     exp = 5 + (w >> 10) % 21                            # biased 5..25
     return (sign | (exp << 10) | (w & 0x3FF)).astype(np.uint16)
+
+
+def finite16_(t, dtype: int, chunk: int = 1 << 26) -> None:
+    """In place on a torch tensor of 16-bit words (any 2-byte dtype, CPU or GPU):
+    the same mapping as :func:`finite16_from_words`, integer ops only."""
+    import torch
+    v = t.view(torch.int16).view(-1)
+    for i in range(0, v.numel(), chunk):
+        w = v[i:i + chunk].to(torch.int32) & 0xFFFF
+        sign = w & 0x8000
+        if dtype == BF16:
+            out = sign | ((100 + (w >> 7) % 55) << 7) | (w & 0x7F)
+        else:
+            out = sign | ((5 + (w >> 10) % 21) << 10) | (w & 0x3FF)
+        out -= (out >> 15) << 16                        # to the int16 range
+        v[i:i + chunk] = out.to(torch.int16)
 
 
 def bias_values(seed: int, P: int, nblk: int, hidden: int, dtype: int) -> np.ndarray:
@@ -191,7 +208,7 @@ class Workload:
 
     def summary(self) -> dict:
         return {"workload": self.name, "P": self.P,
-                "dtype": "fp32" if self.dtype == FP32 else "int8",
+                "dtype": DTYPE_NAME[self.dtype],
                 "core_num": self.core_num, "signal": [self.P, self.S],
                 "in_slab_bytes": self.in_slab, "tgt_slab_bytes": self.tgt_slab,
                 "payload_bytes": self.payload_bytes}
@@ -242,6 +259,25 @@ def workload(k: int, scale: int = 1) -> Workload:
     raise ValueError(f"no workload c{k}")
 
 
+def bias_workload(dtype: int = BF16, scale: int = 1) -> Workload:
+    """c5's exchange in 16 bits with the bias Add fused in front: the tail of the
+    CANN BatchMatMulReduceScatterAllToAll op with a BF16 (or FP16) x, per rank
+    temp2 (E/ep=8, ep*C=8*2048, H/tp=2048) plus bias (E/ep, 1, H/tp), then the
+    AllToAll; nblk = E/ep = 8, rows of H/tp = 2048 elements, core_num 256.
+    The payload is finite 16-bit floats (:func:`input16_np`); the bias comes
+    from :func:`bias_values` with seed ``payload_seed + 1``."""
+    P, A, H = 8, 8, 2048
+    n = (1 << 25) // scale
+    C = np.full((P, P), n, dtype=np.int32)
+    slab = P * n * 2
+    tag = "bf16_fp32bias" if dtype == BF16 else "fp16_fp16bias"
+    return Workload(f"c5b_p8_{tag}_bmm_rs_a2a", f"P=8 {tag} equal counts 2^25, bias Add fused, "
+                    "(E/ep=8, ep*C=8*2048, H/tp=2048) -> (E=64, C=2048, H/tp=2048), core_num 256",
+                    P, dtype, 256, 256, slab, slab, C, 1005,
+                    extra={"E_over_ep": A, "ep": 8, "C": 2048 // scale, "H_over_tp": H,
+                           "nblk": A, "hidden": H})
+
+
 def custom(P: int, dtype: int, counts: np.ndarray, core_num: int = 1, S: int | None = None,
            in_slab: int | None = None, tgt_slab: int | None = None, seed: int = 7,
            name: str = "custom") -> Workload:
@@ -266,6 +302,33 @@ def input_bytes_np(w: Workload) -> np.ndarray:
     if w.routing is None:
         return random_bytes_np(w.payload_seed, 0, w.in_bytes)
     return _moe_input(w, np)
+
+
+def input16_np(w: Workload) -> np.ndarray:
+    """Input allocation of finite 16-bit floats (FP16/BF16 workloads), uint8 view."""
+    words = random_bytes_np(w.payload_seed, 0, w.in_bytes).view(np.uint16)
+    return finite16_from_words(words, w.dtype).view(np.uint8)
+
+
+def input16_tensor(w: Workload, device):
+    """:func:`input16_np` built on ``device`` (flat uint8 torch tensor)."""
+    t = input_tensor(w, device)
+    finite16_(t, w.dtype)
+    return t
+
+
+def bias_np(w: Workload, nblk: int, hidden: int) -> np.ndarray:
+    return bias_values(w.payload_seed + 1, w.P, nblk, hidden, w.dtype)
+
+
+def bias_tensor(w: Workload, nblk: int, hidden: int, device):
+    """The bias as the torch dtype the library takes: float32 for BF16 payloads,
+    float16 for FP16."""
+    import torch
+    b = bias_np(w, nblk, hidden)
+    if w.dtype == FP16:
+        return torch.from_numpy(b.view(np.float16).copy()).to(device)
+    return torch.from_numpy(b).to(device)
 
 
 def input_tensor(w: Workload, device):

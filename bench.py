@@ -27,9 +27,11 @@ METRIC = "all_to_all_v achieved HBM GB/s (read+write) and % of MI355X peak, 1 GP
 PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
 # name -> (workload index, sub-blocks per segment).  c5u is c5's exchange taken
 # on the source's own temp3 layout (E/ep, ep*C, H/tp): the blocked exchange
-# with nblk = E/ep = 8.
+# with nblk = E/ep = 8.  c5b is that exchange in BF16 with the bias Add fused
+# in front (k = 0 marks the bias workload).
 WORKLOADS = {"c1": (1, 1), "c2": (2, 1), "c3": (3, 1), "c4": (4, 1), "c5": (5, 1),
-             "c5u": (5, 8)}
+             "c5u": (5, 8), "c5b": (0, 8)}
+DTYPE_NAMES = {0: "fp32", 1: "u8", 2: "fp16", 3: "bf16"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "copy_kernel_traffic.json")
 
 
@@ -63,11 +65,18 @@ def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
     from all_movement_amd import workloads as wl
 
     dev = torch.device("cuda:0")
-    w = wl.workload(k)
-    if nblk > 1:
-        w.name += f"_temp3_layout_nblk{nblk}"
+    bias, hidden, bias_bytes = None, 0, 0
+    if k == 0:
+        w = wl.bias_workload(wl.BF16)
+        hidden = w.extra["hidden"]
+        bias = wl.bias_tensor(w, nblk, hidden, dev)
+        bias_bytes = bias.numel() * bias.element_size()
+    else:
+        w = wl.workload(k)
+        if nblk > 1:
+            w.name += f"_temp3_layout_nblk{nblk}"
     log(f"[bench] {w.name}: payload {w.payload_bytes} B, generating inputs on the GPU")
-    inp = wl.input_tensor(w, dev)
+    inp = wl.input16_tensor(w, dev) if k == 0 else wl.input_tensor(w, dev)
     tgt = torch.full((w.tgt_bytes,), wl.SENTINEL, dtype=torch.uint8, device=dev)
     sig = torch.zeros((w.P, w.S), dtype=torch.int32, device=dev)
     sc = torch.from_numpy(w.counts).to(dev)
@@ -78,7 +87,8 @@ def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
     torch.cuda.synchronize()
 
     for _ in range(warmup):
-        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, nblk=nblk)
+        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, nblk=nblk, bias=bias,
+               hidden=hidden)
     torch.cuda.synchronize()
     if ex.query_error() != a2av.OK:
         raise RuntimeError("warmup run reported a device-side error")
@@ -86,7 +96,8 @@ def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
 
     t0 = time.perf_counter()
     for _ in range(steps):
-        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, nblk=nblk)
+        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, nblk=nblk, bias=bias,
+               hidden=hidden)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if ex.query_error() != a2av.OK:
@@ -94,7 +105,8 @@ def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
     k1_us, k2_us, k2_launches, runs = ex.profile()
     ex.close()
     sec = t1 - t0
-    moved = 2 * w.payload_bytes            # each payload byte read once, written once
+    # Each payload byte read once and written once (plus the bias, read once).
+    moved = 2 * w.payload_bytes + bias_bytes
     res = {
         "w": w, "info": info, "sec": sec, "steps": steps, "moved": moved,
         "gbps": moved * steps / sec / 1e9, "ms_per_step": sec / steps * 1e3,
@@ -133,18 +145,31 @@ def cpu_baseline(k: int, min_seconds: float = 10.0):
 
     # Sample: the same workload shape at a reduced size (c5 at 1/8: P=8 equal
     # counts of 2^22 fp32, 1 GiB of payload; c3/c4 at 1/4), run whole.
-    scale = {1: 1, 2: 1, 3: 4, 4: 4, 5: 8}[k]
-    w = wl.workload(k, scale=scale)
-    inp = wl.input_bytes_np(w)
+    # c5b (the bias workload) at 1/16.
+    scale = {0: 16, 1: 1, 2: 1, 3: 4, 4: 4, 5: 8}[k]
+    if k == 0:
+        w = wl.bias_workload(wl.BF16, scale=scale)
+        A, H = w.extra["nblk"], w.extra["hidden"]
+        inp = wl.input16_np(w)
+        bias = wl.bias_np(w, A, H)
+        what = "checks + transpose + displacements + one fp32 add and bf16 rounding per element"
+    else:
+        w = wl.workload(k, scale=scale)
+        inp = wl.input_bytes_np(w)
+        what = "checks + transpose + displacements + one memcpy per segment + signal"
     tgt = np.full(w.tgt_bytes, wl.SENTINEL, np.uint8)
     rc = np.zeros((w.P, w.P), np.int32)
     times = []
     t_end = time.perf_counter() + min_seconds
     while len(times) < 3 or time.perf_counter() < t_end:
         sig = np.zeros((w.P, w.S), np.int32)
+        kw = dict(P=w.P, S=w.S, in_slab=w.in_slab, tgt_slab=w.tgt_slab, core_num=w.core_num,
+                  dtype=w.dtype)
         t0 = time.perf_counter()
-        st = oracle.run(inp, tgt, sig, w.counts, rc, P=w.P, S=w.S, in_slab=w.in_slab,
-                        tgt_slab=w.tgt_slab, core_num=w.core_num, dtype=w.dtype)
+        if k == 0:
+            st = oracle.run_bias(inp, tgt, sig, w.counts, rc, bias, nblk=A, hidden=H, **kw)
+        else:
+            st = oracle.run(inp, tgt, sig, w.counts, rc, **kw)
         times.append(time.perf_counter() - t0)
         assert st == oracle.OK
     times.sort()
@@ -153,8 +178,8 @@ def cpu_baseline(k: int, min_seconds: float = 10.0):
         "value": round(2 * w.payload_bytes / med / 1e9, 3), "unit": "GB/s", "cores": 1,
         "kind": "oracle",
         "sample": f"{w.name} at 1/{scale} size ({w.payload_bytes} payload bytes), whole oracle "
-                  f"(checks + transpose + displacements + one memcpy per segment + signal), "
-                  f"single thread, median of {len(times)} runs over {sum(times):.1f} s",
+                  f"({what}), single thread, median of {len(times)} runs over "
+                  f"{sum(times):.1f} s",
         "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
         "cpu_model": _cpu_model(),
     }
@@ -176,7 +201,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="c3,c4,c5u", help="other workloads reported beside it")
+    ap.add_argument("--also", default="c3,c4,c5u,c5b", help="other workloads reported beside it")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain torch device copy of MIB MiB --steps times (the "
@@ -221,7 +246,7 @@ def main():
         "metric": METRIC, "value": round(main_res["gbps"], 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(main_res["ms_per_step"], 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp32" if w.dtype == 0 else "u8",
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAMES[w.dtype],
         "data": "synthetic (seeded SplitMix64 payload, seeded count matrices)",
         "config": {"workload": w.name, "P": w.P, "core_num": w.core_num,
                    "blocks": info.blocks, "workgroups": info.workgroups,

@@ -43,9 +43,10 @@ extern "C" {
 
 typedef struct a2av_handle a2av_handle;
 
-/* Payload element type.  Only FP32 and INT8 exist ("Constraints and
- * diagnostics" section of the PyPTO page); payload moves as raw bits. */
-enum a2av_dtype { A2AV_FP32 = 0, A2AV_INT8 = 1 };
+/* Payload element type.  a2av_run / a2av_run_blocked take FP32 and INT8 only
+ * ("Constraints and diagnostics" section of the PyPTO page) and move raw
+ * bits.  FP16 and BF16 are the payloads of a2av_run_bias, which adds. */
+enum a2av_dtype { A2AV_FP32 = 0, A2AV_INT8 = 1, A2AV_FP16 = 2, A2AV_BF16 = 3 };
 
 /* Status codes.  NULLPTR is kept apart from INVALID_ARGS as in the aclnn
  * error table (ACLNN_ERR_PARAM_NULLPTR vs ACLNN_ERR_PARAM_INVALID). */
@@ -153,6 +154,33 @@ int a2av_run(a2av_handle *h, const void *input, void *target, int32_t *signal,
 int a2av_run_blocked(a2av_handle *h, const void *input, void *target, int32_t *signal,
                      const int32_t *send_counts, int32_t *recv_counts, int32_t P,
                      int64_t core_num, int32_t dtype, int32_t nblk, void *stream);
+
+/*
+ * The blocked exchange with the bias Add fused in front: the tail of the CANN
+ * BatchMatMulReduceScatterAllToAll op ("Function and computation flow":
+ * temp3 = temp2 + bias, y = AllToAll(temp3); "Parameters": BFLOAT16 x takes
+ * an FP32 bias and adds in FP32, FLOAT16 x takes an FP16 bias; "Constraints",
+ * yShardType 0: bias (E/ep, 1, H/tp) broadcast over the C rows).
+ *   input   temp2 of every rank, as in a2av_run_blocked (nblk = E/ep
+ *           block-rows per source), 16-bit elements (FP16 or BF16 bits)
+ *   bias    device, [P, nblk, hidden] values: FP32 for BF16, FP16 for FP16;
+ *           element h of a row in block-row a of source s gets
+ *           bias[(s*nblk + a)*hidden + h]; read only
+ *   hidden  elements per row (H/tp)
+ * Every output element is the sum formed in FP32 and rounded once, to
+ * nearest even, to the payload type; target, signal and recv_counts are as
+ * in a2av_run_blocked.  Counts must be whole rows of every sub-block
+ * (multiples of nblk * hidden; INVALID_ARGS on the device otherwise).
+ * Host checks, first failure wins: NULLPTR (any of the six operands) ->
+ * UNSUPPORTED_DTYPE (not FP16/BF16) -> INVALID_ARGS (P, nblk < 1, hidden < 1,
+ * core_num, S < B) -> LAUNCH_CAPACITY -> INVALID_ARGS (two of the six
+ * operands share a byte; a slab not a whole number of elements; and, as
+ * limits of this implementation, hidden not a multiple of 8 or above 2^28,
+ * or input, target, bias, slabs or the chunk limit not 16-byte aligned).
+ */
+int a2av_run_bias(a2av_handle *h, const void *input, void *target, int32_t *signal,
+                  const int32_t *send_counts, int32_t *recv_counts, const void *bias, int32_t P,
+                  int64_t core_num, int32_t dtype, int32_t nblk, int32_t hidden, void *stream);
 
 /* Free the workspace and the handle (synchronizes the device first).
  * NULL is accepted and ignored. */

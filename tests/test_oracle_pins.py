@@ -378,6 +378,32 @@ def test_fill_random_torch_matches_numpy():
     np.testing.assert_array_equal(wl.random_bytes_np(9, 5, 20), wl.random_bytes_np(9, 0, 25)[5:])
 
 
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.FP16])
+def test_finite16_torch_matches_numpy(dtype):
+    import torch
+    n = 5000
+    t = torch.empty(2 * n, dtype=torch.uint8)
+    wl.fill_random_(t, 55)
+    wl.finite16_(t, dtype, chunk=777)
+    want = wl.finite16_from_words(wl.random_bytes_np(55, 0, 2 * n).view(np.uint16), dtype)
+    np.testing.assert_array_equal(t.numpy().view(np.uint16), want)
+    # Every mapped word is a finite, non-zero float of the type.
+    f = want.view(np.float16).astype(np.float32) if dtype == wl.FP16 else \
+        (want.astype(np.uint32) << 16).view(np.float32)
+    assert np.isfinite(f).all() and (f != 0).all()
+
+
+def test_bias_workload_shape():
+    w = wl.bias_workload(wl.BF16)
+    assert w.payload_bytes == 4 * 2**30 and w.elem == 2
+    A, H = w.extra["nblk"], w.extra["hidden"]
+    assert (w.counts % (A * H) == 0).all()
+    assert w.extra["E_over_ep"] * w.extra["ep"] * w.extra["C"] * H == w.counts[0].sum()
+    assert wl.bias_np(w, A, H).shape == (w.P, A, H) and wl.bias_np(w, A, H).dtype == np.float32
+    w16 = wl.bias_workload(wl.FP16, scale=64)
+    assert wl.bias_np(w16, A, H).dtype == np.uint16
+
+
 def test_workload_shapes():
     w3 = wl.workload(3)
     assert w3.payload_bytes == 448 * 2**20
