@@ -278,6 +278,32 @@ def bias_workload(dtype: int = BF16, scale: int = 1) -> Workload:
                            "nblk": A, "hidden": H})
 
 
+def indexed_workload(scale: int = 1) -> Workload:
+    """c3's MoE dispatch taken as the indexed exchange: input slab s is source
+    s's token table (tokens x 7168 int8 rows, every token stored once) and the
+    gather list index[s] names, for d = 0..P-1 in turn, the tokens routed to d
+    in ascending token order.  Same routing, counts, core_num and payload
+    stream as c3, so the token table of source s is byte for byte the ``tok``
+    block c3 packs from; ``extra`` holds the int32 [P, 2*tokens] index, the
+    row length and the index stride (every token goes to exactly 2 ranks)."""
+    w3 = workload(3, scale)
+    P, tokens, H = w3.P, w3.routing.shape[1], w3.token_bytes
+    index = np.zeros((P, 2 * tokens), np.int32)
+    for s in range(P):
+        k = 0
+        for d in range(P):
+            t = np.nonzero(w3.routing[s, :, d])[0]
+            index[s, k:k + t.size] = t
+            k += t.size
+        assert k == 2 * tokens
+    return Workload("c3i_p8_int8_moe_top2_zipf1.2_indexed",
+                    "P=8 int8 MoE dispatch as a row gather: token tables of 4096 x 7168, "
+                    "top-2 Zipf(1.2) routing as the index, core_num 64",
+                    P, INT8, w3.core_num, w3.S, tokens * H, w3.tgt_slab, w3.counts.copy(),
+                    w3.payload_seed,
+                    extra={"index": index, "row_elems": H, "index_stride": 2 * tokens})
+
+
 def custom(P: int, dtype: int, counts: np.ndarray, core_num: int = 1, S: int | None = None,
            in_slab: int | None = None, tgt_slab: int | None = None, seed: int = 7,
            name: str = "custom") -> Workload:

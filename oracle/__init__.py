@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.a2av_oracle_run_blocked.restype = ctypes.c_int
         L.a2av_oracle_run_bias.argtypes = run_args + [i32, vp, i32]
         L.a2av_oracle_run_bias.restype = ctypes.c_int
+        L.a2av_oracle_run_indexed.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i64,
+                                              i32, i64, i32, i64]
+        L.a2av_oracle_run_indexed.restype = ctypes.c_int
         L.a2av_oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         L.a2av_oracle_f32_to_bf16.restype = ctypes.c_uint16
         L.a2av_oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
@@ -156,6 +159,23 @@ def run_bias(input_bytes: np.ndarray, target_bytes: np.ndarray, signal: np.ndarr
         _ptr(input_bytes), _ptr(target_bytes), _ptr(signal), _ptr(send_counts),
         _ptr(recv_counts), P, S, in_slab, tgt_slab, core_num, dtype, capacity, nblk,
         _ptr(bias), hidden))
+
+
+def run_indexed(input_bytes: np.ndarray, target_bytes: np.ndarray, signal: np.ndarray,
+                send_counts: np.ndarray, recv_counts: np.ndarray, index: np.ndarray | None, *,
+                P: int, S: int, in_slab: int, tgt_slab: int, core_num: int, dtype: int,
+                row_elems: int, index_stride: int, capacity: int = 0) -> int:
+    """The indexed exchange: source s sends the rows of its input table named by
+    index[s] (int32 [P, index_stride]), in destination order."""
+    for a, n in ((input_bytes, P * in_slab), (target_bytes, P * tgt_slab)):
+        assert a.dtype == np.uint8 and a.size == n
+    assert signal.dtype == np.int32 and signal.size == P * S
+    if index is not None:
+        assert index.dtype == np.int32 and index.size == P * index_stride
+    return int(lib().a2av_oracle_run_indexed(
+        _ptr(input_bytes), _ptr(target_bytes), _ptr(signal), _ptr(send_counts),
+        _ptr(recv_counts), _ptr(index), P, S, in_slab, tgt_slab, core_num, dtype, capacity,
+        row_elems, index_stride))
 
 
 def f32_to_bf16(x: float) -> int:

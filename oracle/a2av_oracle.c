@@ -502,6 +502,157 @@ int a2av_oracle_run_bias(const void *input, void *target, int32_t *signal,
     return OR_OK;
 }
 
+/* ------------------------------------------------------------ indexed exchange */
+
+/*
+ * indexed_all_to_all_v(input, target, signal, send_counts, recv_counts, index,
+ * core_num): the variant named in the "A5 URMA indexed exchange" section of
+ * the LowerL2TensorCollectives page, which gives its six operands (index the
+ * sixth; input and index local to the sender, send_counts visible to peers)
+ * but not what index means.  Reading taken here: index is the sender's row
+ * gather list.  Input slab s is a table of rows of row_elems elements
+ * (row_bytes = row_elems * e; the table holds in_slab / row_bytes rows); the
+ * rows source s sends, in destination order d = 0..P-1 as in the plain
+ * exchange, are the table rows named by index[s][0], index[s][1], ...  Row j
+ * of segment s -> d is table row index[s][R(s,d) + j], R(s,d) the rows s
+ * sends to destinations below d.  Target and signal are as in the plain
+ * exchange: segment s -> d lands at rdispl[d][s] of slab d.  index is P
+ * slabs of index_stride int32 entries; the same row may be named any number
+ * of times.  This is the dispatch of an MoE layer with the pack folded in:
+ * a token routed to two ranks is stored once and named twice.
+ * Checks, first failure wins, nothing written on failure:
+ *   1. a null operand (six)                             -> NULLPTR
+ *   2. dtype not FP32 / INT8                            -> UNSUPPORTED_DTYPE
+ *   3. P outside [1, 64], S < 1, a slab size < 1, row_elems < 1,
+ *      index_stride < 1                                 -> INVALID_ARGS
+ *   4-6. core_num range, S < B, launch capacity, as in check_args
+ *   7. two of the six operands share a byte (index covers P*index_stride
+ *      int32)                                           -> INVALID_ARGS
+ *   8. a slab size that is not a whole number of elements -> INVALID_ARGS
+ *   9. a negative count                                 -> INVALID_ARGS
+ *  9b. a count that is not whole rows (row_elems does not divide it)
+ *                                                       -> INVALID_ARGS
+ *  10. a source that sends more rows than index_stride, or a destination
+ *      column whose bytes exceed tgt_slab               -> OVER_CAPACITY
+ * 10b. an index entry in use outside [0, in_slab / row_bytes)
+ *                                                       -> INVALID_ARGS
+ *  11. signal[r][b] (r < P, b < B) not all equal        -> INVALID_ARGS
+ * Pinned by: index[s][k] = k on a packed input is the plain exchange; numpy
+ * row gathers followed by the brute-force exchange; the MoE dispatch of
+ * token tables equal to the plain exchange of the packed (duplicated)
+ * tokens; every diagnostic in the tests.
+ */
+static int check_indexed(const void *input, const void *target, const int32_t *signal,
+                         const int32_t *send_counts, const int32_t *recv_counts,
+                         const int32_t *index, int32_t P, int32_t S, int64_t in_slab,
+                         int64_t tgt_slab, int64_t core_num, int32_t dtype, int64_t capacity,
+                         int32_t row_elems, int64_t index_stride)
+{
+    if (!input || !target || !signal || !send_counts || !recv_counts || !index)
+        return OR_ERR_NULLPTR;
+    if (dtype != OR_DTYPE_FP32 && dtype != OR_DTYPE_INT8)
+        return OR_ERR_UNSUPPORTED_DTYPE;
+    if (P < 1 || P > OR_MAX_P || S < 1 || in_slab < 1 || tgt_slab < 1 || row_elems < 1 ||
+        index_stride < 1)
+        return OR_ERR_INVALID_ARGS;
+    if (core_num < 1 || core_num > OR_INT32_MAX)
+        return OR_ERR_INVALID_ARGS;
+    int64_t B = a2av_oracle_blocks(P, core_num);
+    if ((int64_t)S < B)
+        return OR_ERR_INVALID_ARGS;
+    if (B > 1 && capacity > 0 && B > capacity)
+        return OR_ERR_LAUNCH_CAPACITY;
+
+    uintptr_t base[6] = {(uintptr_t)input, (uintptr_t)target, (uintptr_t)signal,
+                         (uintptr_t)send_counts, (uintptr_t)recv_counts, (uintptr_t)index};
+    uint64_t len[6] = {(uint64_t)P * (uint64_t)in_slab, (uint64_t)P * (uint64_t)tgt_slab,
+                       (uint64_t)P * (uint64_t)S * 4u, (uint64_t)P * (uint64_t)P * 4u,
+                       (uint64_t)P * (uint64_t)P * 4u, (uint64_t)P * (uint64_t)index_stride * 4u};
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j)
+            if (ranges_overlap(base[i], len[i], base[j], len[j]))
+                return OR_ERR_INVALID_ARGS;
+
+    int64_t e = elem_size(dtype);
+    if (in_slab % e != 0 || tgt_slab % e != 0)
+        return OR_ERR_INVALID_ARGS;
+
+    for (int32_t i = 0; i < P * P; ++i)
+        if (send_counts[i] < 0)
+            return OR_ERR_INVALID_ARGS;
+    for (int32_t i = 0; i < P * P; ++i)
+        if (send_counts[i] % row_elems != 0)
+            return OR_ERR_INVALID_ARGS;
+
+    for (int32_t s = 0; s < P; ++s) {
+        int64_t rows = 0;
+        for (int32_t d = 0; d < P; ++d)
+            rows += send_counts[s * P + d] / row_elems;
+        if (rows > index_stride)
+            return OR_ERR_OVER_CAPACITY;
+    }
+    for (int32_t d = 0; d < P; ++d) {
+        int64_t col = 0;
+        for (int32_t s = 0; s < P; ++s)
+            col += (int64_t)send_counts[s * P + d];
+        if (col * e > tgt_slab)
+            return OR_ERR_OVER_CAPACITY;
+    }
+
+    int64_t table_rows = in_slab / (row_elems * e);
+    for (int32_t s = 0; s < P; ++s) {
+        int64_t rows = 0;
+        for (int32_t d = 0; d < P; ++d)
+            rows += send_counts[s * P + d] / row_elems;
+        for (int64_t k = 0; k < rows; ++k) {
+            int32_t v = index[(int64_t)s * index_stride + k];
+            if (v < 0 || (int64_t)v >= table_rows)
+                return OR_ERR_INVALID_ARGS;
+        }
+    }
+
+    int32_t first = signal[0];
+    for (int32_t r = 0; r < P; ++r)
+        for (int64_t b = 0; b < B; ++b)
+            if (signal[(int64_t)r * S + b] != first)
+                return OR_ERR_INVALID_ARGS;
+    return OR_OK;
+}
+
+int a2av_oracle_run_indexed(const void *input, void *target, int32_t *signal,
+                            const int32_t *send_counts, int32_t *recv_counts,
+                            const int32_t *index, int32_t P, int32_t S, int64_t in_slab,
+                            int64_t tgt_slab, int64_t core_num, int32_t dtype, int64_t capacity,
+                            int32_t row_elems, int64_t index_stride)
+{
+    int st = check_indexed(input, target, signal, send_counts, recv_counts, index, P, S,
+                           in_slab, tgt_slab, core_num, dtype, capacity, row_elems, index_stride);
+    if (st != OR_OK)
+        return st;
+
+    int64_t e = elem_size(dtype);
+    int64_t row_bytes = row_elems * e;
+    int64_t B = a2av_oracle_blocks(P, core_num);
+    int64_t sdispl[OR_MAX_P * OR_MAX_P];
+    int64_t rdispl[OR_MAX_P * OR_MAX_P];
+    transpose_counts(send_counts, recv_counts, P);
+    displacements(send_counts, P, e, sdispl, rdispl);
+    for (int32_t s = 0; s < P; ++s) {
+        const uint8_t *table = (const uint8_t *)input + (int64_t)s * in_slab;
+        const int32_t *list = index + (int64_t)s * index_stride;
+        int64_t k = 0; /* position in source s's gather list */
+        for (int32_t d = 0; d < P; ++d) {
+            int64_t rows = send_counts[s * P + d] / row_elems;
+            uint8_t *seg = (uint8_t *)target + (int64_t)d * tgt_slab + rdispl[d * P + s];
+            for (int64_t j = 0; j < rows; ++j, ++k)
+                memcpy(seg + j * row_bytes, table + (int64_t)list[k] * row_bytes,
+                       (size_t)row_bytes);
+        }
+    }
+    arrive(signal, P, S, B);
+    return OR_OK;
+}
+
 /* Displacements alone, for the closed-form pins (no checks). */
 void a2av_oracle_displacements(const int32_t *send_counts, int32_t P, int32_t dtype,
                                int64_t *sdispl, int64_t *rdispl)

@@ -658,3 +658,178 @@ def test_bias_diagnostics():
                          tgt_slab=tgt_slab, core_num=1, dtype=oracle.BF16, nblk=nblk,
                          hidden=hidden)
     assert st == oracle.ERR_INVALID_ARGS
+
+
+# ------------------------------------------------------------ indexed exchange
+
+def _run_indexed(inp, C, index, *, P, in_slab, tgt_slab, dtype, row_elems, stride,
+                 core_num=1, signal=None):
+    S = max(1, oracle.blocks(P, core_num))
+    tgt = np.full(P * tgt_slab, wl.SENTINEL, np.uint8)
+    sig = np.zeros((P, S), np.int32) if signal is None else signal.copy()
+    rc = np.full((P, P), -7, np.int32)
+    st = oracle.run_indexed(inp, tgt, sig, np.ascontiguousarray(C, np.int32), rc,
+                            None if index is None else np.ascontiguousarray(index, np.int32),
+                            P=P, S=S, in_slab=in_slab, tgt_slab=tgt_slab, core_num=core_num,
+                            dtype=dtype, row_elems=row_elems, index_stride=stride)
+    return st, tgt, sig, rc
+
+
+@pytest.mark.parametrize("dtype", [oracle.FP32, oracle.INT8])
+def test_indexed_identity_index_is_the_plain_exchange(dtype):
+    # index[s][k] = k on a packed input: the gather is the identity.
+    rng = np.random.default_rng(31)
+    P, R = 5, 3
+    e = 4 if dtype == oracle.FP32 else 1
+    C = (rng.integers(0, 7, size=(P, P)) * R).astype(np.int32)
+    in_slab = int(C.sum(axis=1).max()) * e + 8 * e
+    tgt_slab = int(C.sum(axis=0).max()) * e + 4 * e
+    inp = wl.random_bytes_np(5, 0, P * in_slab)
+    stride = int(C.sum(axis=1).max()) // R + 2
+    index = np.tile(np.arange(stride, dtype=np.int32), (P, 1))
+    st, tgt, sig, rc = _run_indexed(inp, C, index, P=P, in_slab=in_slab, tgt_slab=tgt_slab,
+                                    dtype=dtype, row_elems=R, stride=stride, core_num=7)
+    assert st == oracle.OK
+    tgt2 = np.full(P * tgt_slab, wl.SENTINEL, np.uint8)
+    sig2 = np.zeros_like(sig)
+    rc2 = np.zeros((P, P), np.int32)
+    assert oracle.run(inp, tgt2, sig2, C, rc2, P=P, S=sig.shape[1], in_slab=in_slab,
+                      tgt_slab=tgt_slab, core_num=7, dtype=dtype) == oracle.OK
+    np.testing.assert_array_equal(tgt, tgt2)
+    np.testing.assert_array_equal(sig, sig2)
+    np.testing.assert_array_equal(rc, C.T)
+
+
+@pytest.mark.parametrize("P,R,dtype", [(1, 4, oracle.FP32), (2, 1, oracle.INT8),
+                                       (4, 3, oracle.INT8), (7, 2, oracle.FP32)])
+def test_indexed_numpy_gather_then_brute_force(P, R, dtype):
+    # numpy fancy indexing builds each source's packed rows; the pure-Python
+    # brute force then places them.  Repeats and arbitrary order in index.
+    rng = np.random.default_rng(P * 10 + R)
+    e = 4 if dtype == oracle.FP32 else 1
+    rb = R * e
+    table_rows = 11
+    in_slab = table_rows * rb + 3 * e          # a partial row at the end is never named
+    C = (rng.integers(0, 5, size=(P, P)) * R).astype(np.int32)
+    rows = C.sum(axis=1) // R
+    stride = int(rows.max()) + 3
+    index = rng.integers(0, table_rows, size=(P, stride)).astype(np.int32)
+    index[:, -1] = -99                         # entries past a source's rows are never read
+    tgt_slab = int(C.sum(axis=0).max()) * e + 2 * e
+    inp = wl.random_bytes_np(P + R, 0, P * in_slab)
+    st, tgt, _, _ = _run_indexed(inp, C, index, P=P, in_slab=in_slab, tgt_slab=tgt_slab,
+                                 dtype=dtype, row_elems=R, stride=stride)
+    assert st == oracle.OK
+    packed = []
+    for s in range(P):
+        table = inp[s * in_slab:s * in_slab + table_rows * rb].reshape(table_rows, rb)
+        packed.append(table[index[s, :rows[s]]].tobytes())
+    old = [bytes([wl.SENTINEL]) * tgt_slab] * P
+    want = brute.exchange(packed, old, C.tolist(), e)
+    assert tgt.tobytes() == b"".join(want)
+
+
+def test_indexed_tiny_brute_force_every_count_matrix():
+    import itertools
+    P, R = 2, 2
+    rb = R
+    for flat in itertools.product([0, 2, 4], repeat=4):
+        C = np.array(flat, np.int32).reshape(P, P)
+        rows = C.sum(axis=1) // R
+        stride = max(1, int(rows.max()))
+        index = np.array([[(3 * s + k) % 3 for k in range(stride)] for s in range(P)], np.int32)
+        in_slab = 3 * rb
+        tgt_slab = 8 + 1
+        inp = wl.random_bytes_np(sum(flat) + 1, 0, P * in_slab)
+        st, tgt, sig, rc = _run_indexed(inp, C, index, P=P, in_slab=in_slab, tgt_slab=tgt_slab,
+                                        dtype=oracle.INT8, row_elems=R, stride=stride)
+        assert st == oracle.OK
+        packed = [b"".join(inp[s * in_slab + index[s, k] * rb:s * in_slab + index[s, k] * rb + rb]
+                           .tobytes() for k in range(rows[s])) for s in range(P)]
+        want = brute.exchange(packed, [bytes([wl.SENTINEL]) * tgt_slab] * P, C.tolist(), 1)
+        assert tgt.tobytes() == b"".join(want), flat
+        np.testing.assert_array_equal(rc, C.T)
+        assert (sig == 1).all()
+
+
+def test_indexed_moe_dispatch_equals_the_packed_exchange():
+    # The MoE dispatch from token tables and the routing's gather list gives
+    # exactly what the plain exchange gives on c3's packed input, in which a
+    # token routed to two ranks is stored twice.
+    w3 = wl.workload(3, scale=64)
+    wi = wl.indexed_workload(scale=64)
+    np.testing.assert_array_equal(wi.counts, w3.counts)
+    tgt3 = np.full(w3.tgt_bytes, wl.SENTINEL, np.uint8)
+    sig3 = np.zeros((w3.P, w3.S), np.int32)
+    rc3 = np.zeros((w3.P, w3.P), np.int32)
+    assert oracle.run(wl.input_bytes_np(w3), tgt3, sig3, w3.counts, rc3, P=w3.P, S=w3.S,
+                      in_slab=w3.in_slab, tgt_slab=w3.tgt_slab, core_num=w3.core_num,
+                      dtype=w3.dtype) == oracle.OK
+    st, tgt, sig, rc = _run_indexed(wl.input_bytes_np(wi), wi.counts, wi.extra["index"], P=wi.P,
+                                    in_slab=wi.in_slab, tgt_slab=wi.tgt_slab, dtype=wi.dtype,
+                                    row_elems=wi.extra["row_elems"],
+                                    stride=wi.extra["index_stride"], core_num=wi.core_num)
+    assert st == oracle.OK
+    np.testing.assert_array_equal(tgt, tgt3)
+    np.testing.assert_array_equal(sig, sig3)
+    assert wi.in_slab * 2 == w3.in_slab                # half the input: no duplicated tokens
+
+
+def test_indexed_diagnostics():
+    P, R = 3, 2
+    rng = np.random.default_rng(4)
+    C = (rng.integers(1, 4, size=(P, P)) * R).astype(np.int32)
+    rows = C.sum(axis=1) // R
+    stride = int(rows.max())
+    table_rows = 6
+    in_slab, tgt_slab = table_rows * R * 4, int(C.sum(axis=0).max()) * 4
+    inp = wl.random_bytes_np(1, 0, P * in_slab)
+    index = rng.integers(0, table_rows, size=(P, stride)).astype(np.int32)
+    kw = dict(P=P, in_slab=in_slab, tgt_slab=tgt_slab, dtype=oracle.FP32, row_elems=R,
+              stride=stride)
+
+    def status(C=C, index=index, **over):
+        args = dict(kw)
+        args.update(over)
+        st, tgt, sig, rc = _run_indexed(inp[:P * args["in_slab"]].copy(), C, index, **args)
+        if st != oracle.OK:
+            assert (tgt == wl.SENTINEL).all() and (rc == -7).all() and (sig == 0).all()
+        return st
+
+    assert status() == oracle.OK
+    assert status(index=None) == oracle.ERR_NULLPTR
+    assert status(dtype=oracle.BF16) == oracle.ERR_UNSUPPORTED_DTYPE
+    assert status(row_elems=0) == oracle.ERR_INVALID_ARGS
+    assert status(stride=0, index=np.zeros((P, 1), np.int32)[:, :0].copy()) == oracle.ERR_INVALID_ARGS
+    C2 = C.copy()
+    C2[1, 2] += 1                                     # not whole rows
+    assert status(C=C2) == oracle.ERR_INVALID_ARGS
+    C3 = C.copy()
+    C3[0, 0] = -2
+    assert status(C=C3) == oracle.ERR_INVALID_ARGS
+    C4 = C.copy()
+    C4[0, 0] += 2 * R * (stride - rows[0] + 1)        # more rows than the index holds
+    assert status(C=C4, tgt_slab=tgt_slab * 4) == oracle.ERR_OVER_CAPACITY
+    assert status(tgt_slab=tgt_slab - 4) == oracle.ERR_OVER_CAPACITY
+    for bad in (-1, table_rows):
+        ix = index.copy()
+        ix[2, rows[2] - 1] = bad
+        assert status(index=ix) == oracle.ERR_INVALID_ARGS
+    # Over capacity is reported before a bad index.
+    ix = index.copy()
+    ix[0, 0] = -1
+    assert status(index=ix, tgt_slab=tgt_slab - 4) == oracle.ERR_OVER_CAPACITY
+    # A partial row at the table's end cannot be named.
+    assert status(in_slab=in_slab - 4, index=np.minimum(index, table_rows - 1)) in (
+        oracle.OK, oracle.ERR_INVALID_ARGS)
+    ix = index.copy()
+    ix[1, 0] = table_rows - 1
+    assert status(in_slab=in_slab - 4, index=ix) == oracle.ERR_INVALID_ARGS
+    # The index may not overlap another operand.
+    S = 1
+    tgt = np.zeros(P * tgt_slab, np.uint8)
+    st = oracle.run_indexed(inp, tgt, np.zeros((P, S), np.int32), C, np.zeros((P, P), np.int32),
+                            tgt[:P * stride * 4].view(np.int32), P=P, S=S, in_slab=in_slab,
+                            tgt_slab=tgt_slab, core_num=1, dtype=oracle.FP32, row_elems=R,
+                            index_stride=stride)
+    assert st == oracle.ERR_INVALID_ARGS
