@@ -34,7 +34,8 @@ BF16 = 3
 ELEM_SIZE = {FP32: 4, INT8: 1, FP16: 2, BF16: 2}
 FLAG_PROFILE = 1
 
-EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_run_bias", "a2av_destroy",
+EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_run_bias", "a2av_run_indexed",
+           "a2av_destroy",
            "a2av_blocks", "a2av_check_args", "a2av_query_error", "a2av_launch_info_get", "a2av_profile_read",
            "a2av_status_string", "a2av_last_hip_error"]
 
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.a2av_run_blocked.restype = ctypes.c_int
     L.a2av_run_bias.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp]
     L.a2av_run_bias.restype = ctypes.c_int
+    L.a2av_run_indexed.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i64, vp]
+    L.a2av_run_indexed.restype = ctypes.c_int
     L.a2av_destroy.argtypes = [vp]
     L.a2av_destroy.restype = ctypes.c_int
     L.a2av_blocks.argtypes = [i64, i64]
@@ -123,6 +126,12 @@ def a2av_run_bias(h, input, target, signal, send_counts, recv_counts, bias, P, c
                   nblk, hidden, stream) -> int:
     return lib().a2av_run_bias(h, input, target, signal, send_counts, recv_counts, bias, P,
                                core_num, dtype, nblk, hidden, stream)
+
+
+def a2av_run_indexed(h, input, target, signal, send_counts, recv_counts, index, P, core_num,
+                     dtype, row_elems, index_stride, stream) -> int:
+    return lib().a2av_run_indexed(h, input, target, signal, send_counts, recv_counts, index, P,
+                                  core_num, dtype, row_elems, index_stride, stream)
 
 
 def a2av_destroy(h) -> int:
@@ -234,11 +243,14 @@ class Exchange:
         return t.data_ptr()
 
     def run(self, input, target, signal, send_counts, recv_counts, core_num: int, dtype: int,
-            stream=None, nblk: int = 1, bias=None, hidden: int = 0) -> None:
+            stream=None, nblk: int = 1, bias=None, hidden: int = 0, index=None,
+            row_elems: int = 0) -> None:
         """One exchange; ``nblk`` > 1 runs the blocked exchange (a2av_run_blocked);
         a ``bias`` tensor (float32 for BF16 payloads, float16 for FP16, [P, nblk,
         hidden] elements) runs the exchange with the bias Add fused in
-        (a2av_run_bias)."""
+        (a2av_run_bias); an ``index`` tensor (int32 [P, index_stride] gather
+        lists of rows of ``row_elems`` elements) runs the indexed exchange
+        (a2av_run_indexed)."""
         import torch
         c = self.cfg
         P = c.P
@@ -249,7 +261,14 @@ class Exchange:
         rcp = self._check(recv_counts, P * P * 4, "recv_counts", torch.int32)
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
-        if bias is not None:
+        if index is not None:
+            if index.dim() != 2 or index.shape[0] != P:
+                raise ValueError(f"index must be [P={P}, index_stride], got {tuple(index.shape)}")
+            stride = index.shape[1]
+            xp = self._check(index, P * stride * 4, "index", torch.int32)
+            st = a2av_run_indexed(self.h, ip, tp, sp, scp, rcp, xp, P, core_num, dtype, row_elems,
+                                  stride, stream.cuda_stream)
+        elif bias is not None:
             be = {BF16: (torch.float32, 4), FP16: (torch.float16, 2)}.get(dtype)
             if be is None:  # the library reports the unsupported dtype
                 bp = self._check(bias, bias.numel() * bias.element_size(), "bias")

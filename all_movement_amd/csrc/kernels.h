@@ -39,7 +39,12 @@ struct CountParams {
   int32_t B;
   int32_t elem;
   int32_t nblk;       // sub-blocks per segment (1 = plain exchange)
-  int64_t unit;       // every count must be a multiple of this (nblk, or nblk * hidden)
+  int64_t unit;       // every count must be a multiple of this (nblk, nblk * hidden, or a row)
+  // Indexed exchange only (index != nullptr): the gather lists, their
+  // stride, and the whole rows each input table holds.
+  const int32_t* index;
+  int64_t index_stride;
+  int64_t table_rows;
 };
 
 struct CopyParams {
@@ -55,9 +60,14 @@ struct CopyParams {
   int32_t B;
   int32_t G;          // workgroups per admitted block
   int32_t nblk;       // sub-blocks per segment (1 = plain exchange)
-  int32_t mode;       // 0: move bytes; 1: BF16 + FP32 bias; 2: FP16 + FP16 bias
+  int32_t mode;       // 0: move bytes; 1: BF16 + FP32 bias; 2: FP16 + FP16 bias; 3: row gather
   int32_t hidden;     // elements per row (bias modes)
   const void* bias;   // [P, nblk, hidden] (bias modes)
+  const int32_t* index;   // gather lists [P, index_stride] (mode 3)
+  int64_t index_stride;
+  int64_t in_slab;
+  int64_t row_bytes;      // bytes per gathered row (mode 3)
+  int32_t gather_words;   // mode 3: 1 when every row and operand is 16-byte aligned
   int32_t last;       // 1 on the run's final launch: raise the block flags
   int32_t wait;       // 1 when the final launch is cooperative (B > 1): wait for all blocks
   int32_t spin_limit;

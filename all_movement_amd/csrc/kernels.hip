@@ -110,16 +110,36 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   }
   __syncthreads();
   if (tid < P) {
-    if (rowsum[tid] * p.elem > p.in_slab || colsum[tid] * p.elem > p.tgt_slab)
-      atomicOr(&flags, 2);
+    // A source overflows its input slab, or, in the indexed exchange, sends
+    // more rows than its gather list holds.
+    const bool src_over = p.index != nullptr ? rowsum[tid] / p.unit > p.index_stride
+                                             : rowsum[tid] * p.elem > p.in_slab;
+    if (src_over || colsum[tid] * p.elem > p.tgt_slab) atomicOr(&flags, 2);
   }
   __syncthreads();
+
+  // Indexed exchange, counts valid: every gather-list entry in use must name
+  // a whole row of its table (bit 4 of the flags word: 16).
+  if (p.index != nullptr && flags == 0) {
+    int bad_row = 0;
+    for (int s = 0; s < P; ++s) {
+      const int64_t rows = rowsum[s] / p.unit;
+      const int32_t* list = p.index + int64_t(s) * p.index_stride;
+#pragma unroll 4
+      for (int64_t k = tid; k < rows; k += kCountThreads) {
+        const int32_t v = list[k];
+        bad_row |= (v < 0 || int64_t(v) >= p.table_rows) ? 16 : 0;
+      }
+    }
+    if (bad_row) atomicOr(&flags, bad_row);
+    __syncthreads();
+  }
 
   const int f = flags;
   if (f != 0) {
     if (tid == 0) {
-      // Order: negative count, count not whole sub-blocks, over-capacity,
-      // unequal signal.
+      // Order: negative count, count not whole sub-blocks or rows,
+      // over-capacity, gather index outside its table, unequal signal.
       const int code = (f & 1) ? A2AV_ERR_INVALID_ARGS
                      : (f & 8) ? A2AV_ERR_INVALID_ARGS
                      : (f & 2) ? A2AV_ERR_OVER_CAPACITY
@@ -472,6 +492,61 @@ __device__ void wg_bias_piece(const uint8_t* src, uint8_t* dst, int64_t n, const
   }
 }
 
+// ------------------------------------------------ K2, indexed (row gather) path
+//
+// The indexed exchange reads row j of segment s -> d from table row
+// list[j] of source s.  With rows and operands 16-byte aligned every piece
+// is whole words on both sides; thread t handles words t, t + NT, ... of the
+// piece, keeping its (row, byte-in-row) position and advancing it by NT
+// words per step.  Each word reads its row's list entry (the lanes of a wave
+// share one or two entries, so the list loads are broadcasts from cache) and
+// then the payload word.
+constexpr int kGatherUnroll = 8;
+
+__device__ void wg_gather_words(const uint8_t* table, uint8_t* dseg, int64_t off0, int64_t n,
+                                const int32_t* list, int64_t RB, int tid) {
+  constexpr int NT = kCopyThreads;
+  table = wave_uniform(table);
+  dseg = wave_uniform(dseg);
+  list = wave_uniform(list);
+  off0 = wave_uniform(off0);
+  n = wave_uniform(n);
+  RB = wave_uniform(RB);
+  const int64_t K = n >> 4;
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(dseg + off0, n);
+  const int64_t step_r = (int64_t(NT) * 16) / RB;
+  const int64_t step_w = int64_t(NT) * 16 - step_r * RB;
+  const int64_t off = off0 + 16 * int64_t(tid);
+  int64_t r = off / RB;
+  int64_t w = off - r * RB;
+  for (int64_t k0 = 0; k0 < K; k0 += int64_t(NT) * kGatherUnroll) {
+    int64_t src[kGatherUnroll];
+#pragma unroll
+    for (int j = 0; j < kGatherUnroll; ++j) {
+      const int64_t k = k0 + int64_t(j) * NT + tid;
+      src[j] = k < K ? int64_t(list[r]) * RB + w : 0;
+      w += step_w;
+      r += step_r;
+      if (w >= RB) {
+        w -= RB;
+        ++r;
+      }
+    }
+    u32x4 v[kGatherUnroll];
+#pragma unroll
+    for (int j = 0; j < kGatherUnroll; ++j) {
+      const int64_t k = k0 + int64_t(j) * NT + tid;
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (k < K) v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(table + src[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < kGatherUnroll; ++j) {
+      const int64_t k = k0 + int64_t(j) * NT + tid;
+      if (k < K) store16(rd, k, v[j]);
+    }
+  }
+}
+
 // Segment tables of one run, staged in LDS by every workgroup.
 struct SegTables {
   int64_t prefix[kMaxP * kMaxP + 1];
@@ -523,7 +598,31 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
     const int64_t seg_hi = tab.prefix[i + 1];
     if (seg_hi > x) {
       const int64_t pe = b < seg_hi ? b : seg_hi;
-      if constexpr (MODE != 0) {
+      if constexpr (MODE == 3) {
+        // Row gather: the segment's rows start at row (src - s * in_slab) / RB
+        // of source s's gather list.
+        const int s = i / p.P;
+        const int64_t RB = p.row_bytes;
+        const int64_t row0 = (tab.src[i] - int64_t(s) * p.in_slab) / RB;
+        const int32_t* list = p.index + int64_t(s) * p.index_stride + row0;
+        const uint8_t* table = p.input + int64_t(s) * p.in_slab;
+        uint8_t* dseg = p.target + tab.dst[i];
+        if (p.gather_words) {
+          wg_gather_words(table, dseg, x - seg_lo, pe - x, list, RB, tid);
+        } else {
+          // Any alignment: one piece per row (or part of a row), copied by
+          // the byte-exact path.
+          for (int64_t off = x - seg_lo; off < pe - seg_lo;) {
+            const int64_t r = off / RB;
+            const int64_t w = off - r * RB;
+            const int64_t end = (r + 1) * RB < pe - seg_lo ? (r + 1) * RB : pe - seg_lo;
+            const int64_t row = __builtin_amdgcn_readfirstlane(list[r]);
+            wg_copy_piece(wave_uniform(table + row * RB + w), wave_uniform(dseg + off),
+                          wave_uniform(end - off), tid, lane, wave, slot);
+            off = end;
+          }
+        }
+      } else if constexpr (MODE != 0) {
         // Fused bias Add: pieces end at sub-block ends; sub-block a of source
         // s takes bias row (s, a).
         const int64_t sub = (seg_hi - seg_lo) / p.nblk;
@@ -677,6 +776,7 @@ const void* copy_kernel_for(int mode) {
   switch (mode) {
     case 1: return reinterpret_cast<const void*>(&copy_kernel<kCopyThreads, 1>);
     case 2: return reinterpret_cast<const void*>(&copy_kernel<kCopyThreads, 2>);
+    case 3: return reinterpret_cast<const void*>(&copy_kernel<kCopyThreads, 3>);
     default: return reinterpret_cast<const void*>(&copy_kernel<kCopyThreads, 0>);
   }
 }
@@ -692,10 +792,10 @@ hipError_t launch_copy(const CopyParams& p, int workgroups, bool cooperative, hi
 }
 
 hipError_t copy_occupancy(int* wgs_per_cu) {
-  // The largest of the three instantiations decides (they share the LDS
+  // The largest of the instantiations decides (they share the LDS
   // footprint; register counts differ).
   int best = 1 << 30;
-  for (int mode = 0; mode < 3; ++mode) {
+  for (int mode = 0; mode < 4; ++mode) {
     int n = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, copy_kernel_for(mode),
                                                                       kCopyThreads, 0);

@@ -111,6 +111,39 @@ int check_bias_args(const a2av_config* cfg, int64_t capacity, int64_t chunk_limi
   return A2AV_OK;
 }
 
+int check_indexed_args(const a2av_config* cfg, int64_t capacity, const void* input,
+                       const void* target, const int32_t* signal, const int32_t* send_counts,
+                       const int32_t* recv_counts, const int32_t* index, int32_t P,
+                       int64_t core_num, int32_t dtype, int32_t row_elems, int64_t index_stride) {
+  if (!cfg || !input || !target || !signal || !send_counts || !recv_counts || !index)
+    return A2AV_ERR_NULLPTR;
+  if (dtype != A2AV_FP32 && dtype != A2AV_INT8) return A2AV_ERR_UNSUPPORTED_DTYPE;
+  if (check_config(cfg) != A2AV_OK) return A2AV_ERR_INVALID_ARGS;
+  if (P != cfg->P || row_elems < 1 || index_stride < 1) return A2AV_ERR_INVALID_ARGS;
+  // Keep P * index_stride entries far from 64-bit overflow.
+  if (index_stride > (int64_t(1) << 40)) return A2AV_ERR_INVALID_ARGS;
+  if (core_num < 1 || core_num > kInt32Max) return A2AV_ERR_INVALID_ARGS;
+  const int64_t B = fold_blocks(P, core_num);
+  if (int64_t(cfg->S) < B) return A2AV_ERR_INVALID_ARGS;
+  if (B > 1 && capacity > 0 && B > capacity) return A2AV_ERR_LAUNCH_CAPACITY;
+
+  const uint64_t p = uint64_t(P);
+  const Range r[6] = {
+      {uintptr_t(input), p * uint64_t(cfg->in_slab_bytes)},
+      {uintptr_t(target), p * uint64_t(cfg->tgt_slab_bytes)},
+      {uintptr_t(signal), p * uint64_t(cfg->S) * 4u},
+      {uintptr_t(send_counts), p * p * 4u},
+      {uintptr_t(recv_counts), p * p * 4u},
+      {uintptr_t(index), p * uint64_t(index_stride) * 4u},
+  };
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(r[i], r[j])) return A2AV_ERR_INVALID_ARGS;
+  const int64_t e = elem_bytes(dtype);
+  if (cfg->in_slab_bytes % e != 0 || cfg->tgt_slab_bytes % e != 0) return A2AV_ERR_INVALID_ARGS;
+  return A2AV_OK;
+}
+
 int64_t max_payload(const a2av_config* cfg) {
   return int64_t(cfg->P) * std::min(cfg->in_slab_bytes, cfg->tgt_slab_bytes);
 }

@@ -40,6 +40,12 @@ int check_bias_args(const a2av_config* cfg, int64_t capacity, int64_t chunk_limi
                     const int32_t* send_counts, const int32_t* recv_counts, const void* bias,
                     int32_t P, int64_t core_num, int32_t dtype, int32_t nblk, int32_t hidden);
 
+// The host-side checks of a2av_run_indexed, in the documented order.
+int check_indexed_args(const a2av_config* cfg, int64_t capacity, const void* input,
+                       const void* target, const int32_t* signal, const int32_t* send_counts,
+                       const int32_t* recv_counts, const int32_t* index, int32_t P,
+                       int64_t core_num, int32_t dtype, int32_t row_elems, int64_t index_stride);
+
 // Upper bound of the payload of any valid run: every row fits its input slab
 // and every column its target slab, so T <= P * min(in_slab, tgt_slab).
 int64_t max_payload(const a2av_config* cfg);

@@ -201,13 +201,25 @@ int a2av_launch_info_get(a2av_handle* h, int64_t core_num, a2av_launch_info* out
 
 namespace {
 
+// What a run adds to the plain exchange (all defaults: the plain exchange).
+struct RunExtras {
+  int32_t nblk = 1;                // sub-blocks per segment
+  const void* bias = nullptr;      // fused bias Add (modes 1, 2)
+  int32_t hidden = 0;
+  const int32_t* index = nullptr;  // row gather (mode 3)
+  int64_t index_stride = 0;
+  int32_t row_elems = 0;
+  int32_t mode = 0;
+};
+
 // Enqueue one run whose arguments passed the host checks: K1, then the K2
 // launches.  mode selects the body of K2 (0: move bytes; 1 and 2: the fused
-// bias Add for BF16 and FP16 payloads).
+// bias Add for BF16 and FP16 payloads; 3: the row gather).
 int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal,
                 const int32_t* send_counts, int32_t* recv_counts, int32_t P, int64_t core_num,
-                int32_t dtype, int32_t nblk, const void* bias, int32_t hidden, int32_t mode,
-                void* stream) {
+                int32_t dtype, const RunExtras& x, void* stream) {
+  const int32_t nblk = x.nblk;
+  const int32_t mode = x.mode;
   a2av_launch_info li;
   int st = a2av_launch_info_get(h, core_num, &li);
   if (st != A2AV_OK) return st;
@@ -229,7 +241,15 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   cp.B = int32_t(li.blocks);
   cp.elem = int32_t(a2av::elem_bytes(dtype));
   cp.nblk = nblk;
-  cp.unit = int64_t(nblk) * (mode != 0 ? hidden : 1);
+  const int64_t elem = a2av::elem_bytes(dtype);
+  if (mode == 3) {
+    cp.unit = x.row_elems;
+    cp.index = x.index;
+    cp.index_stride = x.index_stride;
+    cp.table_rows = h->cfg.in_slab_bytes / (int64_t(x.row_elems) * elem);
+  } else {
+    cp.unit = int64_t(nblk) * (mode != 0 ? x.hidden : 1);
+  }
 
   hipEvent_t* ev = nullptr;
   if (h->profile)
@@ -250,8 +270,17 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   kp.G = li.wg_per_block;
   kp.nblk = nblk;
   kp.mode = mode;
-  kp.hidden = hidden;
-  kp.bias = bias;
+  kp.hidden = x.hidden;
+  kp.bias = x.bias;
+  kp.index = x.index;
+  kp.index_stride = x.index_stride;
+  kp.in_slab = h->cfg.in_slab_bytes;
+  kp.row_bytes = int64_t(x.row_elems) * elem;
+  // The word gather needs every row start and every piece bound 16-byte
+  // aligned on both sides.
+  kp.gather_words = mode == 3 && kp.row_bytes % 16 == 0 && (uintptr_t(input) & 15u) == 0 &&
+                    (uintptr_t(target) & 15u) == 0 && h->cfg.in_slab_bytes % 16 == 0 &&
+                    h->cfg.tgt_slab_bytes % 16 == 0 && h->chunk_limit % 16 == 0;
   kp.spin_limit = h->spin_limit;
   // Chunks are issued from the highest to chunk 0.  Chunks past the run's
   // payload cost only a plain launch that exits at once, and the final launch
@@ -287,8 +316,10 @@ int a2av_run_blocked(a2av_handle* h, const void* input, void* target, int32_t* s
   const int st = a2av::check_run_args(&h->cfg, h->capacity, input, target, signal, send_counts,
                                       recv_counts, P, core_num, dtype, nblk);
   if (st != A2AV_OK) return st;
-  return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, nblk,
-                     nullptr, 0, 0, stream);
+  RunExtras x;
+  x.nblk = nblk;
+  return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, x,
+                     stream);
 }
 
 int a2av_run_bias(a2av_handle* h, const void* input, void* target, int32_t* signal,
@@ -299,8 +330,31 @@ int a2av_run_bias(a2av_handle* h, const void* input, void* target, int32_t* sign
                                        signal, send_counts, recv_counts, bias, P, core_num, dtype,
                                        nblk, hidden);
   if (st != A2AV_OK) return st;
-  return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, nblk,
-                     bias, hidden, dtype == A2AV_BF16 ? 1 : 2, stream);
+  RunExtras x;
+  x.nblk = nblk;
+  x.bias = bias;
+  x.hidden = hidden;
+  x.mode = dtype == A2AV_BF16 ? 1 : 2;
+  return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, x,
+                     stream);
+}
+
+int a2av_run_indexed(a2av_handle* h, const void* input, void* target, int32_t* signal,
+                     const int32_t* send_counts, int32_t* recv_counts, const int32_t* index,
+                     int32_t P, int64_t core_num, int32_t dtype, int32_t row_elems,
+                     int64_t index_stride, void* stream) {
+  if (!h) return A2AV_ERR_NULLPTR;
+  const int st = a2av::check_indexed_args(&h->cfg, h->capacity, input, target, signal,
+                                          send_counts, recv_counts, index, P, core_num, dtype,
+                                          row_elems, index_stride);
+  if (st != A2AV_OK) return st;
+  RunExtras x;
+  x.index = index;
+  x.index_stride = index_stride;
+  x.row_elems = row_elems;
+  x.mode = 3;
+  return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, x,
+                     stream);
 }
 
 int a2av_run(a2av_handle* h, const void* input, void* target, int32_t* signal,

@@ -28,9 +28,10 @@ PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
 # name -> (workload index, sub-blocks per segment).  c5u is c5's exchange taken
 # on the source's own temp3 layout (E/ep, ep*C, H/tp): the blocked exchange
 # with nblk = E/ep = 8.  c5b is that exchange in BF16 with the bias Add fused
-# in front (k = 0 marks the bias workload).
+# in front (k = 0 marks the bias workload).  c3i is c3's MoE dispatch as the
+# indexed exchange: token tables stored once, the routing as gather lists.
 WORKLOADS = {"c1": (1, 1), "c2": (2, 1), "c3": (3, 1), "c4": (4, 1), "c5": (5, 1),
-             "c5u": (5, 8), "c5b": (0, 8)}
+             "c5u": (5, 8), "c5b": (0, 8), "c3i": (-3, 1)}
 DTYPE_NAMES = {0: "fp32", 1: "u8", 2: "fp16", 3: "bf16"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "copy_kernel_traffic.json")
 
@@ -60,13 +61,21 @@ def measured_traffic(workload: str):
 
 
 def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
+    import numpy as np
     import torch
     from all_movement_amd import a2av
     from all_movement_amd import workloads as wl
 
     dev = torch.device("cuda:0")
     bias, hidden, bias_bytes = None, 0, 0
-    if k == 0:
+    index, row_elems, index_bytes = None, 0, 0
+    if k == -3:
+        w = wl.indexed_workload()
+        row_elems = w.extra["row_elems"]
+        index = torch.from_numpy(w.extra["index"]).to(dev)
+        # The gather-list entries in use are read once per run.
+        index_bytes = 4 * int(w.counts.astype(np.int64).sum()) // row_elems
+    elif k == 0:
         w = wl.bias_workload(wl.BF16)
         hidden = w.extra["hidden"]
         bias = wl.bias_tensor(w, nblk, hidden, dev)
@@ -88,7 +97,7 @@ def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
 
     for _ in range(warmup):
         ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, nblk=nblk, bias=bias,
-               hidden=hidden)
+               hidden=hidden, index=index, row_elems=row_elems)
     torch.cuda.synchronize()
     if ex.query_error() != a2av.OK:
         raise RuntimeError("warmup run reported a device-side error")
@@ -97,7 +106,7 @@ def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
     t0 = time.perf_counter()
     for _ in range(steps):
         ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, nblk=nblk, bias=bias,
-               hidden=hidden)
+               hidden=hidden, index=index, row_elems=row_elems)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if ex.query_error() != a2av.OK:
@@ -105,8 +114,9 @@ def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
     k1_us, k2_us, k2_launches, runs = ex.profile()
     ex.close()
     sec = t1 - t0
-    # Each payload byte read once and written once (plus the bias, read once).
-    moved = 2 * w.payload_bytes + bias_bytes
+    # Each payload byte read once and written once (plus the bias or the
+    # gather lists, read once).
+    moved = 2 * w.payload_bytes + bias_bytes + index_bytes
     res = {
         "w": w, "info": info, "sec": sec, "steps": steps, "moved": moved,
         "gbps": moved * steps / sec / 1e9, "ms_per_step": sec / steps * 1e3,
@@ -145,9 +155,13 @@ def cpu_baseline(k: int, min_seconds: float = 10.0):
 
     # Sample: the same workload shape at a reduced size (c5 at 1/8: P=8 equal
     # counts of 2^22 fp32, 1 GiB of payload; c3/c4 at 1/4), run whole.
-    # c5b (the bias workload) at 1/16.
-    scale = {0: 16, 1: 1, 2: 1, 3: 4, 4: 4, 5: 8}[k]
-    if k == 0:
+    # c5b (the bias workload) at 1/16, c3i (indexed) at 1/4.
+    scale = {-3: 4, 0: 16, 1: 1, 2: 1, 3: 4, 4: 4, 5: 8}[k]
+    if k == -3:
+        w = wl.indexed_workload(scale=scale)
+        inp = wl.input_bytes_np(w)
+        what = "checks + transpose + displacements + one memcpy per gathered row + signal"
+    elif k == 0:
         w = wl.bias_workload(wl.BF16, scale=scale)
         A, H = w.extra["nblk"], w.extra["hidden"]
         inp = wl.input16_np(w)
@@ -166,7 +180,11 @@ def cpu_baseline(k: int, min_seconds: float = 10.0):
         kw = dict(P=w.P, S=w.S, in_slab=w.in_slab, tgt_slab=w.tgt_slab, core_num=w.core_num,
                   dtype=w.dtype)
         t0 = time.perf_counter()
-        if k == 0:
+        if k == -3:
+            st = oracle.run_indexed(inp, tgt, sig, w.counts, rc, w.extra["index"],
+                                    row_elems=w.extra["row_elems"],
+                                    index_stride=w.extra["index_stride"], **kw)
+        elif k == 0:
             st = oracle.run_bias(inp, tgt, sig, w.counts, rc, bias, nblk=A, hidden=H, **kw)
         else:
             st = oracle.run(inp, tgt, sig, w.counts, rc, **kw)
@@ -201,7 +219,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="c3,c4,c5u,c5b", help="other workloads reported beside it")
+    ap.add_argument("--also", default="c3,c4,c5u,c5b,c3i",
+                    help="other workloads reported beside it")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain torch device copy of MIB MiB --steps times (the "

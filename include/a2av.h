@@ -182,6 +182,36 @@ int a2av_run_bias(a2av_handle *h, const void *input, void *target, int32_t *sign
                   const int32_t *send_counts, int32_t *recv_counts, const void *bias, int32_t P,
                   int64_t core_num, int32_t dtype, int32_t nblk, int32_t hidden, void *stream);
 
+/*
+ * indexed_all_to_all_v: the six-operand variant named in the "A5 URMA indexed
+ * exchange" section of the LowerL2TensorCollectives page (index the sixth
+ * operand, local to the sender).  The page does not say what index means;
+ * this library reads it as the sender's row gather list.
+ *   input   P token tables at stride in_slab bytes; table s holds
+ *           in_slab / (row_elems * e) whole rows of row_elems elements
+ *   index   device, int32 [P, index_stride], read only: the rows source s
+ *           sends, for d = 0..P-1 in turn, are table rows index[s][0],
+ *           index[s][1], ...; a row may be named any number of times;
+ *           entries past the rows a source sends are never read
+ *   send_counts / recv_counts / target / signal as in a2av_run (counts in
+ *           elements, whole rows)
+ * Segment s -> d lands where a2av_run puts it: the exchange of the packed
+ * rows, without packing them.
+ * Host checks, first failure wins: NULLPTR (any of the six operands) ->
+ * UNSUPPORTED_DTYPE (not FP32/INT8) -> INVALID_ARGS (P, row_elems < 1,
+ * index_stride < 1, core_num, S < B) -> LAUNCH_CAPACITY -> INVALID_ARGS (two
+ * of the six operands share a byte; a slab not a whole number of elements).
+ * Device checks (a2av_query_error), nothing written on failure: a negative
+ * count -> INVALID_ARGS; a count that is not whole rows -> INVALID_ARGS; a
+ * source sending more rows than index_stride or a column over tgt_slab ->
+ * OVER_CAPACITY; an index entry in use outside the table -> INVALID_ARGS;
+ * unequal signal -> INVALID_ARGS.
+ */
+int a2av_run_indexed(a2av_handle *h, const void *input, void *target, int32_t *signal,
+                     const int32_t *send_counts, int32_t *recv_counts, const int32_t *index,
+                     int32_t P, int64_t core_num, int32_t dtype, int32_t row_elems,
+                     int64_t index_stride, void *stream);
+
 /* Free the workspace and the handle (synchronizes the device first).
  * NULL is accepted and ignored. */
 int a2av_destroy(a2av_handle *h);

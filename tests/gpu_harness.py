@@ -52,18 +52,19 @@ class Case:
         self.recv = torch.full((P, P), -7, dtype=torch.int32, device=DEV)
 
     def run_gpu(self, ex: a2av.Exchange, core_num: int | None = None, sync: bool = True,
-                nblk: int = 1, bias=None, hidden: int = 0) -> int:
+                nblk: int = 1, bias=None, hidden: int = 0, index=None, row_elems: int = 0) -> int:
         w = self.w
         ex.run(self.input, self.target, self.signal, self.send, self.recv,
                w.core_num if core_num is None else core_num, w.dtype, nblk=nblk, bias=bias,
-               hidden=hidden)
+               hidden=hidden, index=index, row_elems=row_elems)
         if sync:
             torch.cuda.synchronize()
             return ex.query_error()
         return a2av.OK
 
     def run_oracle(self, core_num: int | None = None, capacity: int = 0, nblk: int = 1,
-                   bias: np.ndarray | None = None, hidden: int = 0):
+                   bias: np.ndarray | None = None, hidden: int = 0,
+                   index: np.ndarray | None = None, row_elems: int = 0):
         w = self.w
         inp = self.input_np if self.input_np is not None else self.input.cpu().numpy()
         tgt = np.full(w.tgt_bytes, wl.SENTINEL, np.uint8)
@@ -73,7 +74,10 @@ class Case:
                   core_num=w.core_num if core_num is None else core_num, dtype=w.dtype,
                   capacity=capacity)
         C = np.ascontiguousarray(w.counts, np.int32)
-        if bias is not None:
+        if index is not None:
+            st = oracle.run_indexed(inp, tgt, sig, C, rc, np.ascontiguousarray(index, np.int32),
+                                    row_elems=row_elems, index_stride=index.shape[1], **kw)
+        elif bias is not None:
             st = oracle.run_bias(inp, tgt, sig, C, rc, np.ascontiguousarray(bias), nblk=nblk,
                                  hidden=hidden, **kw)
         elif nblk == 1:

@@ -1,0 +1,174 @@
+"""GPU parity of the indexed exchange (a2av_run_indexed): source s sends, in
+destination order, the rows of its input table named by its gather list
+index[s] -- the reading of indexed_all_to_all_v's sixth operand.  Bit-exact
+against the oracle's run_indexed."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from all_movement_amd import a2av  # noqa: E402
+from all_movement_amd import workloads as wl  # noqa: E402
+from tests.gpu_harness import DEV, Case, exchange_for, say, upload  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _gpu_or_skip():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def indexed_case(P, R, dtype, max_rows, table_rows, core_num=1, seed=1, zero_frac=0.15,
+                 in_pad=0, tgt_pad=0):
+    """Counts of whole rows, a random gather list (repeats, any order) and a
+    table of table_rows rows (plus in_pad bytes of partial row)."""
+    rng = np.random.default_rng(seed)
+    e = wl.ELEM_SIZE[dtype]
+    C = (rng.integers(0, max_rows + 1, size=(P, P)) * R).astype(np.int32)
+    C[rng.random((P, P)) < zero_frac] = 0
+    rows = C.astype(np.int64).sum(axis=1) // R
+    stride = int(rows.max(initial=0)) + 5
+    index = rng.integers(0, table_rows, size=(P, stride)).astype(np.int32)
+    index[:, -1] = -1                           # never read: past every source's rows
+    w = wl.custom(P, dtype, C, core_num=core_num, seed=seed + 17,
+                  in_slab=table_rows * R * e + in_pad)
+    w.tgt_slab += tgt_pad
+    return w, index
+
+
+def check_indexed(w, index, R, runs=1, core_num=None, **kw):
+    c = Case(w)
+    ix = upload(index)
+    ex = exchange_for(w, **kw)
+    try:
+        for _ in range(runs):
+            st = c.run_gpu(ex, core_num, index=ix, row_elems=R)
+        exp = None
+        for _ in range(runs):
+            exp = c.run_oracle(core_num, index=index, row_elems=R)
+            c.signal_np0 = exp[2].copy()
+        c.assert_matches(st, exp)
+    finally:
+        ex.close()
+    return c
+
+
+# Row lengths: int8 rows of 1 and 3 bytes and fp32 rows of 3 elements take the
+# byte-exact path (rows not whole 16-byte words); 16 and 7168 int8 and 4 and
+# 1792 fp32 (7168 bytes) take the word gather.
+@pytest.mark.parametrize("R,dtype", [(1, wl.INT8), (3, wl.INT8), (16, wl.INT8), (7168, wl.INT8),
+                                     (3, wl.FP32), (4, wl.FP32), (1792, wl.FP32)])
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 32])
+def test_indexed_sweep(P, R, dtype):
+    rb = R * wl.ELEM_SIZE[dtype]
+    budget = {1: 400_000, 2: 400_000, 3: 300_000, 8: 120_000, 32: 12_000}[P]
+    max_rows = max(1, budget // (rb * P))
+    for L in sorted({1, 2 * P + 1, 256}):
+        say("P", P, "R", R, "dtype", dtype, "L", L)
+        w, index = indexed_case(P, R, dtype, max_rows, table_rows=max(2, max_rows), core_num=L,
+                                seed=P * 100 + R + L, in_pad=16, tgt_pad=16 * wl.ELEM_SIZE[dtype])
+        check_indexed(w, index, R)
+
+
+@pytest.mark.parametrize("limit", [4096, 1000])
+def test_indexed_small_chunks_and_two_runs(limit):
+    # 1000 is not a multiple of 16: the byte-exact path even for aligned rows.
+    w, index = indexed_case(4, 64, wl.INT8, 40, 30, core_num=8, seed=limit)
+    check_indexed(w, index, 64, runs=2, chunk_limit_bytes=limit)
+
+
+def test_indexed_unaligned_operands_and_partial_last_row():
+    w, index = indexed_case(4, 64, wl.INT8, 20, 25, core_num=4, seed=3, in_pad=37)
+    c = Case(w, in_offset=3, tgt_offset=5)
+    ex = exchange_for(w)
+    try:
+        st = c.run_gpu(ex, index=upload(index), row_elems=64)
+        c.assert_matches(st, c.run_oracle(index=index, row_elems=64))
+    finally:
+        ex.close()
+
+
+def test_indexed_host_rejections():
+    P, R = 4, 16
+    w, index = indexed_case(P, R, wl.INT8, 10, 12, core_num=4, seed=5)
+    c = Case(w)
+    ix = upload(index)
+    ex = exchange_for(w)
+    try:
+        args = lambda **o: dict(dict(idx=ix.data_ptr(), P=P, dtype=wl.INT8, R=R,  # noqa: E731
+                                     stride=index.shape[1]), **o)
+
+        def raw(idx, P, dtype, R, stride):
+            return a2av.a2av_run_indexed(ex.h, c.input.data_ptr(), c.target.data_ptr(),
+                                         c.signal.data_ptr(), c.send.data_ptr(),
+                                         c.recv.data_ptr(), idx, P, 4, dtype, R, stride, None)
+        assert raw(**args(idx=None)) == a2av.ERR_NULLPTR
+        assert raw(**args(dtype=wl.BF16)) == a2av.ERR_UNSUPPORTED_DTYPE
+        assert raw(**args(R=0)) == a2av.ERR_INVALID_ARGS
+        assert raw(**args(stride=0)) == a2av.ERR_INVALID_ARGS
+        assert raw(**args(P=P + 1)) == a2av.ERR_INVALID_ARGS
+        assert raw(**args(idx=c.target.data_ptr())) == a2av.ERR_INVALID_ARGS   # overlaps target
+        with pytest.raises(ValueError, match="index must be"):
+            c.run_gpu(ex, index=ix.view(-1), row_elems=R)
+        torch.cuda.synchronize()
+        assert (c.target.cpu().numpy() == wl.SENTINEL).all()
+        assert (c.signal.cpu().numpy() == 0).all()
+    finally:
+        ex.close()
+
+
+@pytest.mark.parametrize("what", ["partial_row", "negative", "too_many_rows", "column_over",
+                                  "index_low", "index_high", "over_before_index"])
+def test_indexed_device_rejections_match_oracle(what):
+    P, R = 4, 8
+    w, index = indexed_case(P, R, wl.INT8, 12, 10, core_num=4, seed=21, zero_frac=0.0,
+                            tgt_pad=64)
+    C = w.counts.copy()
+    rows = C.astype(np.int64).sum(axis=1) // R
+    index = index.copy()
+    if what == "partial_row":
+        C[1, 2] += 3
+    elif what == "negative":
+        C[2, 0] = -R
+    elif what == "too_many_rows":
+        C[0, 1] += R * (index.shape[1] - rows[0] + 1)
+        w.tgt_slab += int(C[0, 1]) * 2
+    elif what == "column_over":
+        w.tgt_slab = int(C.sum(axis=0).max()) - 16 - 64
+        w.tgt_slab -= w.tgt_slab % 16
+    elif what == "index_low":
+        index[3, rows[3] - 1] = -1
+    elif what == "index_high":
+        index[0, 0] = 10
+    elif what == "over_before_index":
+        index[0, 0] = -5
+        w.tgt_slab = int(C.sum(axis=0).max()) - 80
+    w.counts = C.astype(np.int32)
+    say(what)
+    c = check_indexed(w, index, R)
+    assert (c.target.cpu().numpy() == wl.SENTINEL).all()
+
+
+def test_indexed_moe_full_size():
+    # The MoE dispatch at full size: token tables of 4096 x 7168 int8 per
+    # source, c3's routing as the gather lists.  Whole target against the
+    # whole oracle, and the same bytes as the plain exchange of c3's packed
+    # input on the GPU.
+    wi = wl.indexed_workload()
+    R = wi.extra["row_elems"]
+    say(wi.name, wi.payload_bytes)
+    c = check_indexed(wi, wi.extra["index"], R)
+    w3 = wl.workload(3)
+    c3 = Case(w3, host_input=False)
+    ex = exchange_for(w3)
+    try:
+        assert c3.run_gpu(ex) == a2av.OK
+    finally:
+        ex.close()
+    assert torch.equal(c3.target, c.target)
