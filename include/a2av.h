@@ -54,7 +54,7 @@ enum a2av_status {
     A2AV_OK = 0,
     A2AV_ERR_NULLPTR = 1,           /* a required pointer is NULL               */
     A2AV_ERR_INVALID_ARGS = 2,      /* bad size, range, stride, alias or signal */
-    A2AV_ERR_UNSUPPORTED_DTYPE = 3, /* dtype not FP32 / INT8                    */
+    A2AV_ERR_UNSUPPORTED_DTYPE = 3, /* dtype not one the entry point takes      */
     A2AV_ERR_OVER_CAPACITY = 4,     /* a row or column of counts overflows its slab */
     A2AV_ERR_LAUNCH_CAPACITY = 5,   /* B > 1 blocks cannot all be co-resident   */
     A2AV_ERR_HIP = 6,               /* a HIP runtime call failed                */
