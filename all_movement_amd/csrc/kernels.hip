@@ -3,8 +3,9 @@
 // K1 (count_kernel, one 1024-thread workgroup): checks the count matrix and
 // the signal on the device, writes recv_counts as the transpose of
 // send_counts, and derives every segment's source and target byte offsets
-// with wave64 exclusive scans (send side along d, receive side along s, and
-// the flattened s-major payload prefix that K2 partitions).
+// (exclusive prefixes along d on the send side and along s on the receive
+// side, one thread per row or column walking the LDS copy of the matrix),
+// and the flattened s-major payload prefix that K2 partitions.
 //
 // K2 (copy_kernel, W = B * G workgroups): the flattened payload is cut into
 // 128 KiB tiles dealt round-robin to the workgroups.  Inside a segment the copy is
@@ -50,20 +51,14 @@ constexpr int kStorePolicy = 2 | 16;
 
 // ------------------------------------------------------------------ K1
 
-__device__ inline int64_t wave_inclusive_scan(int64_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int64_t y = __shfl_up(v, o, kWave);
-    if (lane >= o) v += y;
-  }
-  return v;
-}
-
 __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   __shared__ int32_t C[kMaxP * kMaxP];
-  __shared__ int64_t rowsum[kMaxP];
-  __shared__ int64_t colsum[kMaxP];
-  __shared__ int64_t rowbase[kMaxP + 1];
+  __shared__ int64_t soff[kMaxP * kMaxP];  // staged outputs, written back coalesced
+  __shared__ int64_t pre[kMaxP * kMaxP];
+  __shared__ int64_t doff[kMaxP * kMaxP];
+  __shared__ int64_t rowsum[kMaxP];        // elements each source sends
+  __shared__ int64_t colsum[kMaxP];        // elements each destination receives
+  __shared__ int64_t rowbase[kMaxP + 1];   // bytes before source s in the flattened order
   __shared__ int flags;
 
   const int tid = threadIdx.x;
@@ -77,15 +72,17 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   __syncthreads();
 
   // Load the counts; note negatives (bit 0), counts that are not whole
-  // sub-blocks (bit 3: nblk, or nblk rows of the bias path, does not divide) and a signal that is not uniform over the admitted entries (bit 2).
-  // The loops are unrolled so each thread issues its loads back to back.
+  // sub-blocks or rows (bit 3: p.unit does not divide them) and a signal that
+  // is not uniform over the admitted entries (bit 2).  The loops are unrolled
+  // so each thread issues its loads back to back.
+  const int64_t unit = p.unit;
   int bad = 0;
 #pragma unroll 4
   for (int i = tid; i < PP; i += kCountThreads) {
     const int32_t c = p.send_counts[i];
     C[i] = c;
     bad |= c < 0 ? 1 : 0;
-    bad |= int64_t(c) % p.unit != 0 ? 8 : 0;
+    bad |= (unit > kInt32Max ? c != 0 : c % int32_t(unit) != 0) ? 8 : 0;
   }
   const int32_t base = p.signal[0];
   for (int r = wave; r < P; r += kWaves) {
@@ -96,40 +93,51 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   if (bad) atomicOr(&flags, bad);
   __syncthreads();
 
-  // Row sums (what each source sends) and column sums (what each destination
-  // receives), one wave per row or column.
-  for (int s = wave; s < P; s += kWaves) {
-    const int64_t v = lane < P ? int64_t(C[s * P + lane]) : 0;
-    const int64_t t = wave_inclusive_scan(v, lane);
-    if (lane == kWave - 1) rowsum[s] = t;
-  }
-  for (int d = wave; d < P; d += kWaves) {
-    const int64_t v = lane < P ? int64_t(C[lane * P + d]) : 0;
-    const int64_t t = wave_inclusive_scan(v, lane);
-    if (lane == kWave - 1) colsum[d] = t;
+  // Row sums (what each source sends) in wave 0 and column sums (what each
+  // destination receives) in wave 1: one thread walks its row or column of
+  // the LDS matrix (at most 64 entries; cheaper than a cross-lane scan).
+  if (wave == 0 && lane < P) {
+    int64_t acc = 0;
+    for (int d = 0; d < P; ++d) acc += C[lane * P + d];
+    rowsum[lane] = acc;
+  } else if (wave == 1 && lane < P) {
+    int64_t acc = 0;
+    for (int s2 = 0; s2 < P; ++s2) acc += C[s2 * P + lane];
+    colsum[lane] = acc;
   }
   __syncthreads();
   if (tid < P) {
     // A source overflows its input slab, or, in the indexed exchange, sends
     // more rows than its gather list holds.
-    const bool src_over = p.index != nullptr ? rowsum[tid] / p.unit > p.index_stride
+    const bool src_over = p.index != nullptr ? rowsum[tid] / unit > p.index_stride
                                              : rowsum[tid] * p.elem > p.in_slab;
     if (src_over || colsum[tid] * p.elem > p.tgt_slab) atomicOr(&flags, 2);
+  } else if (tid == kWave) {
+    // Flattened payload order is s-major (segment i = s*P + d): row bases
+    // are the exclusive prefix of the row byte totals, rowbase[kMaxP] = T.
+    int64_t acc = 0;
+    for (int s2 = 0; s2 < P; ++s2) {
+      rowbase[s2] = acc;
+      acc += rowsum[s2] * p.elem;
+    }
+    rowbase[kMaxP] = acc;
   }
   __syncthreads();
 
   // Indexed exchange, counts valid: every gather-list entry in use must name
   // a whole row of its table (bit 4 of the flags word: 16).
   if (p.index != nullptr && flags == 0) {
+    // Unsigned compare: a negative entry is a huge value.  Entries are int32,
+    // so a table of 2^31 rows or more admits every non-negative entry.
+    const uint32_t limit = uint32_t(p.table_rows < (int64_t(1) << 31) ? p.table_rows
+                                                                      : (int64_t(1) << 31));
     int bad_row = 0;
-    for (int s = 0; s < P; ++s) {
-      const int64_t rows = rowsum[s] / p.unit;
-      const int32_t* list = p.index + int64_t(s) * p.index_stride;
+    for (int s2 = 0; s2 < P; ++s2) {
+      const int64_t rows = rowsum[s2] / unit;
+      const int32_t* list = p.index + int64_t(s2) * p.index_stride;
 #pragma unroll 4
-      for (int64_t k = tid; k < rows; k += kCountThreads) {
-        const int32_t v = list[k];
-        bad_row |= (v < 0 || int64_t(v) >= p.table_rows) ? 16 : 0;
-      }
+      for (int64_t k = tid; k < rows; k += kCountThreads)
+        bad_row |= uint32_t(list[k]) >= limit ? 16 : 0;
     }
     if (bad_row) atomicOr(&flags, bad_row);
     __syncthreads();
@@ -150,42 +158,41 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     return;
   }
 
-  // Flattened payload order is s-major: segment i = s*P + d.  Row bases are
-  // the exclusive scan of the row byte totals; lane 63 ends with T.
-  if (wave == 0) {
-    const int64_t v = lane < P ? rowsum[lane] * p.elem : 0;
-    const int64_t incl = wave_inclusive_scan(v, lane);
-    if (lane < P) rowbase[lane] = incl - v;
-    if (lane == kWave - 1) rowbase[kMaxP] = incl;
+  // Send side (wave 0, one thread per source): the exclusive prefix along d
+  // (input packed by destination) gives the flattened prefix; the source
+  // offset is the prefix of the sub-block sizes (the segment's sub-block in
+  // block-row 0; block-rows are sstride[s] bytes apart; nblk = 1 is the plain
+  // exchange).  Receive side (wave 1, one thread per destination): the
+  // exclusive prefix along s (target packed by source).
+  if (wave == 0 && lane < P) {
+    const int s2 = lane;
+    int64_t ex = 0;
+    int64_t sub_ex = 0;
+    for (int d = 0; d < P; ++d) {
+      const int32_t c = C[s2 * P + d];
+      soff[s2 * P + d] = int64_t(s2) * p.in_slab + sub_ex;
+      pre[s2 * P + d] = rowbase[s2] + ex;
+      ex += int64_t(c) * p.elem;
+      sub_ex += int64_t(c / p.nblk) * p.elem;
+    }
+    p.ws.sstride[s2] = sub_ex;
+  } else if (wave == 1 && lane < P) {
+    const int d = lane;
+    int64_t ex = int64_t(d) * p.tgt_slab;
+    for (int s2 = 0; s2 < P; ++s2) {
+      doff[s2 * P + d] = ex;
+      ex += int64_t(C[s2 * P + d]) * p.elem;
+    }
   }
   __syncthreads();
-
-  // Send side: exclusive scan along d of row s (input packed by destination).
-  // The blocked exchange scans the sub-block sizes instead: segment s -> d
-  // starts at its sub-block's offset inside block-row 0 of source s, and the
-  // following block-rows are sstride[s] bytes apart.
-  for (int s = wave; s < P; s += kWaves) {
-    const int64_t v = lane < P ? int64_t(C[s * P + lane]) * p.elem : 0;
-    const int64_t incl = wave_inclusive_scan(v, lane);
-    const int64_t sub = v / p.nblk;
-    const int64_t sub_ex = wave_inclusive_scan(sub, lane) - sub;
-    if (lane < P) {
-      p.ws.src_off[s * P + lane] = int64_t(s) * p.in_slab + sub_ex;
-      p.ws.prefix[s * P + lane] = rowbase[s] + (incl - v);
-    }
-    if (lane == kWave - 1) p.ws.sstride[s] = incl / p.nblk;
-  }
-  // Receive side: exclusive scan along s of column d (target packed by source).
-  for (int d = wave; d < P; d += kWaves) {
-    const int64_t v = lane < P ? int64_t(C[lane * P + d]) * p.elem : 0;
-    const int64_t ex = wave_inclusive_scan(v, lane) - v;
-    if (lane < P) p.ws.dst_off[lane * P + d] = int64_t(d) * p.tgt_slab + ex;
-  }
-  // recv_counts[d][s] = send_counts[s][d].
   for (int i = tid; i < PP; i += kCountThreads) {
+    p.ws.src_off[i] = soff[i];
+    p.ws.prefix[i] = pre[i];
+    p.ws.dst_off[i] = doff[i];
+    // recv_counts[d][s] = send_counts[s][d].
     const int d = i / P;
-    const int s = i - d * P;
-    p.recv_counts[i] = C[s * P + d];
+    const int s2 = i - d * P;
+    p.recv_counts[i] = C[s2 * P + d];
   }
   for (int b = tid; b < p.B; b += kCountThreads) p.ws.blk_cnt[b] = 0u;
   if (tid == 0) {
@@ -684,6 +691,9 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   const int64_t T = plan->total_bytes;
   const int64_t c_lo = p.chunk_lo < T ? p.chunk_lo : T;
   const int64_t c_hi = p.chunk_hi < T ? p.chunk_hi : T;
+  // A chunk past the run's payload has nothing to copy (the final launch
+  // still arrives, even with no payload).
+  if (c_lo >= c_hi && !p.last) return;
   const int nseg = p.nseg;
   for (int i = tid; i <= nseg; i += NT) tab.prefix[i] = p.ws.prefix[i];
   for (int i = tid; i < nseg; i += NT) {
