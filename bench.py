@@ -228,7 +228,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the exchange runs its P virtual ranks as slabs "
-              "of one GPU's memory; runs on more than one GPU are not part of this build.",
+              "of one GPU's memory, and there is no multi-GPU exchange to time.",
               file=sys.stderr)
         sys.exit(2)
 
