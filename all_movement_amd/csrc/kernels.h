@@ -15,6 +15,7 @@ struct alignas(64) RunPlan {
   int64_t total_bytes;  // payload bytes T of the run
   uint32_t arrived;     // admitted blocks that have raised their flags
   int32_t error;        // latched status (first failure since the last query)
+  uint32_t claim[2];    // dynamic tile counters; K2 launch c uses claim[c & 1]
 };
 
 // Device workspace layout, carved out of one allocation by the host.
@@ -68,6 +69,7 @@ struct CopyParams {
   int64_t in_slab;
   int64_t row_bytes;      // bytes per gathered row (mode 3)
   int32_t gather_words;   // mode 3: 1 when every row and operand is 16-byte aligned
+  int32_t chunk;      // chunk index of this launch (launches run from the highest to 0)
   int32_t last;       // 1 on the run's final launch: raise the block flags
   int32_t wait;       // 1 when the final launch is cooperative (B > 1): wait for all blocks
   int32_t spin_limit;

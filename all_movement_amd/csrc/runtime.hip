@@ -291,6 +291,7 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
     const bool last = (c == 0);
     kp.chunk_lo = int64_t(c) * h->chunk_limit;
     kp.chunk_hi = (c == h->launches - 1) ? INT64_MAX : int64_t(c + 1) * h->chunk_limit;
+    kp.chunk = c;
     kp.last = last ? 1 : 0;
     kp.wait = (last && li.blocks > 1) ? 1 : 0;
     e = a2av::launch_copy(kp, li.workgroups, kp.wait != 0, s);
