@@ -62,7 +62,8 @@ enum a2av_status {
 };
 
 /* a2av_config.flags */
-#define A2AV_FLAG_PROFILE 1u /* record HIP events around K1 and every K2 launch */
+#define A2AV_FLAG_PROFILE 1u /* time each run: HIP events before and after K1 and
+                                 after the last K2 launch */
 
 typedef struct a2av_config {
     int32_t device;            /* HIP device ordinal the handle binds to                 */
