@@ -673,12 +673,13 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
 }
 
 // One K2 launch copies the flattened payload bytes [c_lo, c_hi) of the run.
-// The range is cut into 128 KiB tiles dealt round-robin to the workgroups, so
-// at any moment the grid streams through one narrow window of the source and
-// of the destination (measured on gfx950: contiguous per-workgroup ranges that
-// fan out to destination slabs 1 GiB apart ran at ~4.1 TB/s, the same bytes as
-// interleaved tiles at ~5.6 TB/s).  Every wave derives the same tile bounds
-// and pieces from the LDS tables, so tiles need no workgroup barrier.
+// The range is cut into tiles of at most 128 KiB, handed out in tile order
+// (round-robin first, then by claim), so at any moment the grid streams
+// through one narrow window of the source and of the destination (measured
+// on gfx950: contiguous per-workgroup ranges that fan out to destination
+// slabs 1 GiB apart ran at ~4.1 TB/s, the same bytes as interleaved tiles at
+// ~5.6 TB/s).  Every wave derives the same tile bounds and pieces from the
+// LDS tables, so static tiles need no workgroup barrier.
 template <int NT, int MODE>
 __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   constexpr int NW = NT / kWave;
@@ -713,8 +714,8 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   if (tid < p.P) tab.sstride[tid] = p.ws.sstride[tid];
   __syncthreads();
 
-  // Tile size: at most kTileBytes, chosen so every workgroup gets the same
-  // number of tiles (no workgroup is left with one extra tile at the end).
+  // Tile size: at most kTileBytes, chosen so W workgroups take the same number
+  // of rounds (with the static deal, no workgroup is left with one extra tile).
   const int64_t len = c_hi - c_lo;
   const int64_t W = gridDim.x;
   const int64_t rounds = (len + W * kTileBytes - 1) / (W * kTileBytes);
