@@ -191,6 +191,35 @@ def test_error_then_valid_run_reports_first_error_once():
         ex.close()
 
 
+def test_tiny_spin_limit_latches_timeout_and_the_run_still_completes():
+    # The arrival wait is bounded by the handle's spin limit.  With a limit of
+    # 1 the first workgroups to arrive give up after two polls (they finish
+    # microseconds apart) and latch TIMEOUT; every workgroup still leaves the
+    # kernel, and the payload and the flags are complete, since a workgroup
+    # copies and arrives before it waits.  The next run reports cleanly.
+    P = 8
+    rng = np.random.default_rng(17)
+    C = rng.integers(1 << 18, 1 << 19, size=(P, P)).astype(np.int32)
+    w = wl.custom(P, wl.FP32, C, core_num=8, S=8)
+    c = Case(w)
+    ex = exchange_for(w, spin_limit=1, wg_per_block=32)
+    try:
+        assert ex.launch_info(w.core_num).workgroups == 256
+        assert c.run_gpu(ex) == a2av.ERR_TIMEOUT
+        exp = c.run_oracle()
+        c.assert_matches(a2av.OK, exp)
+        assert ex.query_error() == a2av.OK              # the latch was cleared by the read
+    finally:
+        ex.close()
+    ex2 = exchange_for(w)
+    try:
+        c.signal_np0 = exp[2].copy()
+        c.target.fill_(wl.SENTINEL)
+        c.assert_matches(c.run_gpu(ex2), c.run_oracle())
+    finally:
+        ex2.close()
+
+
 # ------------------------------------------------------------------ host-side errors
 
 def test_launch_capacity_refused_not_partial():
