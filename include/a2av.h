@@ -58,7 +58,8 @@ enum a2av_status {
     A2AV_ERR_OVER_CAPACITY = 4,     /* a row or column of counts overflows its slab */
     A2AV_ERR_LAUNCH_CAPACITY = 5,   /* B > 1 blocks cannot all be co-resident   */
     A2AV_ERR_HIP = 6,               /* a HIP runtime call failed                */
-    A2AV_ERR_TIMEOUT = 7            /* the block barrier's bounded wait expired */
+    A2AV_ERR_TIMEOUT = 7            /* the block barrier's bounded wait expired; the
+                                       run's copies and flags still complete */
 };
 
 /* a2av_config.flags */
