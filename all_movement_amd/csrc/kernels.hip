@@ -167,16 +167,27 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   // exclusive prefix along s (target packed by source).
   if (wave == 0 && lane < P) {
     const int s2 = lane;
+    const int64_t in0 = int64_t(s2) * p.in_slab;
+    const int64_t rb = rowbase[s2];
     int64_t ex = 0;
-    int64_t sub_ex = 0;
-    for (int d = 0; d < P; ++d) {
-      const int32_t c = C[s2 * P + d];
-      soff[s2 * P + d] = int64_t(s2) * p.in_slab + sub_ex;
-      pre[s2 * P + d] = rowbase[s2] + ex;
-      ex += int64_t(c) * p.elem;
-      sub_ex += int64_t(c / p.nblk) * p.elem;
+    if (p.nblk == 1) {
+      for (int d = 0; d < P; ++d) {
+        soff[s2 * P + d] = in0 + ex;
+        pre[s2 * P + d] = rb + ex;
+        ex += int64_t(C[s2 * P + d]) * p.elem;
+      }
+      p.ws.sstride[s2] = ex;
+    } else {
+      int64_t sub_ex = 0;
+      for (int d = 0; d < P; ++d) {
+        const int32_t c = C[s2 * P + d];
+        soff[s2 * P + d] = in0 + sub_ex;
+        pre[s2 * P + d] = rb + ex;
+        ex += int64_t(c) * p.elem;
+        sub_ex += int64_t(c / p.nblk) * p.elem;
+      }
+      p.ws.sstride[s2] = sub_ex;
     }
-    p.ws.sstride[s2] = sub_ex;
   } else if (wave == 1 && lane < P) {
     const int d = lane;
     int64_t ex = int64_t(d) * p.tgt_slab;
