@@ -87,3 +87,42 @@ def test_c5_full_size_block_transpose_and_samples():
             assert got[j] == want, (int(d_idx[j]), int(offs[j]))
     finally:
         ex.close()
+
+
+def test_largest_count_int8():
+    # The largest int32 count: 2^31 - 1 int8 elements in one segment, beside
+    # segments of 3 and 5 bytes, P = 2 with core_num 2 (B = 2, cooperative).
+    # The payload, 2^31 + 7 bytes, spans chunks of 1 GiB, 1 GiB and 7 bytes
+    # (segments cut at odd offsets), plus one launch past it.  Checked
+    # on the GPU against the source bytes and at sampled bytes located by the
+    # oracle from regenerated input.
+    P, big = 2, (1 << 31) - 1
+    C = np.array([[big, 0], [3, 5]], np.int32)
+    w = wl.custom(P, wl.INT8, C, core_num=2, S=2, in_slab=big + 1, tgt_slab=big + 9, seed=77)
+    say("largest count", w.payload_bytes)
+    c = Case(w, host_input=False)
+    ex = exchange_for(w)
+    try:
+        info = ex.launch_info(w.core_num)
+        assert info.chunk_launches == 4 and info.blocks == 2
+        assert c.run_gpu(ex) == a2av.OK
+        inp = c.input.view(P, w.in_slab)
+        tgt = c.target.view(P, w.tgt_slab)
+        assert torch.equal(tgt[0, :big], inp[0, :big])          # segment 0 -> 0
+        assert torch.equal(tgt[0, big:big + 3], inp[1, :3])     # segment 1 -> 0
+        assert (tgt[0, big + 3:] == wl.SENTINEL).all()
+        assert torch.equal(tgt[1, :5], inp[1, 3:8])             # segment 1 -> 1
+        assert (tgt[1, 5:] == wl.SENTINEL).all()
+        assert (c.signal.cpu().numpy() == 1).all()
+        np.testing.assert_array_equal(c.recv.cpu().numpy(), C.T)
+        rng = np.random.default_rng(7)
+        d_idx = np.concatenate([np.zeros(300, np.int64), np.ones(20, np.int64)])
+        offs = np.concatenate([rng.integers(0, w.tgt_slab, 300), np.arange(20)])
+        offs[:6] = [0, (1 << 30) - 1, 1 << 30, big - 1, big, big + 2]
+        got = tgt[torch.as_tensor(d_idx, device=DEV), torch.as_tensor(offs, device=DEV)].cpu().numpy()
+        for j in range(len(d_idx)):
+            src = locate.source_of(C, int(d_idx[j]), int(offs[j]), 1, w.in_slab)
+            want = wl.SENTINEL if src is None else wl.random_bytes_np(w.payload_seed, src, 1)[0]
+            assert got[j] == want, (int(d_idx[j]), int(offs[j]))
+    finally:
+        ex.close()
