@@ -21,6 +21,15 @@ The five workloads (c1..c5) are the exchange at growing sizes:
       H/tp=2048) to (E=64, C=2048, H/tp=2048), input already packed by
       destination; core_num 256.
 
+Beside them, the shapes of the exchange's variants:
+
+* c5b (:func:`bias_workload`): c5's shape in BF16 (or FP16) with the bias Add
+      fused in front, nblk = E/ep = 8, rows of H/tp = 2048 elements.
+* c3i (:func:`indexed_workload`): c3's MoE dispatch as the indexed exchange,
+      token tables stored once and the routing as gather lists.
+* c5's counts taken as the blocked exchange (nblk = 8) need no workload of
+      their own: the same bytes are read as temp3's block-rows.
+
 Payload bytes come from a counter-based SplitMix64 stream (Steele, Lea and
 Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014; the
 finalizer constants are Vigna's published splitmix64), so any byte can be

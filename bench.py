@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+from dataclasses import dataclass
 import json
 import os
 import platform
@@ -25,13 +26,24 @@ if ROOT not in sys.path:
 
 METRIC = "all_to_all_v achieved HBM GB/s (read+write) and % of MI355X peak, 1 GPU"
 PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
-# name -> (workload index, sub-blocks per segment).  c5u is c5's exchange taken
-# on the source's own temp3 layout (E/ep, ep*C, H/tp): the blocked exchange
-# with nblk = E/ep = 8.  c5b is that exchange in BF16 with the bias Add fused
-# in front (k = 0 marks the bias workload).  c3i is c3's MoE dispatch as the
-# indexed exchange: token tables stored once, the routing as gather lists.
-WORKLOADS = {"c1": (1, 1), "c2": (2, 1), "c3": (3, 1), "c4": (4, 1), "c5": (5, 1),
-             "c5u": (5, 8), "c5b": (0, 8), "c3i": (-3, 1)}
+# The workloads bench.py can time.  c1..c5 are the plain exchange.  c5u is
+# c5's exchange taken on the source's own temp3 layout (E/ep, ep*C, H/tp):
+# the blocked exchange with nblk = E/ep = 8.  c5b is that exchange in BF16
+# with the bias Add fused in front.  c3i is c3's MoE dispatch as the indexed
+# exchange: token tables stored once, the routing as gather lists.
+# cpu_scale: the size divisor of the oracle sample for the CPU baseline.
+@dataclass(frozen=True)
+class Spec:
+    kind: str            # "plain", "blocked", "bias" or "indexed"
+    k: int = 5           # workload index (plain and blocked)
+    nblk: int = 1
+    cpu_scale: int = 1
+
+
+WORKLOADS = {"c1": Spec("plain", 1), "c2": Spec("plain", 2), "c3": Spec("plain", 3, cpu_scale=4),
+             "c4": Spec("plain", 4, cpu_scale=4), "c5": Spec("plain", 5, cpu_scale=8),
+             "c5u": Spec("blocked", 5, nblk=8, cpu_scale=8),
+             "c5b": Spec("bias", nblk=8, cpu_scale=16), "c3i": Spec("indexed", cpu_scale=4)}
 DTYPE_NAMES = {0: "fp32", 1: "u8", 2: "fp16", 3: "bf16"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "copy_kernel_traffic.json")
 
@@ -60,32 +72,41 @@ def measured_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
-def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
+def make_workload(spec: Spec, scale: int = 1):
+    """The workload of a spec, at 1/scale of its size where the spec allows."""
+    from all_movement_amd import workloads as wl
+    if spec.kind == "indexed":
+        return wl.indexed_workload(scale=scale)
+    if spec.kind == "bias":
+        return wl.bias_workload(wl.BF16, scale=scale)
+    w = wl.workload(spec.k, scale=scale)
+    if spec.kind == "blocked":
+        w.name += f"_temp3_layout_nblk{spec.nblk}"
+    return w
+
+
+def run_gpu(spec: Spec, steps: int, warmup: int):
     import numpy as np
     import torch
     from all_movement_amd import a2av
     from all_movement_amd import workloads as wl
 
     dev = torch.device("cuda:0")
-    bias, hidden, bias_bytes = None, 0, 0
-    index, row_elems, index_bytes = None, 0, 0
-    if k == -3:
-        w = wl.indexed_workload()
-        row_elems = w.extra["row_elems"]
-        index = torch.from_numpy(w.extra["index"]).to(dev)
-        # The gather-list entries in use are read once per run.
-        index_bytes = 4 * int(w.counts.astype(np.int64).sum()) // row_elems
-    elif k == 0:
-        w = wl.bias_workload(wl.BF16)
-        hidden = w.extra["hidden"]
-        bias = wl.bias_tensor(w, nblk, hidden, dev)
-        bias_bytes = bias.numel() * bias.element_size()
-    else:
-        w = wl.workload(k)
-        if nblk > 1:
-            w.name += f"_temp3_layout_nblk{nblk}"
+    w = make_workload(spec)
+    # Arguments of Exchange.run beyond the five operands, and the extra bytes
+    # a run reads once (the bias, or the gather-list entries in use).
+    extra = {"nblk": spec.nblk}
+    extra_bytes = 0
+    if spec.kind == "indexed":
+        extra["row_elems"] = w.extra["row_elems"]
+        extra["index"] = torch.from_numpy(w.extra["index"]).to(dev)
+        extra_bytes = 4 * int(w.counts.astype(np.int64).sum()) // w.extra["row_elems"]
+    elif spec.kind == "bias":
+        extra["hidden"] = w.extra["hidden"]
+        extra["bias"] = wl.bias_tensor(w, spec.nblk, extra["hidden"], dev)
+        extra_bytes = extra["bias"].numel() * extra["bias"].element_size()
     log(f"[bench] {w.name}: payload {w.payload_bytes} B, generating inputs on the GPU")
-    inp = wl.input16_tensor(w, dev) if k == 0 else wl.input_tensor(w, dev)
+    inp = wl.input16_tensor(w, dev) if spec.kind == "bias" else wl.input_tensor(w, dev)
     tgt = torch.full((w.tgt_bytes,), wl.SENTINEL, dtype=torch.uint8, device=dev)
     sig = torch.zeros((w.P, w.S), dtype=torch.int32, device=dev)
     sc = torch.from_numpy(w.counts).to(dev)
@@ -96,8 +117,7 @@ def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
     torch.cuda.synchronize()
 
     for _ in range(warmup):
-        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, nblk=nblk, bias=bias,
-               hidden=hidden, index=index, row_elems=row_elems)
+        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, **extra)
     torch.cuda.synchronize()
     if ex.query_error() != a2av.OK:
         raise RuntimeError("warmup run reported a device-side error")
@@ -105,8 +125,7 @@ def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
 
     t0 = time.perf_counter()
     for _ in range(steps):
-        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, nblk=nblk, bias=bias,
-               hidden=hidden, index=index, row_elems=row_elems)
+        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, **extra)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if ex.query_error() != a2av.OK:
@@ -116,7 +135,7 @@ def run_gpu(k: int, steps: int, warmup: int, nblk: int = 1):
     sec = t1 - t0
     # Each payload byte read once and written once (plus the bias or the
     # gather lists, read once).
-    moved = 2 * w.payload_bytes + bias_bytes + index_bytes
+    moved = 2 * w.payload_bytes + extra_bytes
     res = {
         "w": w, "info": info, "sec": sec, "steps": steps, "moved": moved,
         "gbps": moved * steps / sec / 1e9, "ms_per_step": sec / steps * 1e3,
@@ -146,29 +165,29 @@ def copy_probe(nbytes: int, steps: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": steps}), flush=True)
 
 
-def cpu_baseline(k: int, min_seconds: float = 10.0):
-    """The oracle (as it stands) on a bounded sample of workload k on the host."""
+def cpu_baseline(spec: Spec, min_seconds: float = 10.0):
+    """The oracle (as it stands) on a bounded sample of the workload on the host."""
     import numpy as np
 
     import oracle
     from all_movement_amd import workloads as wl
 
-    # Sample: the same workload shape at a reduced size (c5 at 1/8: P=8 equal
-    # counts of 2^22 fp32, 1 GiB of payload; c3/c4 at 1/4), run whole.
-    # c5b (the bias workload) at 1/16, c3i (indexed) at 1/4.
-    scale = {-3: 4, 0: 16, 1: 1, 2: 1, 3: 4, 4: 4, 5: 8}[k]
-    if k == -3:
-        w = wl.indexed_workload(scale=scale)
+    # Sample: the same workload shape at 1/cpu_scale of its size (c5 at 1/8:
+    # P=8 equal counts of 2^22 fp32, 1 GiB of payload), run whole.
+    scale = spec.cpu_scale
+    w = make_workload(spec, scale=scale)
+    if spec.kind == "indexed":
         inp = wl.input_bytes_np(w)
         what = "checks + transpose + displacements + one memcpy per gathered row + signal"
-    elif k == 0:
-        w = wl.bias_workload(wl.BF16, scale=scale)
+    elif spec.kind == "bias":
         A, H = w.extra["nblk"], w.extra["hidden"]
         inp = wl.input16_np(w)
         bias = wl.bias_np(w, A, H)
         what = "checks + transpose + displacements + one fp32 add and bf16 rounding per element"
+    elif spec.kind == "blocked":
+        inp = wl.input_bytes_np(w)
+        what = "checks + transpose + displacements + one memcpy per sub-block + signal"
     else:
-        w = wl.workload(k, scale=scale)
         inp = wl.input_bytes_np(w)
         what = "checks + transpose + displacements + one memcpy per segment + signal"
     tgt = np.full(w.tgt_bytes, wl.SENTINEL, np.uint8)
@@ -180,12 +199,14 @@ def cpu_baseline(k: int, min_seconds: float = 10.0):
         kw = dict(P=w.P, S=w.S, in_slab=w.in_slab, tgt_slab=w.tgt_slab, core_num=w.core_num,
                   dtype=w.dtype)
         t0 = time.perf_counter()
-        if k == -3:
+        if spec.kind == "indexed":
             st = oracle.run_indexed(inp, tgt, sig, w.counts, rc, w.extra["index"],
                                     row_elems=w.extra["row_elems"],
                                     index_stride=w.extra["index_stride"], **kw)
-        elif k == 0:
+        elif spec.kind == "bias":
             st = oracle.run_bias(inp, tgt, sig, w.counts, rc, bias, nblk=A, hidden=H, **kw)
+        elif spec.kind == "blocked":
+            st = oracle.run_blocked(inp, tgt, sig, w.counts, rc, nblk=spec.nblk, **kw)
         else:
             st = oracle.run(inp, tgt, sig, w.counts, rc, **kw)
         times.append(time.perf_counter() - t0)
@@ -235,14 +256,14 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe << 20, args.steps)
         return
-    k, nblk = WORKLOADS[args.workload]
-    main_res = run_gpu(k, args.steps, args.warmup, nblk)
+    spec = WORKLOADS[args.workload]
+    main_res = run_gpu(spec, args.steps, args.warmup)
     w, info = main_res["w"], main_res["info"]
     log(f"[bench] {w.name}: {main_res['gbps']:.1f} GB/s whole run, K2 "
         f"{main_res['k2_gbps']:.1f} GB/s, {main_res['ms_per_step']:.3f} ms/step")
     also = {}
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
-        r = run_gpu(*WORKLOADS[name][:1], args.steps, args.warmup, WORKLOADS[name][1])
+        r = run_gpu(WORKLOADS[name], args.steps, args.warmup)
         log(f"[bench] {r['w'].name}: {r['gbps']:.1f} GB/s whole run, K2 {r['k2_gbps']:.1f} GB/s")
         also[r["w"].name] = {"value": round(r["gbps"], 1), "frac_of_peak": round(r["gbps"] / PEAK_GBPS, 4),
                              "k2_gbps": round(r["k2_gbps"], 1), "ms_per_step": round(r["ms_per_step"], 4),
@@ -276,7 +297,7 @@ def main():
         "also": also,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(k)
+        out["cpu_baseline"] = cpu_baseline(spec)
     print(json.dumps(out), flush=True)
 
 
