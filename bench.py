@@ -267,7 +267,8 @@ def main():
         log(f"[bench] {r['w'].name}: {r['gbps']:.1f} GB/s whole run, K2 {r['k2_gbps']:.1f} GB/s")
         also[r["w"].name] = {"value": round(r["gbps"], 1), "frac_of_peak": round(r["gbps"] / PEAK_GBPS, 4),
                              "k2_gbps": round(r["k2_gbps"], 1), "ms_per_step": round(r["ms_per_step"], 4),
-                             "blocks": r["info"].blocks, "workgroups": r["info"].workgroups}
+                             "blocks": r["info"].blocks, "workgroups": r["info"].workgroups,
+                             "traffic_per_launch": measured_traffic(r["w"].name)}
 
     traffic = measured_traffic(w.name)
     per_launch_bytes = main_res["moved"] / main_res["k2_launches_per_run"]
