@@ -35,7 +35,7 @@ ELEM_SIZE = {FP32: 4, INT8: 1, FP16: 2, BF16: 2}
 FLAG_PROFILE = 1
 
 EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_run_bias", "a2av_run_indexed",
-           "a2av_destroy",
+           "a2av_check_bias_args", "a2av_check_indexed_args", "a2av_destroy",
            "a2av_blocks", "a2av_check_args", "a2av_query_error", "a2av_launch_info_get", "a2av_profile_read",
            "a2av_status_string", "a2av_last_hip_error"]
 
@@ -86,6 +86,11 @@ def lib() -> ctypes.CDLL:
     L.a2av_blocks.restype = i64
     L.a2av_check_args.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, i32, i64, i32]
     L.a2av_check_args.restype = ctypes.c_int
+    L.a2av_check_bias_args.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32]
+    L.a2av_check_bias_args.restype = ctypes.c_int
+    L.a2av_check_indexed_args.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                          i64]
+    L.a2av_check_indexed_args.restype = ctypes.c_int
     L.a2av_query_error.argtypes = [vp]
     L.a2av_query_error.restype = ctypes.c_int
     L.a2av_launch_info_get.argtypes = [vp, i64, ctypes.POINTER(a2av_launch_info)]
@@ -146,6 +151,21 @@ def a2av_check_args(cfg: a2av_config, capacity, input, target, signal, send_coun
                     recv_counts, P, core_num, dtype) -> int:
     return lib().a2av_check_args(ctypes.byref(cfg), capacity, input, target, signal,
                                  send_counts, recv_counts, P, core_num, dtype)
+
+
+def a2av_check_bias_args(cfg: a2av_config, capacity, input, target, signal, send_counts,
+                         recv_counts, bias, P, core_num, dtype, nblk, hidden) -> int:
+    return lib().a2av_check_bias_args(ctypes.byref(cfg), capacity, input, target, signal,
+                                      send_counts, recv_counts, bias, P, core_num, dtype, nblk,
+                                      hidden)
+
+
+def a2av_check_indexed_args(cfg: a2av_config, capacity, input, target, signal, send_counts,
+                            recv_counts, index, P, core_num, dtype, row_elems,
+                            index_stride) -> int:
+    return lib().a2av_check_indexed_args(ctypes.byref(cfg), capacity, input, target, signal,
+                                         send_counts, recv_counts, index, P, core_num, dtype,
+                                         row_elems, index_stride)
 
 
 def a2av_query_error(h) -> int:

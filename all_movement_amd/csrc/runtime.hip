@@ -104,6 +104,25 @@ int a2av_check_args(const a2av_config* cfg, int64_t capacity, const void* input,
                               core_num, dtype);
 }
 
+int a2av_check_bias_args(const a2av_config* cfg, int64_t capacity, const void* input,
+                         const void* target, const int32_t* signal, const int32_t* send_counts,
+                         const int32_t* recv_counts, const void* bias, int32_t P,
+                         int64_t core_num, int32_t dtype, int32_t nblk, int32_t hidden) {
+  const int64_t limit = cfg && cfg->chunk_limit_bytes > 0 ? cfg->chunk_limit_bytes
+                                                          : a2av::kDefaultChunkLimit;
+  return a2av::check_bias_args(cfg, capacity, limit, input, target, signal, send_counts,
+                               recv_counts, bias, P, core_num, dtype, nblk, hidden);
+}
+
+int a2av_check_indexed_args(const a2av_config* cfg, int64_t capacity, const void* input,
+                            const void* target, const int32_t* signal,
+                            const int32_t* send_counts, const int32_t* recv_counts,
+                            const int32_t* index, int32_t P, int64_t core_num, int32_t dtype,
+                            int32_t row_elems, int64_t index_stride) {
+  return a2av::check_indexed_args(cfg, capacity, input, target, signal, send_counts, recv_counts,
+                                  index, P, core_num, dtype, row_elems, index_stride);
+}
+
 int a2av_create(a2av_handle** out, const a2av_config* cfg) {
   if (!out || !cfg) return A2AV_ERR_NULLPTR;
   *out = nullptr;

@@ -231,6 +231,21 @@ int a2av_check_args(const a2av_config *cfg, int64_t capacity, const void *input,
                     const void *target, const int32_t *signal, const int32_t *send_counts,
                     const int32_t *recv_counts, int32_t P, int64_t core_num, int32_t dtype);
 
+/* The host-side checks of a2av_run_bias and a2av_run_indexed alone (no GPU
+ * needed; nothing is dereferenced): the status either entry point would
+ * return before enqueuing anything, for a handle created with `cfg` (its
+ * chunk limit included, 0 = the default) whose co-resident capacity is
+ * `capacity` (0 = no limit). */
+int a2av_check_bias_args(const a2av_config *cfg, int64_t capacity, const void *input,
+                         const void *target, const int32_t *signal, const int32_t *send_counts,
+                         const int32_t *recv_counts, const void *bias, int32_t P,
+                         int64_t core_num, int32_t dtype, int32_t nblk, int32_t hidden);
+int a2av_check_indexed_args(const a2av_config *cfg, int64_t capacity, const void *input,
+                            const void *target, const int32_t *signal,
+                            const int32_t *send_counts, const int32_t *recv_counts,
+                            const int32_t *index, int32_t P, int64_t core_num, int32_t dtype,
+                            int32_t row_elems, int64_t index_stride);
+
 /* Wait for the handle's last stream, then return and clear the latched
  * device-side status (A2AV_OK when every run since the last query was valid;
  * otherwise the first failure: INVALID_ARGS, OVER_CAPACITY or TIMEOUT). */

@@ -153,3 +153,140 @@ def test_create_rejects_bad_geometry_without_touching_the_device():
                 _cfg(4, 1, 16, -1)]:
         st, h = a2av.a2av_create(cfg)
         assert st == a2av.ERR_INVALID_ARGS and h is None
+
+
+# ------------------------------------------------ bias and indexed host checks
+
+def _bias_bufs(P=4, nblk=2, hidden=8, slab=128, dtype=wl.BF16):
+    C = np.full((P, P), nblk * hidden, np.int32)           # whole rows of every sub-block
+    bias = np.zeros(P * nblk * hidden, np.float32 if dtype == wl.BF16 else np.uint16)
+    return [np.zeros(P * slab, np.uint8), np.full(P * slab, wl.SENTINEL, np.uint8),
+            np.zeros((P, 8), np.int32), C, np.zeros((P, P), np.int32), bias]
+
+
+def _bias_both(bufs, P=4, S=8, slab=128, tgt_slab=None, core_num=1, dtype=wl.BF16, nblk=2,
+               hidden=8, capacity=0, chunk=0, override=None):
+    tgt_slab = slab if tgt_slab is None else tgt_slab
+    ptrs = [b.ctypes.data for b in bufs]
+    for i, v in (override or {}).items():
+        ptrs[i] = v
+    cfg = a2av.a2av_config(0, P, slab, tgt_slab, S, 0, chunk, 0, 0, 0)
+    lib_st = a2av.a2av_check_bias_args(cfg, capacity, *ptrs, P, core_num, dtype, nblk, hidden)
+    or_st = oracle.lib().a2av_oracle_run_bias(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], P, S,
+                                              slab, tgt_slab, core_num, dtype, capacity, nblk,
+                                              ptrs[5], hidden)
+    return lib_st, or_st
+
+
+BIAS_ROWS = [
+    ("ok", {}),
+    ("ok fp16", {"dtype": wl.FP16}),
+    ("null bias", {"override": {5: None}}),
+    ("null input", {"override": {0: None}}),
+    ("dtype fp32", {"dtype": wl.FP32}),
+    ("dtype int8", {"dtype": wl.INT8}),
+    ("nblk 0", {"nblk": 0}),
+    ("hidden 0", {"hidden": 0}),
+    ("P differs", {"P": 5}),
+    ("core_num 0", {"core_num": 0}),
+    ("S < B", {"core_num": 12}),
+    ("capacity", {"core_num": 8, "capacity": 4}),
+    ("odd slab", {"slab": 129}),
+]
+
+
+@pytest.mark.parametrize("row", BIAS_ROWS, ids=[r[0] for r in BIAS_ROWS])
+def test_bias_host_checks_match_oracle(row):
+    name, kw = row
+    kw = dict(kw)
+    dtype = kw.get("dtype", wl.BF16)
+    slab = kw.get("slab", 128)
+    b = _bias_bufs(dtype=dtype if dtype in (wl.BF16, wl.FP16) else wl.BF16, slab=slab)
+    if "P" in kw:            # the run names a P the handle was not created for
+        P = kw.pop("P")
+        ptrs = [x.ctypes.data for x in b]
+        cfg = a2av.a2av_config(0, 4, slab, slab, 8, 0, 0, 0, 0, 0)
+        st = a2av.a2av_check_bias_args(cfg, 0, *ptrs, P, 1, wl.BF16, 2, 8)
+        assert st == a2av.ERR_INVALID_ARGS
+        return
+    lib_st, or_st = _bias_both(b, **kw)
+    assert lib_st == or_st, (name, lib_st, or_st)
+
+
+def test_bias_host_checks_aliasing_matches_oracle():
+    b = _bias_bufs()
+    for j in range(5):
+        lib_st, or_st = _bias_both(b, override={5: b[j].ctypes.data})
+        assert lib_st == or_st == a2av.ERR_INVALID_ARGS, j
+
+
+def test_bias_host_limits_of_the_gpu_path():
+    # Rows of a multiple of 8 elements, 16-byte aligned operands, slabs and
+    # chunk limit: the GPU path refuses what the oracle (no such limits) runs.
+    b = _bias_bufs(hidden=12)
+    assert _bias_both(b, hidden=12, slab=192) == (a2av.ERR_INVALID_ARGS, a2av.OK)
+    b = _bias_bufs()
+    buf = np.zeros(4 * 128 + 16, np.uint8)
+    for off, idx in [(2, 0), (8, 1)]:
+        lib_st, or_st = _bias_both(b, override={idx: buf.ctypes.data + off})
+        assert (lib_st, or_st) == (a2av.ERR_INVALID_ARGS, a2av.OK), (off, idx)
+    b = _bias_bufs(slab=136)
+    assert _bias_both(b, slab=136) == (a2av.ERR_INVALID_ARGS, a2av.OK)
+    b = _bias_bufs()
+    assert _bias_both(b, chunk=1000) == (a2av.ERR_INVALID_ARGS, a2av.OK)
+    assert _bias_both(b, chunk=4096) == (a2av.OK, a2av.OK)
+
+
+def _idx_bufs(P=4, R=4, rows=2, slab=64, stride=8, dtype=wl.INT8):
+    C = np.full((P, P), rows * R, np.int32)
+    table_rows = slab // (R * wl.ELEM_SIZE[dtype])
+    index = (np.arange(P * stride) % table_rows).astype(np.int32)
+    return [np.zeros(P * slab, np.uint8), np.full(P * 256, wl.SENTINEL, np.uint8),
+            np.zeros((P, 8), np.int32), C, np.zeros((P, P), np.int32), index]
+
+
+def _idx_both(bufs, P=4, S=8, slab=64, core_num=1, dtype=wl.INT8, R=4, stride=8, capacity=0,
+              override=None):
+    ptrs = [b.ctypes.data for b in bufs]
+    for i, v in (override or {}).items():
+        ptrs[i] = v
+    cfg = a2av.a2av_config(0, P, slab, 256, S, 0, 0, 0, 0, 0)
+    lib_st = a2av.a2av_check_indexed_args(cfg, capacity, *ptrs, P, core_num, dtype, R, stride)
+    or_st = oracle.lib().a2av_oracle_run_indexed(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4],
+                                                 ptrs[5], P, S, slab, 256, core_num, dtype,
+                                                 capacity, R, stride)
+    return lib_st, or_st
+
+
+IDX_ROWS = [
+    ("ok", {}),
+    ("null index", {"override": {5: None}}),
+    ("null recv", {"override": {4: None}}),
+    ("dtype bf16", {"dtype": wl.BF16}),
+    ("row_elems 0", {"R": 0}),
+    ("stride 0", {"stride": 0}),
+    ("core_num 2^31", {"core_num": 2**31}),
+    ("S < B", {"core_num": 12}),
+    ("capacity", {"core_num": 8, "capacity": 4}),
+    ("slab not whole fp32", {"dtype": wl.FP32, "slab": 66}),
+]
+
+
+@pytest.mark.parametrize("row", IDX_ROWS, ids=[r[0] for r in IDX_ROWS])
+def test_indexed_host_checks_match_oracle(row):
+    name, kw = row
+    slab = kw.get("slab", 64)
+    b = _idx_bufs(slab=slab)
+    lib_st, or_st = _idx_both(b, **kw)
+    assert lib_st == or_st, (name, lib_st, or_st)
+
+
+def test_indexed_host_checks_aliasing_matches_oracle():
+    b = _idx_bufs()
+    for j in range(5):
+        lib_st, or_st = _idx_both(b, override={5: b[j].ctypes.data + 4})
+        assert lib_st == or_st == a2av.ERR_INVALID_ARGS, j
+    # The device decides bad entries: the host check passes them.
+    b = _idx_bufs()
+    b[5][3] = -1
+    assert _idx_both(b) == (a2av.OK, a2av.ERR_INVALID_ARGS)
