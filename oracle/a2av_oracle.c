@@ -25,8 +25,11 @@
  * typeSize bytes move.  The displacements are the exclusive prefix sums of the
  * counts (no displacement operand exists in the five-operand statement).
  *
- * Parity status of every function here is recorded at its definition.  There
- * is no floating-point arithmetic: payload moves as raw bytes.
+ * Parity status of every function here is recorded at its definition.  One
+ * part is "parity unpinned": the signal update (arrive), whose +1 per exchange
+ * the pages do not fix; the tests hold the GPU path to this definition only.
+ * The plain, blocked and indexed exchanges move raw bytes; the fused-bias
+ * exchange adds in binary32 and rounds to the 16-bit payload type.
  */
 #include <math.h>
 #include <stdint.h>
