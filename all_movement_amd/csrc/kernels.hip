@@ -16,7 +16,10 @@
 // segment is ever written.  When source and destination are not congruent
 // mod 16 the body is realigned through LDS: each wave stages a row of 64
 // aligned source words, then every lane funnels its word and its right
-// neighbour's with v_alignbyte.  On the run's final launch every admitted
+// neighbour's with v_alignbyte.  Pieces of at most 8 KiB are copied by one
+// wave each, dealt to the waves in turn, so a tile of many small segments
+// costs about one memory round trip instead of one per segment.  On the
+// run's final launch every admitted
 // block raises its flag in every rank's signal row, and when B > 1 (a
 // cooperative launch) every workgroup waits, with a bounded spin, until all
 // B blocks have arrived.  The block/flag protocol is the block-aware
@@ -244,12 +247,17 @@ __device__ inline u32x4 funnel(u32x4 a, u32x4 b, uint32_t r) {
   return o;
 }
 
-// Body with source and destination both 16-byte aligned: K words, copied by
-// the whole workgroup.  Thread t moves words t, t + NT, ... : each load
-// instruction of a wave covers 1 KiB, and a thread's kUnroll loads in flight
-// are NT words (16 KiB) apart.
-__device__ inline void wg_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int tid) {
-  constexpr int NT = kCopyThreads;
+// The copy bodies below run on a group of ng threads, ng / kWave waves: the
+// whole workgroup (ng = kCopyThreads, t = thread index, gw = wave index) or
+// one wave (ng = kWave, t = lane, gw = 0).  The group size is a run-time
+// value so that both share one copy of each body (two inlined copies of the
+// bodies overflow the 128 registers a 1024-thread workgroup allows).
+
+// Body with source and destination both 16-byte aligned: K words.  Thread t
+// moves words t, t + NG, ... : each load instruction of a wave covers 1 KiB,
+// and a thread's kUnroll loads in flight are ng words apart.
+__device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int tid, int ng) {
+  const int NT = ng;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, K * 16);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(d, K * 16);
   int64_t k0 = 0;
@@ -281,14 +289,14 @@ __device__ inline void wg_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int 
 // Body whose source sits phi = 4*Q + r bytes (1..15) past a 16-byte boundary:
 // output word k is bytes [phi, phi+16) of aligned source words A[k], A[k+1].
 // Words A[0..K] all hold body bytes, so every load stays inside 16-byte words
-// that the segment touches.  Rows of 64 output words go to the waves in turn;
+// that the segment touches.  Rows of 64 output words go to the group's waves in turn;
 // lane l of row q loads A[64q + l], takes A[64q + l + 1] from its right
 // neighbour through the wave's LDS slot (1 KiB, reused row after row), and
 // lane 63 uses A[64q + 64], which the whole wave loads as one broadcast word.
 template <int Q>
-__device__ void wg_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r, u32x4* slot,
-                                int lane, int wave) {
-  constexpr int NW = kCopyThreads / kWave;
+__device__ void grp_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r, u32x4* slot,
+                                 int lane, int wave, int ng) {
+  const int NW = ng / kWave;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(A, (K + 1) * 16);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(D, K * 16);
   const int64_t nrows = (K + kWave - 1) / kWave;
@@ -321,46 +329,70 @@ __device__ void wg_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r,
   }
 }
 
-// Copy n bytes src -> dst (one piece of one segment) with the whole
-// workgroup.  The destination body is whole aligned 16-byte words; the at
-// most 15 bytes on either side are written one byte per thread, so no byte
-// outside the piece is ever stored.
-__device__ void wg_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int tid, int lane,
-                              int wave, u32x4* slot) {
+// Copy n bytes src -> dst (one piece of one segment) with a group.  The
+// destination body is whole aligned 16-byte words; the at most 15 bytes on
+// either side are written one byte per thread, so no byte outside the piece
+// is ever stored.  Those edge bytes are loaded before the body and stored
+// after it, so their round trip overlaps the body's instead of preceding it.
+__device__ void grp_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int t, int lane,
+                               int gw, int ng, u32x4* slot) {
   const uintptr_t d0 = uintptr_t(dst);
   const uintptr_t body_lo = (d0 + 15u) & ~uintptr_t(15);
   const uintptr_t body_hi = (d0 + uintptr_t(n)) & ~uintptr_t(15);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(dst, n);
   if (body_lo >= body_hi) {
-    for (int64_t k = tid; k < n; k += kCopyThreads)
+    for (int64_t k = t; k < n; k += ng)
       __builtin_amdgcn_raw_buffer_store_b8(src[k], rb, int(k), 0, kStorePolicy);
     return;
   }
   const int64_t head = int64_t(body_lo - d0);
   const int64_t tail_at = int64_t(body_hi - d0);
   const int64_t tail = n - tail_at;
-  if (tid < head) __builtin_amdgcn_raw_buffer_store_b8(src[tid], rb, tid, 0, kStorePolicy);
-  if (tid >= 16 && tid - 16 < tail) {
-    const int64_t k = tail_at + tid - 16;
-    __builtin_amdgcn_raw_buffer_store_b8(src[k], rb, int(k), 0, kStorePolicy);
-  }
+  // Threads 0..head-1 take the head bytes, threads 16..16+tail-1 the tail.
+  const bool edge = t < head || (t >= 16 && t - 16 < tail);
+  const int64_t ek = t < 16 ? int64_t(t) : tail_at + t - 16;
+  uint8_t ev = 0;
+  if (edge) ev = src[ek];
 
   const uint8_t* sb = src + head;
   const int64_t K = int64_t(body_hi - body_lo) >> 4;
   const uint32_t phi = uint32_t(uintptr_t(sb) & 15u);
   u32x4* D = reinterpret_cast<u32x4*>(dst + head);
   if (phi == 0) {
-    wg_copy_aligned(reinterpret_cast<const u32x4*>(sb), D, K, tid);
-    return;
+    grp_copy_aligned(reinterpret_cast<const u32x4*>(sb), D, K, t, ng);
+  } else {
+    const u32x4* A = reinterpret_cast<const u32x4*>(sb - phi);
+    const uint32_t r = phi & 3u;
+    switch (phi >> 2) {
+      case 0: grp_copy_realign<0>(A, D, K, r, slot, lane, gw, ng); break;
+      case 1: grp_copy_realign<1>(A, D, K, r, slot, lane, gw, ng); break;
+      case 2: grp_copy_realign<2>(A, D, K, r, slot, lane, gw, ng); break;
+      default: grp_copy_realign<3>(A, D, K, r, slot, lane, gw, ng); break;
+    }
   }
-  const u32x4* A = reinterpret_cast<const u32x4*>(sb - phi);
-  const uint32_t r = phi & 3u;
-  switch (phi >> 2) {
-    case 0: wg_copy_realign<0>(A, D, K, r, slot, lane, wave); break;
-    case 1: wg_copy_realign<1>(A, D, K, r, slot, lane, wave); break;
-    case 2: wg_copy_realign<2>(A, D, K, r, slot, lane, wave); break;
-    default: wg_copy_realign<3>(A, D, K, r, slot, lane, wave); break;
+  if (edge) __builtin_amdgcn_raw_buffer_store_b8(ev, rb, int(ek), 0, kStorePolicy);
+}
+
+// Pieces of at most kSmallPiece bytes (one pass of a wave's aligned body)
+// take one wave each, dealt to the waves in turn; `small` counts the small
+// pieces met so far and is the same in every wave.  A workgroup copying such
+// pieces one after another would pay a memory round trip per piece (measured
+// on gfx950: 16 pieces of ~130 bytes took 24 us in one workgroup).  Larger
+// pieces take the whole workgroup.
+constexpr int64_t kSmallPiece = int64_t(kWave) * kUnroll * 16;
+
+__device__ inline void wg_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int tid,
+                                     int lane, int wave, u32x4* slot, int& small) {
+  constexpr int NW = kCopyThreads / kWave;
+  const bool one = n <= kSmallPiece;
+  if (one) {
+    const bool mine = (small & (NW - 1)) == __builtin_amdgcn_readfirstlane(wave);
+    ++small;
+    if (!mine) return;
   }
+  // One call site, so the bodies are inlined once.
+  grp_copy_piece(src, dst, n, one ? lane : tid, lane, one ? 0 : wave, one ? kWave : kCopyThreads,
+                 slot);
 }
 
 // ------------------------------------------------ K2, fused bias Add path
@@ -613,7 +645,7 @@ __device__ inline int64_t readlane64(int64_t v, int lane) {
 // so a piece is also cut where a sub-block ends.
 template <int MODE>
 __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int64_t x, int64_t b,
-                                  int i, int tid, int lane, int wave, u32x4* slot) {
+                                  int i, int tid, int lane, int wave, u32x4* slot, int& small) {
   while (x < b) {
     const int64_t seg_lo = tab.prefix[i];
     const int64_t seg_hi = tab.prefix[i + 1];
@@ -639,7 +671,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
             const int64_t end = (r + 1) * RB < pe - seg_lo ? (r + 1) * RB : pe - seg_lo;
             const int64_t row = __builtin_amdgcn_readfirstlane(list[r]);
             wg_copy_piece(wave_uniform(table + row * RB + w), wave_uniform(dseg + off),
-                          wave_uniform(end - off), tid, lane, wave, slot);
+                          wave_uniform(end - off), tid, lane, wave, slot, small);
             off = end;
           }
         }
@@ -664,7 +696,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
       } else if (p.nblk == 1) {
         const int64_t off = x - seg_lo;
         wg_copy_piece(p.input + tab.src[i] + off, p.target + tab.dst[i] + off, pe - x, tid,
-                      lane, wave, slot);
+                      lane, wave, slot, small);
       } else {
         const int64_t sub = (seg_hi - seg_lo) / p.nblk;
         const int64_t stride = tab.sstride[i / p.P];
@@ -673,7 +705,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
           const int64_t w = off - a * sub;
           const int64_t end = (a + 1) * sub < pe - seg_lo ? (a + 1) * sub : pe - seg_lo;
           wg_copy_piece(p.input + tab.src[i] + a * stride + w, p.target + tab.dst[i] + off,
-                        end - off, tid, lane, wave, slot);
+                        end - off, tid, lane, wave, slot, small);
           off = end;
         }
       }
@@ -701,7 +733,10 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   RunPlan* plan = p.ws.plan;
-  if (plan->valid == 0) return;  // the run failed its device checks: write nothing
+  // The flag and the payload size are loaded together (one round trip).
+  const int valid = plan->valid;
+  const int64_t T = plan->total_bytes;
+  if (valid == 0) return;  // the run failed its device checks: write nothing
 
   // Launch c claims tiles on plan->claim[c & 1]; the launch before it in the
   // stream (c + 1) has finished with the other counter, which launch c - 1
@@ -710,7 +745,6 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
     __hip_atomic_store(&plan->claim[(p.chunk + 1) & 1], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 
-  const int64_t T = plan->total_bytes;
   const int64_t c_lo = p.chunk_lo < T ? p.chunk_lo : T;
   const int64_t c_hi = p.chunk_hi < T ? p.chunk_hi : T;
   // A chunk past the run's payload has nothing to copy (the final launch
@@ -743,6 +777,8 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   const int64_t rounds_static = MODE == 3 ? rounds : (rounds + 3) / 4;
   const int64_t nstatic = W * rounds_static < ntiles ? W * rounds_static : ntiles;
 
+  int small = 0;  // small pieces met so far (see wg_copy_piece)
+
   // A wave works through its workgroup's static tiles (blockIdx.x, + W, ...)
   // 64 at a time: lane l first finds the bounds and first segment of the l-th
   // tile of the batch, then the wave walks the batch, reading them with
@@ -761,7 +797,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
     }
     for (int j = 0; j < kWave && t0 + int64_t(j) * W < nstatic; ++j) {
       copy_range<MODE>(p, tab, readlane64(la, j), readlane64(lb, j), __builtin_amdgcn_readlane(li, j),
-                 tid, lane, wave, slots[wave]);
+                 tid, lane, wave, slots[wave], small);
     }
   }
 
@@ -786,7 +822,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
       if (a < b)
         copy_range<MODE>(p, tab, wave_uniform(a), wave_uniform(b),
                          __builtin_amdgcn_readfirstlane(seg_of(tab.prefix, nseg, a)), tid, lane,
-                         wave, slots[wave]);
+                         wave, slots[wave], small);
       __syncthreads();  // every wave is done with s_claim's tile
       if (tid == 0) s_claim = nstatic + int64_t(next);
       __syncthreads();
@@ -805,8 +841,11 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   __syncthreads();
   if (tid == 0) {
     const int b = int(blockIdx.x) / p.G;
+    // A block of one workgroup needs no count (and saves its round trip).
     const uint32_t done =
-        __hip_atomic_fetch_add(&p.ws.blk_cnt[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p.G == 1 ? 0u
+                 : __hip_atomic_fetch_add(&p.ws.blk_cnt[b], 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
     if (done == uint32_t(p.G - 1)) {
       for (int r = 0; r < p.P; ++r)
         __hip_atomic_fetch_add(&p.signal[int64_t(r) * p.S + b], 1, __ATOMIC_RELAXED,

@@ -5,7 +5,9 @@ seeded synthetic workload already resident in HBM.  Prints ONE JSON line with
 the whole-run throughput (payload bytes read + written per second), the
 roofline of the dominant kernel (K2, HBM-bound) from HIP events recorded by
 the library on the run's stream during the timed region, and the CPU oracle
-timed on a bounded sample of the same workload on the host.
+timed on a bounded sample of the same workload on the host.  Each workload
+is also timed cache-cold: a 1 GiB buffer is written before every run, and
+the medians of the single runs are reported under "cold".
 
     python bench.py [--steps K] [--warmup W] [--workload c5] [--also c3,c4]
 """
@@ -38,12 +40,16 @@ class Spec:
     k: int = 5           # workload index (plain and blocked)
     nblk: int = 1
     cpu_scale: int = 1
+    cold_runs: int = 50  # runs of the cache-cold protocol (each after a 1 GiB flush)
 
 
 WORKLOADS = {"c1": Spec("plain", 1), "c2": Spec("plain", 2), "c3": Spec("plain", 3, cpu_scale=4),
-             "c4": Spec("plain", 4, cpu_scale=4), "c5": Spec("plain", 5, cpu_scale=8),
-             "c5u": Spec("blocked", 5, nblk=8, cpu_scale=8),
-             "c5b": Spec("bias", nblk=8, cpu_scale=16), "c3i": Spec("indexed", cpu_scale=4)}
+             "c4": Spec("plain", 4, cpu_scale=4, cold_runs=20),
+             "c5": Spec("plain", 5, cpu_scale=8, cold_runs=5),
+             "c5u": Spec("blocked", 5, nblk=8, cpu_scale=8, cold_runs=5),
+             "c5b": Spec("bias", nblk=8, cpu_scale=16, cold_runs=5),
+             "c3i": Spec("indexed", cpu_scale=4)}
+FLUSH_BYTES = 1 << 30       # written before each cache-cold run: above the 256 MB MALL
 DTYPE_NAMES = {0: "fp32", 1: "u8", 2: "fp16", 3: "bf16"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "copy_kernel_traffic.json")
 
@@ -85,7 +91,7 @@ def make_workload(spec: Spec, scale: int = 1):
     return w
 
 
-def run_gpu(spec: Spec, steps: int, warmup: int):
+def run_gpu(spec: Spec, steps: int, warmup: int, cold: bool = True):
     import numpy as np
     import torch
     from all_movement_amd import a2av
@@ -131,6 +137,25 @@ def run_gpu(spec: Spec, steps: int, warmup: int):
     if ex.query_error() != a2av.OK:
         raise RuntimeError("timed run reported a device-side error")
     k1_us, k2_us, k2_launches, runs = ex.profile()
+
+    # Cache-cold protocol: before each run, write a 1 GiB scratch buffer so
+    # that no payload line survives in the L2s or the MALL, then time that
+    # run alone -- by its events (K1 start to last K2 end) and by the host
+    # clock around the run and a synchronize.  Medians are reported.
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if cold else None
+    dev_s, wall_s = [], []
+    for i in range(spec.cold_runs if cold else 0):
+        flush.fill_(i & 0xFF)
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, stream, **extra)
+        torch.cuda.synchronize()
+        wall_s.append(time.perf_counter() - c0)
+        c1_us, c2_us, _, n = ex.profile()
+        dev_s.append((c1_us + c2_us) * 1e-6 / max(n, 1))
+    if ex.query_error() != a2av.OK:
+        raise RuntimeError("cache-cold run reported a device-side error")
+    del flush
     ex.close()
     sec = t1 - t0
     # Each payload byte read once and written once (plus the bias or the
@@ -145,6 +170,15 @@ def run_gpu(spec: Spec, steps: int, warmup: int):
     # The dominant kernel is K2; its launches share the payload.
     res["k2_us_per_launch"] = res["k2_us_per_run"] / res["k2_launches_per_run"]
     res["k2_gbps"] = moved / (res["k2_us_per_run"] * 1e-6) / 1e9
+    dev_s.sort()
+    wall_s.sort()
+    res["cold"] = None if not dev_s else {
+        "runs": spec.cold_runs, "flush_bytes": FLUSH_BYTES,
+        "gbps_device_median": round(moved / dev_s[len(dev_s) // 2] / 1e9, 1),
+        "gbps_wall_median": round(moved / wall_s[len(wall_s) // 2] / 1e9, 1),
+        "us_device_median": round(dev_s[len(dev_s) // 2] * 1e6, 2),
+        "us_wall_median": round(wall_s[len(wall_s) // 2] * 1e6, 2),
+    }
     del inp, tgt
     torch.cuda.empty_cache()
     return res
@@ -240,9 +274,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="c3,c4,c5u,c5b,c3i",
+    ap.add_argument("--also", default="c1,c2,c3,c4,c5u,c5b,c3i",
                     help="other workloads reported beside it")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cache-cold runs (profiler runs that count only the timed runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain torch device copy of MIB MiB --steps times (the "
                          "known-size reference for HBM byte counters) and exit")
@@ -257,18 +293,19 @@ def main():
         copy_probe(args.copy_probe << 20, args.steps)
         return
     spec = WORKLOADS[args.workload]
-    main_res = run_gpu(spec, args.steps, args.warmup)
+    main_res = run_gpu(spec, args.steps, args.warmup, cold=not args.no_cold)
     w, info = main_res["w"], main_res["info"]
     log(f"[bench] {w.name}: {main_res['gbps']:.1f} GB/s whole run, K2 "
         f"{main_res['k2_gbps']:.1f} GB/s, {main_res['ms_per_step']:.3f} ms/step")
     also = {}
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
-        r = run_gpu(WORKLOADS[name], args.steps, args.warmup)
+        r = run_gpu(WORKLOADS[name], args.steps, args.warmup, cold=not args.no_cold)
         log(f"[bench] {r['w'].name}: {r['gbps']:.1f} GB/s whole run, K2 {r['k2_gbps']:.1f} GB/s")
         also[r["w"].name] = {"value": round(r["gbps"], 1), "frac_of_peak": round(r["gbps"] / PEAK_GBPS, 4),
                              "k2_gbps": round(r["k2_gbps"], 1), "ms_per_step": round(r["ms_per_step"], 4),
                              "blocks": r["info"].blocks, "workgroups": r["info"].workgroups,
-                             "traffic_per_launch": measured_traffic(r["w"].name)}
+                             "traffic_per_launch": measured_traffic(r["w"].name),
+                             "cold": r["cold"]}
 
     traffic = measured_traffic(w.name)
     per_launch_bytes = main_res["moved"] / main_res["k2_launches_per_run"]
@@ -295,6 +332,7 @@ def main():
                    "payload_bytes": w.payload_bytes, "parallelism": "1 GPU, P virtual ranks"},
         "frac_of_peak": round(main_res["gbps"] / PEAK_GBPS, 4),
         "roofline": roofline,
+        "cold": main_res["cold"],
         "also": also,
     }
     if not args.no_cpu:
