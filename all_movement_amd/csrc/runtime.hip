@@ -270,9 +270,17 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
     cp.unit = int64_t(nblk) * (mode != 0 ? x.hidden : 1);
   }
 
+  // Profiling events are not recorded while the stream is being captured
+  // into a graph: the host tally counts enqueued runs, and a graph's replays
+  // would not pass through it.
   hipEvent_t* ev = nullptr;
-  if (h->profile)
-    ev = &h->events[size_t(h->run_counter % kProfileRuns) * size_t(h->events_per_run)];
+  if (h->profile) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(s, &cs)) != hipSuccess)
+      return hip_fail(h, e, "hipStreamIsCapturing");
+    if (cs == hipStreamCaptureStatusNone)
+      ev = &h->events[size_t(h->run_counter % kProfileRuns) * size_t(h->events_per_run)];
+  }
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
   if ((e = a2av::launch_count(cp, s)) != hipSuccess) return hip_fail(h, e, "count_kernel launch");
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");

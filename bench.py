@@ -7,7 +7,9 @@ roofline of the dominant kernel (K2, HBM-bound) from HIP events recorded by
 the library on the run's stream during the timed region, and the CPU oracle
 timed on a bounded sample of the same workload on the host.  Each workload
 is also timed cache-cold: a 1 GiB buffer is written before every run, and
-the medians of the single runs are reported under "cold".
+the medians of the single runs are reported under "cold".  The small
+exchanges (c1, c2) are also timed as replays of one run captured into a HIP
+graph ("graph").
 
     python bench.py [--steps K] [--warmup W] [--workload c5] [--also c3,c4]
 """
@@ -41,9 +43,10 @@ class Spec:
     nblk: int = 1
     cpu_scale: int = 1
     cold_runs: int = 50  # runs of the cache-cold protocol (each after a 1 GiB flush)
+    graph: bool = False  # also time replays of one run captured into a HIP graph
 
 
-WORKLOADS = {"c1": Spec("plain", 1), "c2": Spec("plain", 2), "c3": Spec("plain", 3, cpu_scale=4),
+WORKLOADS = {"c1": Spec("plain", 1, graph=True), "c2": Spec("plain", 2, graph=True), "c3": Spec("plain", 3, cpu_scale=4),
              "c4": Spec("plain", 4, cpu_scale=4, cold_runs=20),
              "c5": Spec("plain", 5, cpu_scale=8, cold_runs=5),
              "c5u": Spec("blocked", 5, nblk=8, cpu_scale=8, cold_runs=5),
@@ -156,6 +159,28 @@ def run_gpu(spec: Spec, steps: int, warmup: int, cold: bool = True):
     if ex.query_error() != a2av.OK:
         raise RuntimeError("cache-cold run reported a device-side error")
     del flush
+
+    # Small exchanges are bound by the host's enqueue; a caller that replays a
+    # captured run pays only the graph launch.  One run is captured and
+    # replayed back to back (each replay is one more run).
+    graph = None
+    if spec.graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ex.run(inp, tgt, sig, sc, rc, w.core_num, w.dtype, **extra)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        g_sec = (time.perf_counter() - g0) / steps
+        if ex.query_error() != a2av.OK:
+            raise RuntimeError("graph replay reported a device-side error")
+        del g
+        graph = {"runs": steps, "us_per_run": round(g_sec * 1e6, 2)}
     ex.close()
     sec = t1 - t0
     # Each payload byte read once and written once (plus the bias or the
@@ -172,6 +197,9 @@ def run_gpu(spec: Spec, steps: int, warmup: int, cold: bool = True):
     res["k2_gbps"] = moved / (res["k2_us_per_run"] * 1e-6) / 1e9
     dev_s.sort()
     wall_s.sort()
+    if graph is not None:
+        graph["gbps"] = round(moved / (graph["us_per_run"] * 1e-6) / 1e9, 2)
+    res["graph"] = graph
     res["cold"] = None if not dev_s else {
         "runs": spec.cold_runs, "flush_bytes": FLUSH_BYTES,
         "gbps_device_median": round(moved / dev_s[len(dev_s) // 2] / 1e9, 1),
@@ -305,7 +333,7 @@ def main():
                              "k2_gbps": round(r["k2_gbps"], 1), "ms_per_step": round(r["ms_per_step"], 4),
                              "blocks": r["info"].blocks, "workgroups": r["info"].workgroups,
                              "traffic_per_launch": measured_traffic(r["w"].name),
-                             "cold": r["cold"]}
+                             "cold": r["cold"], "graph": r["graph"]}
 
     traffic = measured_traffic(w.name)
     per_launch_bytes = main_res["moved"] / main_res["k2_launches_per_run"]
@@ -333,6 +361,7 @@ def main():
         "frac_of_peak": round(main_res["gbps"] / PEAK_GBPS, 4),
         "roofline": roofline,
         "cold": main_res["cold"],
+        "graph": main_res["graph"],
         "also": also,
     }
     if not args.no_cpu:

@@ -31,6 +31,12 @@
  * Thread safety: a handle is not thread-safe and its workspace is shared by
  * all runs on it; runs on one handle must be ordered (one stream, or streams
  * the caller orders).  Use one handle per concurrent stream.
+ *
+ * Graphs: a run enqueues only kernel launches on its stream (no copies, no
+ * memsets, no synchronization), so a run may be captured into a HIP graph;
+ * every replay is one more run over the buffers' contents at replay time,
+ * ordered with the handle's other runs like any run.  A handle created with
+ * A2AV_FLAG_PROFILE records no events while its stream is capturing.
  */
 #ifndef A2AV_H
 #define A2AV_H
