@@ -37,7 +37,7 @@ FLAG_PROFILE = 1
 EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_run_bias", "a2av_run_indexed",
            "a2av_check_bias_args", "a2av_check_indexed_args", "a2av_destroy",
            "a2av_blocks", "a2av_check_args", "a2av_query_error", "a2av_launch_info_get", "a2av_profile_read",
-           "a2av_status_string", "a2av_last_hip_error"]
+           "a2av_profile_sample", "a2av_status_string", "a2av_last_hip_error"]
 
 
 class a2av_config(ctypes.Structure):
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32),
                                     ctypes.POINTER(i32)]
     L.a2av_profile_read.restype = ctypes.c_int
+    L.a2av_profile_sample.argtypes = [vp, i32]
+    L.a2av_profile_sample.restype = ctypes.c_int
     L.a2av_status_string.argtypes = [ctypes.c_int]
     L.a2av_status_string.restype = ctypes.c_char_p
     L.a2av_last_hip_error.argtypes = [vp]
@@ -184,6 +186,10 @@ def a2av_profile_read(h) -> tuple[int, float, float, int, int]:
     st = lib().a2av_profile_read(h, ctypes.byref(k1), ctypes.byref(k2), ctypes.byref(n),
                                  ctypes.byref(runs))
     return st, k1.value, k2.value, n.value, runs.value
+
+
+def a2av_profile_sample(h, every: int) -> int:
+    return lib().a2av_profile_sample(h, every)
 
 
 def a2av_status_string(status: int) -> str:
@@ -310,6 +316,10 @@ class Exchange:
         st, info = a2av_launch_info_get(self.h, core_num)
         _raise(st, "a2av_launch_info_get")
         return info
+
+    def profile_sample(self, every: int) -> None:
+        """Record the profiling events on one run in ``every`` from now on."""
+        _raise(a2av_profile_sample(self.h, every), "a2av_profile_sample", self.h)
 
     def profile(self) -> tuple[float, float, int, int]:
         """(K1 us, K2 us, K2 launches, runs) summed over the runs since the last call."""

@@ -42,7 +42,9 @@ struct a2av_handle {
   std::vector<hipEvent_t> events;
   int32_t events_per_run = 0;
   int64_t profiled_runs = 0;  // runs recorded since the last a2av_profile_read
-  int64_t run_counter = 0;
+  int64_t run_counter = 0;    // runs recorded
+  int32_t profile_every = 1;  // record one run in profile_every ...
+  int64_t enqueued = 0;       // ... counting the runs enqueued since it was set
   std::string last_error;
 };
 
@@ -278,7 +280,7 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if ((e = hipStreamIsCapturing(s, &cs)) != hipSuccess)
       return hip_fail(h, e, "hipStreamIsCapturing");
-    if (cs == hipStreamCaptureStatusNone)
+    if (cs == hipStreamCaptureStatusNone && h->enqueued++ % h->profile_every == 0)
       ev = &h->events[size_t(h->run_counter % kProfileRuns) * size_t(h->events_per_run)];
   }
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
@@ -432,6 +434,14 @@ int a2av_profile_read(a2av_handle* h, double* k1_us, double* k2_us, int32_t* k2_
   *k2_launches = int32_t(n * h->launches);
   *runs = int32_t(n);
   h->profiled_runs = 0;
+  return A2AV_OK;
+}
+
+int a2av_profile_sample(a2av_handle* h, int32_t every) {
+  if (!h) return A2AV_ERR_NULLPTR;
+  if (!h->profile || every < 1) return A2AV_ERR_INVALID_ARGS;
+  h->profile_every = every;
+  h->enqueued = 0;
   return A2AV_OK;
 }
 

@@ -270,6 +270,14 @@ int a2av_launch_info_get(a2av_handle *h, int64_t core_num, a2av_launch_info *out
 int a2av_profile_read(a2av_handle *h, double *k1_us, double *k2_us, int32_t *k2_launches,
                       int32_t *runs);
 
+/* With A2AV_FLAG_PROFILE: record the events on one run in `every`, counting
+ * runs as they are enqueued from this call on (the first run after the call
+ * is recorded), so that a series of short runs is timed on a sample instead
+ * of paying the events' own cost (a few microseconds each on the stream) on
+ * every run.  every = 1, the default, records every run.  Errors: NULLPTR,
+ * INVALID_ARGS (every < 1, or a handle created without profiling). */
+int a2av_profile_sample(a2av_handle *h, int32_t every);
+
 /* Human-readable name of a status code (static storage). */
 const char *a2av_status_string(int status);
 
