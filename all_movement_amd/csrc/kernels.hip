@@ -1013,8 +1013,10 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
 }  // namespace
 
 hipError_t launch_count(const CountParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(count_kernel, dim3(1), dim3(kCountThreads), 0, stream, p);
-  return hipGetLastError();
+  // The launch's own status (hipGetLastError could report an earlier call's).
+  void* args[] = {const_cast<CountParams*>(&p)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&count_kernel), dim3(1),
+                         dim3(kCountThreads), args, 0, stream);
 }
 
 namespace {

@@ -74,6 +74,9 @@ int hip_fail(a2av_handle* h, hipError_t e, const char* what) {
   if (h) {
     h->last_error = std::string(what) + ": " + hipGetErrorString(e);
   }
+  // The status carries the failure: clear HIP's per-thread last error so a
+  // later, unrelated call does not report it again.
+  (void)hipGetLastError();
   return A2AV_ERR_HIP;
 }
 

@@ -32,6 +32,13 @@
  * all runs on it; runs on one handle must be ordered (one stream, or streams
  * the caller orders).  Use one handle per concurrent stream.
  *
+ * Processes: a run with B > 1 ends in a cooperative launch.  On ROCm a
+ * process that has made a cooperative launch keeps the device's resource for
+ * them until it exits, and meanwhile another process's cooperative launch on
+ * the same GPU fails (A2AV_ERR_HIP, "the operation cannot be performed in the
+ * present state").  Runs with B = 1 are unaffected.  Drive each GPU from one
+ * process.
+ *
  * Graphs: a run enqueues only kernel launches on its stream (no copies, no
  * memsets, no synchronization), so a run may be captured into a HIP graph;
  * every replay is one more run over the buffers' contents at replay time,
@@ -135,7 +142,8 @@ int a2av_create(a2av_handle **out, const a2av_config *cfg);
  * failure writes nothing, is latched in the handle and is reported by
  * a2av_query_error; a2av_run itself has already returned A2AV_OK.
  * The call does not synchronize: results are visible to later work on
- * `stream`.  Returns A2AV_ERR_HIP if a launch fails.
+ * `stream`.  Returns A2AV_ERR_HIP if a launch fails; K1 may then have run,
+ * so recv_counts may be written while the target and the signal are not.
  */
 int a2av_run(a2av_handle *h, const void *input, void *target, int32_t *signal,
              const int32_t *send_counts, int32_t *recv_counts, int32_t P, int64_t core_num,
