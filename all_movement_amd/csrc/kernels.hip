@@ -260,7 +260,32 @@ __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int
   const int NT = ng;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, K * 16);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(d, K * 16);
-  int64_t k0 = 0;
+  // Words are numbered from the start of the 128-byte destination line that
+  // holds word 0 (the lp words before it get k < 0 and are skipped), so each
+  // wave's store instruction writes whole lines: a line split between two
+  // instructions can reach HBM as two partial writes.
+  const int64_t lp = int64_t((reinterpret_cast<uintptr_t>(d) >> 4) & 7u);
+  // A predicated pass over words [k0, k0 + NT * kUnroll) of [0, K), so short
+  // pieces keep kUnroll loads in flight too.
+  auto guarded_pass = [&](int64_t k0) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t k = k0 + j * NT + tid;
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (k >= 0 && k < K) v[j] = load16(rs, k);
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t k = k0 + j * NT + tid;
+      if (k >= 0 && k < K) store16(rd, k, v[j]);
+    }
+  };
+  int64_t k0 = -lp;
+  if (lp != 0) {
+    guarded_pass(k0);
+    k0 += int64_t(NT) * kUnroll;
+  }
   for (; k0 + int64_t(NT) * kUnroll <= K; k0 += int64_t(NT) * kUnroll) {
     u32x4 v[kUnroll];
 #pragma unroll
@@ -268,55 +293,44 @@ __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) store16(rd, k0 + j * NT + tid, v[j]);
   }
-  // The remainder (under NT * kUnroll words) in one predicated pass, so short
-  // pieces keep kUnroll loads in flight too.
-  if (k0 < K) {
-    u32x4 v[kUnroll];
-#pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t k = k0 + j * NT + tid;
-      v[j] = u32x4{0u, 0u, 0u, 0u};
-      if (k < K) v[j] = load16(rs, k);
-    }
-#pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t k = k0 + j * NT + tid;
-      if (k < K) store16(rd, k, v[j]);
-    }
-  }
+  if (k0 < K) guarded_pass(k0);  // the remainder, under NT * kUnroll words
 }
 
 // Body whose source sits phi = 4*Q + r bytes (1..15) past a 16-byte boundary:
 // output word k is bytes [phi, phi+16) of aligned source words A[k], A[k+1].
 // Words A[0..K] all hold body bytes, so every load stays inside 16-byte words
-// that the segment touches.  Rows of 64 output words go to the group's waves in turn;
-// lane l of row q loads A[64q + l], takes A[64q + l + 1] from its right
-// neighbour through the wave's LDS slot (1 KiB, reused row after row), and
-// lane 63 uses A[64q + 64], which the whole wave loads as one broadcast word.
+// that the segment touches.  Rows of 64 output words go to the group's waves
+// in turn, each row one whole 1 KiB run of destination lines: row q holds
+// output words k = 64q + l - lp (lp = D's word within its 128-byte line; the
+// words with k < 0 are skipped).  Lane l of row q loads A[k], takes A[k + 1]
+// from its right neighbour through the wave's LDS slot (1 KiB, reused row
+// after row), and lane 63 uses A[64q + 64 - lp], which the whole wave loads
+// as one broadcast word.
 template <int Q>
 __device__ void grp_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r, u32x4* slot,
                                  int lane, int wave, int ng) {
   const int NW = ng / kWave;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(A, (K + 1) * 16);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(D, K * 16);
-  const int64_t nrows = (K + kWave - 1) / kWave;
+  const int64_t lp = int64_t((reinterpret_cast<uintptr_t>(D) >> 4) & 7u);
+  const int64_t nrows = (K + lp + kWave - 1) / kWave;
   for (int64_t r0 = 0; r0 < nrows; r0 += int64_t(kRealignUnroll) * NW) {
     u32x4 v[kRealignUnroll];
     u32x4 x[kRealignUnroll];
 #pragma unroll
     for (int j = 0; j < kRealignUnroll; ++j) {
       const int64_t row = r0 + int64_t(j) * NW + wave;
-      const int64_t k = row * kWave + lane;
-      const int64_t next = row * kWave + kWave;
+      const int64_t k = row * kWave + lane - lp;
+      const int64_t next = row * kWave + kWave - lp;
       v[j] = u32x4{0u, 0u, 0u, 0u};
       x[j] = u32x4{0u, 0u, 0u, 0u};
-      if (row < nrows && k <= K) v[j] = load16(rs, k);
+      if (row < nrows && k >= 0 && k <= K) v[j] = load16(rs, k);
       if (row < nrows && next <= K) x[j] = load16(rs, next);
     }
 #pragma unroll
     for (int j = 0; j < kRealignUnroll; ++j) {
       const int64_t row = r0 + int64_t(j) * NW + wave;
-      const int64_t k = row * kWave + lane;
+      const int64_t k = row * kWave + lane - lp;
       slot[lane] = v[j];
       // Lanes read a word another lane wrote: keep the compiler from moving
       // LDS accesses across these points (a wave's LDS operations run in order).
@@ -324,7 +338,7 @@ __device__ void grp_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r
       u32x4 hi = slot[(lane + 1) & (kWave - 1)];
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       if (lane == kWave - 1) hi = x[j];
-      if (row < nrows && k < K) store16(rd, k, funnel<Q>(v[j], hi, r));
+      if (row < nrows && k >= 0 && k < K) store16(rd, k, funnel<Q>(v[j], hi, r));
     }
   }
 }
