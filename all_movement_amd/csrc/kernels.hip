@@ -306,6 +306,45 @@ __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int
 // from its right neighbour through the wave's LDS slot (1 KiB, reused row
 // after row), and lane 63 uses A[64q + 64 - lp], which the whole wave loads
 // as one broadcast word.
+// One batch of kRealignUnroll rows per wave, starting at row r0.  Guarded
+// batches check every word against [0, K]; interior batches (every row whole
+// and inside the piece) run unpredicated, so their loads issue back to back.
+template <int Q, bool kGuard>
+__device__ inline void realign_batch(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rd,
+                                     int64_t r0, int64_t nrows, int64_t K, int64_t lp,
+                                     uint32_t r, u32x4* slot, int lane, int wave, int NW) {
+  u32x4 v[kRealignUnroll];
+  u32x4 x[kRealignUnroll];
+#pragma unroll
+  for (int j = 0; j < kRealignUnroll; ++j) {
+    const int64_t row = r0 + int64_t(j) * NW + wave;
+    const int64_t k = row * kWave + lane - lp;
+    const int64_t next = row * kWave + kWave - lp;
+    if (kGuard) {
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      x[j] = u32x4{0u, 0u, 0u, 0u};
+      if (row < nrows && k >= 0 && k <= K) v[j] = load16(rs, k);
+      if (row < nrows && next <= K) x[j] = load16(rs, next);
+    } else {
+      v[j] = load16(rs, k);
+      x[j] = load16(rs, next);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kRealignUnroll; ++j) {
+    const int64_t row = r0 + int64_t(j) * NW + wave;
+    const int64_t k = row * kWave + lane - lp;
+    slot[lane] = v[j];
+    // Lanes read a word another lane wrote: keep the compiler from moving
+    // LDS accesses across these points (a wave's LDS operations run in order).
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    u32x4 hi = slot[(lane + 1) & (kWave - 1)];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (lane == kWave - 1) hi = x[j];
+    if (!kGuard || (row < nrows && k >= 0 && k < K)) store16(rd, k, funnel<Q>(v[j], hi, r));
+  }
+}
+
 template <int Q>
 __device__ void grp_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r, u32x4* slot,
                                  int lane, int wave, int ng) {
@@ -314,32 +353,16 @@ __device__ void grp_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(D, K * 16);
   const int64_t lp = int64_t((reinterpret_cast<uintptr_t>(D) >> 4) & 7u);
   const int64_t nrows = (K + lp + kWave - 1) / kWave;
-  for (int64_t r0 = 0; r0 < nrows; r0 += int64_t(kRealignUnroll) * NW) {
-    u32x4 v[kRealignUnroll];
-    u32x4 x[kRealignUnroll];
-#pragma unroll
-    for (int j = 0; j < kRealignUnroll; ++j) {
-      const int64_t row = r0 + int64_t(j) * NW + wave;
-      const int64_t k = row * kWave + lane - lp;
-      const int64_t next = row * kWave + kWave - lp;
-      v[j] = u32x4{0u, 0u, 0u, 0u};
-      x[j] = u32x4{0u, 0u, 0u, 0u};
-      if (row < nrows && k >= 0 && k <= K) v[j] = load16(rs, k);
-      if (row < nrows && next <= K) x[j] = load16(rs, next);
-    }
-#pragma unroll
-    for (int j = 0; j < kRealignUnroll; ++j) {
-      const int64_t row = r0 + int64_t(j) * NW + wave;
-      const int64_t k = row * kWave + lane - lp;
-      slot[lane] = v[j];
-      // Lanes read a word another lane wrote: keep the compiler from moving
-      // LDS accesses across these points (a wave's LDS operations run in order).
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      u32x4 hi = slot[(lane + 1) & (kWave - 1)];
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      if (lane == kWave - 1) hi = x[j];
-      if (row < nrows && k >= 0 && k < K) store16(rd, k, funnel<Q>(v[j], hi, r));
-    }
+  const int64_t batch = int64_t(kRealignUnroll) * NW;
+  for (int64_t r0 = 0; r0 < nrows; r0 += batch) {
+    // Interior: no row of the batch starts before word 0 (row 0 does when
+    // lp > 0) and the last one's next-row word A[64 (r0 + batch) - lp] is
+    // inside A[0..K].
+    const bool interior = (r0 > 0 || lp == 0) && (r0 + batch) * kWave - lp <= K;
+    if (interior)
+      realign_batch<Q, false>(rs, rd, r0, nrows, K, lp, r, slot, lane, wave, NW);
+    else
+      realign_batch<Q, true>(rs, rd, r0, nrows, K, lp, r, slot, lane, wave, NW);
   }
 }
 
@@ -515,7 +538,19 @@ __device__ void wg_bias_piece(const uint8_t* src, uint8_t* dst, int64_t n, const
     const u32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, int(h * BE), 0, 0);
     u32x4 b1 = u32x4{0u, 0u, 0u, 0u};
     if constexpr (MODE == 1) b1 = __builtin_amdgcn_raw_buffer_load_b128(rb, int(h * BE + 16), 0, 0);
-    for (int64_t k0 = 0; k0 < K; k0 += int64_t(NTe) * kBiasUnroll) {
+    // Whole steps unpredicated, so a step's loads issue back to back; then
+    // the remainder predicated.
+    const int64_t step = int64_t(NTe) * kBiasUnroll;
+    int64_t k0 = 0;
+    for (; k0 + step <= K; k0 += step) {
+      u32x4 v[kBiasUnroll];
+#pragma unroll
+      for (int j = 0; j < kBiasUnroll; ++j) v[j] = load16(rs, k0 + int64_t(j) * NTe + tid);
+#pragma unroll
+      for (int j = 0; j < kBiasUnroll; ++j)
+        store16(rd, k0 + int64_t(j) * NTe + tid, add_bias_word<MODE>(v[j], b0, b1));
+    }
+    if (k0 < K) {
       u32x4 v[kBiasUnroll];
 #pragma unroll
       for (int j = 0; j < kBiasUnroll; ++j) {
