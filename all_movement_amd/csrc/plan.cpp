@@ -25,6 +25,10 @@ int check_config(const a2av_config* cfg) {
   // Slab offsets are formed in 64-bit arithmetic; keep P * slab far from overflow.
   if (cfg->in_slab_bytes > (int64_t(1) << 46) || cfg->tgt_slab_bytes > (int64_t(1) << 46))
     return A2AV_ERR_INVALID_ARGS;
+  // A chunk limit so small that the payload bound needs more than
+  // kMaxLaunches launches is refused.
+  const int64_t limit = cfg->chunk_limit_bytes > 0 ? cfg->chunk_limit_bytes : kDefaultChunkLimit;
+  if ((max_payload(cfg) + limit - 1) / limit > kMaxLaunches) return A2AV_ERR_INVALID_ARGS;
   return A2AV_OK;
 }
 

@@ -11,6 +11,10 @@ namespace a2av {
 
 constexpr int32_t kMaxP = 64;
 constexpr int64_t kDefaultChunkLimit = int64_t(1) << 30;
+// At most this many K2 launches per run (the chunk plan's launch count is an
+// int32 and every launch costs microseconds; 2^20 GiB-sized chunks is far
+// beyond any device's memory).
+constexpr int64_t kMaxLaunches = int64_t(1) << 20;
 constexpr int64_t kInt32Max = 2147483647LL;
 // Longest bias row of a2av_run_bias: the row's bytes must stay a 32-bit
 // buffer offset.

@@ -107,7 +107,8 @@ typedef struct a2av_launch_info {
 
 /*
  * Create a handle bound to cfg->device: checks the geometry (P in 1..64,
- * slabs >= 1, S >= 1, chunk limit >= 0), queries the co-resident capacity of
+ * slabs >= 1, S >= 1, chunk limit >= 0 and at most 2^20 launches to cover
+ * P * min(slabs) bytes), queries the co-resident capacity of
  * the copy kernel and allocates the workspace (displacement tables, plan
  * words, block counters, the latched error word).
  * Returns A2AV_OK and sets *out, or an error with *out left NULL.

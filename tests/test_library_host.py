@@ -155,6 +155,20 @@ def test_create_rejects_bad_geometry_without_touching_the_device():
         assert st == a2av.ERR_INVALID_ARGS and h is None
 
 
+def test_chunk_plan_is_bounded_to_2_pow_20_launches():
+    # P * min(slabs) / chunk limit: exactly 2^20 launches is the largest plan.
+    P, slab = 8, 1 << 20
+    ok = a2av.a2av_config(0, P, slab, slab, 1, 0, 8, 0, 0, 0)         # 2^23 / 8 = 2^20
+    over = a2av.a2av_config(0, P, slab, slab, 1, 0, 7, 0, 0, 0)       # > 2^20
+    # Host checks only: the five operands are distinct, non-overlapping fake addresses.
+    args = lambda cfg: (ctypes.byref(cfg), 0, 1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44,
+                        P, 1, wl.INT8)
+    assert a2av.lib().a2av_check_args(*args(ok)) == a2av.OK
+    assert a2av.lib().a2av_check_args(*args(over)) == a2av.ERR_INVALID_ARGS
+    st, h = a2av.a2av_create(over)
+    assert st == a2av.ERR_INVALID_ARGS and h is None
+
+
 # ------------------------------------------------ bias and indexed host checks
 
 def _bias_bufs(P=4, nblk=2, hidden=8, slab=128, dtype=wl.BF16):
