@@ -237,7 +237,7 @@ def test_bias_host_checks_aliasing_matches_oracle():
 def test_bias_host_limits_of_the_gpu_path():
     # Rows of a multiple of 8 elements, 16-byte aligned operands, slabs and
     # chunk limit: the GPU path refuses what the oracle (no such limits) runs.
-    b = _bias_bufs(hidden=12)
+    b = _bias_bufs(hidden=12, slab=192)     # buffers sized for the slab the run names
     assert _bias_both(b, hidden=12, slab=192) == (a2av.ERR_INVALID_ARGS, a2av.OK)
     b = _bias_bufs()
     buf = np.zeros(4 * 128 + 16, np.uint8)
