@@ -256,7 +256,7 @@ __device__ inline u32x4 funnel(u32x4 a, u32x4 b, uint32_t r) {
 // bodies overflow the 128 registers a 1024-thread workgroup allows).
 
 // Body with source and destination both 16-byte aligned: K words.  Thread t
-// moves words t, t + NG, ... : each load instruction of a wave covers 1 KiB,
+// moves words t, t + ng, ... : each load instruction of a wave covers 1 KiB,
 // and a thread's kUnroll loads in flight are ng words apart.
 __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int tid, int ng) {
   const int NT = ng;
