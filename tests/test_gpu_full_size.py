@@ -44,6 +44,25 @@ def test_full_size_against_oracle(k):
         ex.close()
 
 
+def test_p64_against_oracle():
+    # The largest P: 64 ranks (4,096 segments), FP32 counts uniform in
+    # [0, 2^17] with a fifth zeroed, 32 MiB slabs (4 GiB of allocations),
+    # core_num 256 (B = 256, cooperative); whole oracle on the host.
+    rng = np.random.default_rng(64)
+    C = wl.uniform_counts(rng, 64, 1 << 17, 0.2)
+    w = wl.custom(64, wl.FP32, C, core_num=256, S=256, in_slab=32 << 20, tgt_slab=32 << 20,
+                  seed=64)
+    say("P=64", w.payload_bytes)
+    c = Case(w, host_input=False)
+    ex = exchange_for(w)
+    try:
+        info = ex.launch_info(w.core_num)
+        assert info.blocks == 256
+        c.assert_matches(c.run_gpu(ex), c.run_oracle())
+    finally:
+        ex.close()
+
+
 def test_c4_with_small_chunks_against_oracle():
     # The chunked path the c4 text intends: 256 MiB per launch (about 4 launches).
     w = wl.workload(4)
