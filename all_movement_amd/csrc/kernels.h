@@ -21,9 +21,10 @@ struct alignas(64) RunPlan {
 // Device workspace layout, carved out of one allocation by the host.
 struct Workspace {
   RunPlan* plan;
-  int64_t* prefix;   // [P*P + 1] exclusive prefix of segment bytes, s-major order
-  int64_t* src_off;  // [P*P] byte offset of segment (s, d) inside `input`
-  int64_t* dst_off;  // [P*P] byte offset of segment (s, d) inside `target`
+  int64_t* prefix;   // [P*P + 1] exclusive prefix of segment bytes in the flattened
+                     // order (d-major, or s-major for the row gather)
+  int64_t* src_off;  // [P*P] byte offset inside `input` of each segment, flattened order
+  int64_t* dst_off;  // [P*P] byte offset inside `target` of each segment, flattened order
   uint32_t* blk_cnt; // [max blocks] workgroups of each block that finished copying
   int64_t* sstride;  // [P] bytes per source block-row (blocked exchange)
 };

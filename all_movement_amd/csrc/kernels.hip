@@ -5,7 +5,7 @@
 // send_counts, and derives every segment's source and target byte offsets
 // (exclusive prefixes along d on the send side and along s on the receive
 // side, one thread per row or column walking the LDS copy of the matrix),
-// and the flattened s-major payload prefix that K2 partitions.
+// and the prefix of the flattened payload that K2 partitions.
 //
 // K2 (copy_kernel, W = B * G workgroups): the flattened payload is cut into
 // tiles of at most 128 KiB; the first quarter is dealt round-robin to the
@@ -64,7 +64,8 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   __shared__ int64_t doff[kMaxP * kMaxP];
   __shared__ int64_t rowsum[kMaxP];        // elements each source sends
   __shared__ int64_t colsum[kMaxP];        // elements each destination receives
-  __shared__ int64_t rowbase[kMaxP + 1];   // bytes before source s in the flattened order
+  __shared__ int64_t rowbase[kMaxP + 1];   // bytes before source s (s-major order)
+  __shared__ int64_t colbase[kMaxP];       // bytes before destination d (d-major order)
   __shared__ int flags;
 
   const int tid = threadIdx.x;
@@ -119,14 +120,19 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
                                              : rowsum[tid] * p.elem > p.in_slab;
     if (src_over || colsum[tid] * p.elem > p.tgt_slab) atomicOr(&flags, 2);
   } else if (tid == kWave) {
-    // Flattened payload order is s-major (segment i = s*P + d): row bases
-    // are the exclusive prefix of the row byte totals, rowbase[kMaxP] = T.
+    // Row bases, the exclusive prefix of the row byte totals (rowbase[kMaxP]
+    // = T), and column bases, that of the column byte totals.
     int64_t acc = 0;
     for (int s2 = 0; s2 < P; ++s2) {
       rowbase[s2] = acc;
       acc += rowsum[s2] * p.elem;
     }
     rowbase[kMaxP] = acc;
+    acc = 0;
+    for (int d = 0; d < P; ++d) {
+      colbase[d] = acc;
+      acc += colsum[d] * p.elem;
+    }
   }
   __syncthreads();
 
@@ -164,12 +170,21 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     return;
   }
 
+  // The flattened order K2 partitions.  The copy and bias bodies take it
+  // destination-major (segment j = d*P + s): the tiles in flight then write
+  // one contiguous stretch of a target slab and read pieces of several
+  // source slabs, which DRAM serves better than the transpose the other way
+  // round.  The row gather takes it source-major (j = s*P + d), measured
+  // faster for it.
+  const bool dmajor = p.index == nullptr;
+
   // Send side (wave 0, one thread per source): the exclusive prefix along d
-  // (input packed by destination) gives the flattened prefix; the source
-  // offset is the prefix of the sub-block sizes (the segment's sub-block in
-  // block-row 0; block-rows are sstride[s] bytes apart; nblk = 1 is the plain
-  // exchange).  Receive side (wave 1, one thread per destination): the
-  // exclusive prefix along s (target packed by source).
+  // (input packed by destination); the source offset is the prefix of the
+  // sub-block sizes (the segment's sub-block in block-row 0; block-rows are
+  // sstride[s] bytes apart; nblk = 1 is the plain exchange).  Receive side
+  // (wave 1, one thread per destination): the exclusive prefix along s
+  // (target packed by source).  Each side writes the flattened prefix in
+  // its own order.
   if (wave == 0 && lane < P) {
     const int s2 = lane;
     const int64_t in0 = int64_t(s2) * p.in_slab;
@@ -178,7 +193,7 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     if (p.nblk == 1) {
       for (int d = 0; d < P; ++d) {
         soff[s2 * P + d] = in0 + ex;
-        pre[s2 * P + d] = rb + ex;
+        if (!dmajor) pre[s2 * P + d] = rb + ex;
         ex += int64_t(C[s2 * P + d]) * p.elem;
       }
       p.ws.sstride[s2] = ex;
@@ -187,7 +202,7 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
       for (int d = 0; d < P; ++d) {
         const int32_t c = C[s2 * P + d];
         soff[s2 * P + d] = in0 + sub_ex;
-        pre[s2 * P + d] = rb + ex;
+        if (!dmajor) pre[s2 * P + d] = rb + ex;
         ex += int64_t(c) * p.elem;
         sub_ex += int64_t(c / p.nblk) * p.elem;
       }
@@ -195,17 +210,22 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     }
   } else if (wave == 1 && lane < P) {
     const int d = lane;
-    int64_t ex = int64_t(d) * p.tgt_slab;
+    const int64_t t0 = int64_t(d) * p.tgt_slab;
+    const int64_t cb = colbase[d];
+    int64_t ex = 0;
     for (int s2 = 0; s2 < P; ++s2) {
-      doff[s2 * P + d] = ex;
+      doff[s2 * P + d] = t0 + ex;
+      if (dmajor) pre[d * P + s2] = cb + ex;
       ex += int64_t(C[s2 * P + d]) * p.elem;
     }
   }
   __syncthreads();
   for (int i = tid; i < PP; i += kCountThreads) {
-    p.ws.src_off[i] = soff[i];
+    // Segment s -> d sits at index k = s*P + d of soff and doff.
+    const int k = dmajor ? (i - (i / P) * P) * P + i / P : i;
+    p.ws.src_off[i] = soff[k];
     p.ws.prefix[i] = pre[i];
-    p.ws.dst_off[i] = doff[i];
+    p.ws.dst_off[i] = doff[k];
     // recv_counts[d][s] = send_counts[s][d].
     const int d = i / P;
     const int s2 = i - d * P;
@@ -651,6 +671,12 @@ __device__ void wg_gather_words(const uint8_t* table, uint8_t* dseg, int64_t off
   }
 }
 
+// Source rank of flattened segment i (the order K1 chose for the body).
+template <int MODE>
+__device__ inline int source_of(int i, int P) {
+  return MODE == 3 ? i / P : i % P;
+}
+
 // Segment tables of one run, staged in LDS by every workgroup.
 struct SegTables {
   int64_t prefix[kMaxP * kMaxP + 1];
@@ -773,7 +799,7 @@ __device__ void gather_static(const CopyParams& p, const SegTables& tab, int nse
         }
         int64_t pe = b < seg_hi ? b : seg_hi;
         if (pe > x + kPassBytes) pe = x + kPassBytes;
-        const int s = i / p.P;
+        const int s = source_of<3>(i, p.P);
         const int64_t src_i = wave_uniform(tab.src[i]);
         const int64_t row0 = (src_i - int64_t(s) * p.in_slab) / RB;
         g.table = wave_uniform(p.input + int64_t(s) * p.in_slab);
@@ -844,7 +870,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
       if constexpr (MODE == 3) {
         // Row gather: the segment's rows start at row (src - s * in_slab) / RB
         // of source s's gather list.
-        const int s = i / p.P;
+        const int s = source_of<MODE>(i, p.P);
         const int64_t RB = p.row_bytes;
         const int64_t row0 = (tab.src[i] - int64_t(s) * p.in_slab) / RB;
         const int32_t* list = p.index + int64_t(s) * p.index_stride + row0;
@@ -869,7 +895,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
         // Fused bias Add: pieces end at sub-block ends; sub-block a of source
         // s takes bias row (s, a).
         const int64_t sub = (seg_hi - seg_lo) / p.nblk;
-        const int s = i / p.P;
+        const int s = source_of<MODE>(i, p.P);
         const int64_t stride = tab.sstride[s];
         constexpr int be = MODE == 1 ? 4 : 2;
         for (int64_t off = x - seg_lo; off < pe - seg_lo;) {
@@ -889,7 +915,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
                       lane, wave, slot, small);
       } else {
         const int64_t sub = (seg_hi - seg_lo) / p.nblk;
-        const int64_t stride = tab.sstride[i / p.P];
+        const int64_t stride = tab.sstride[source_of<MODE>(i, p.P)];
         for (int64_t off = x - seg_lo; off < pe - seg_lo;) {
           const int64_t a = off / sub;
           const int64_t w = off - a * sub;

@@ -6,7 +6,7 @@
 //                                                   segment offsets, payload prefix
 //   K2  copy_kernel x launches  (B*G workgroups)    launch c copies payload bytes
 //                                                   [c*limit, (c+1)*limit) of the
-//                                                   s-major flattened order
+//                                                   flattened payload order
 // The number of K2 launches comes from the slab geometry (the payload bound
 // P * min(in_slab, tgt_slab)), so the host never reads the counts back; a
 // launch whose range lies past the run's payload does no copying.  Launches
