@@ -16,7 +16,7 @@ from all_movement_amd import a2av  # noqa: E402
 from all_movement_amd import workloads as wl  # noqa: E402
 from tests.gpu_harness import DEV, Case, exchange_for, say, upload  # noqa: E402
 
-N_CASES = 96
+N_CASES = 200
 
 
 @pytest.fixture(autouse=True)
