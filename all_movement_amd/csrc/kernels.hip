@@ -57,11 +57,17 @@ constexpr int kStorePolicy = 2 | 16;
 
 // ------------------------------------------------------------------ K1
 
+// The LDS matrices of K1 are indexed [row][column] with a pitch of
+// kMaxP + 1 entries, so a wave's lanes walking rows (a stride of one pitch)
+// and lanes walking columns (consecutive entries) both hit distinct banks.
+constexpr int kPitch = kMaxP + 1;
+__device__ inline int lds_at(int r, int c) { return r * kPitch + c; }
+
 __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
-  __shared__ int32_t C[kMaxP * kMaxP];
-  __shared__ int64_t soff[kMaxP * kMaxP];  // staged outputs, written back coalesced
-  __shared__ int64_t pre[kMaxP * kMaxP];
-  __shared__ int64_t doff[kMaxP * kMaxP];
+  __shared__ int32_t C[kMaxP * kPitch];     // C[lds_at(s, d)] = send_counts[s][d]
+  __shared__ int64_t soff[kMaxP * kPitch];  // staged outputs, written back coalesced
+  __shared__ int64_t pre[kMaxP * kPitch];
+  __shared__ int64_t doff[kMaxP * kPitch];
   __shared__ int64_t rowsum[kMaxP];        // elements each source sends
   __shared__ int64_t colsum[kMaxP];        // elements each destination receives
   __shared__ int64_t rowbase[kMaxP + 1];   // bytes before source s (s-major order)
@@ -87,7 +93,7 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
 #pragma unroll 4
   for (int i = tid; i < PP; i += kCountThreads) {
     const int32_t c = p.send_counts[i];
-    C[i] = c;
+    C[lds_at(i / P, i - (i / P) * P)] = c;
     bad |= c < 0 ? 1 : 0;
     bad |= (unit > kInt32Max ? c != 0 : c % int32_t(unit) != 0) ? 8 : 0;
   }
@@ -105,11 +111,11 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   // the LDS matrix (at most 64 entries; cheaper than a cross-lane scan).
   if (wave == 0 && lane < P) {
     int64_t acc = 0;
-    for (int d = 0; d < P; ++d) acc += C[lane * P + d];
+    for (int d = 0; d < P; ++d) acc += C[lds_at(lane, d)];
     rowsum[lane] = acc;
   } else if (wave == 1 && lane < P) {
     int64_t acc = 0;
-    for (int s2 = 0; s2 < P; ++s2) acc += C[s2 * P + lane];
+    for (int s2 = 0; s2 < P; ++s2) acc += C[lds_at(s2, lane)];
     colsum[lane] = acc;
   }
   __syncthreads();
@@ -192,17 +198,17 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     int64_t ex = 0;
     if (p.nblk == 1) {
       for (int d = 0; d < P; ++d) {
-        soff[s2 * P + d] = in0 + ex;
-        if (!dmajor) pre[s2 * P + d] = rb + ex;
-        ex += int64_t(C[s2 * P + d]) * p.elem;
+        soff[lds_at(s2, d)] = in0 + ex;
+        if (!dmajor) pre[lds_at(s2, d)] = rb + ex;
+        ex += int64_t(C[lds_at(s2, d)]) * p.elem;
       }
       p.ws.sstride[s2] = ex;
     } else {
       int64_t sub_ex = 0;
       for (int d = 0; d < P; ++d) {
-        const int32_t c = C[s2 * P + d];
-        soff[s2 * P + d] = in0 + sub_ex;
-        if (!dmajor) pre[s2 * P + d] = rb + ex;
+        const int32_t c = C[lds_at(s2, d)];
+        soff[lds_at(s2, d)] = in0 + sub_ex;
+        if (!dmajor) pre[lds_at(s2, d)] = rb + ex;
         ex += int64_t(c) * p.elem;
         sub_ex += int64_t(c / p.nblk) * p.elem;
       }
@@ -214,22 +220,24 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     const int64_t cb = colbase[d];
     int64_t ex = 0;
     for (int s2 = 0; s2 < P; ++s2) {
-      doff[s2 * P + d] = t0 + ex;
-      if (dmajor) pre[d * P + s2] = cb + ex;
-      ex += int64_t(C[s2 * P + d]) * p.elem;
+      doff[lds_at(s2, d)] = t0 + ex;
+      if (dmajor) pre[lds_at(d, s2)] = cb + ex;
+      ex += int64_t(C[lds_at(s2, d)]) * p.elem;
     }
   }
   __syncthreads();
   for (int i = tid; i < PP; i += kCountThreads) {
-    // Segment s -> d sits at index k = s*P + d of soff and doff.
-    const int k = dmajor ? (i - (i / P) * P) * P + i / P : i;
-    p.ws.src_off[i] = soff[k];
-    p.ws.prefix[i] = pre[i];
-    p.ws.dst_off[i] = doff[k];
-    // recv_counts[d][s] = send_counts[s][d].
-    const int d = i / P;
-    const int s2 = i - d * P;
-    p.recv_counts[i] = C[s2 * P + d];
+    // Flattened segment i is s -> d: i = d*P + s (destination-major) or
+    // s*P + d (source-major); pre holds it at lds_at(d, s) or lds_at(s, d).
+    const int hi = i / P;
+    const int lo = i - hi * P;
+    const int s2 = dmajor ? lo : hi;
+    const int d = dmajor ? hi : lo;
+    p.ws.src_off[i] = soff[lds_at(s2, d)];
+    p.ws.prefix[i] = pre[lds_at(hi, lo)];
+    p.ws.dst_off[i] = doff[lds_at(s2, d)];
+    // recv_counts[d'][s'] = send_counts[s'][d'] with i = d'*P + s'.
+    p.recv_counts[i] = C[lds_at(lo, hi)];
   }
   for (int b = tid; b < p.B; b += kCountThreads) p.ws.blk_cnt[b] = 0u;
   if (tid == 0) {
