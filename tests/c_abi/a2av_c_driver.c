@@ -1,7 +1,8 @@
 /*
  * a2av_c_driver.c -- test program: the library's C ABI driven from C alone.
  *
- * For a few seeded exchanges (plain FP32 and INT8, chunked, blocked, indexed)
+ * For a few seeded exchanges (plain FP32 and INT8, chunked, blocked, BF16 and
+ * FP16 with the bias Add, indexed)
  * it allocates the five operands with hipMalloc, calls a2av_create, two runs
  * of the entry point on a stream of its own, a2av_query_error and
  * a2av_destroy, then runs the CPU oracle twice on host copies of the same
@@ -27,6 +28,10 @@ int a2av_oracle_run_blocked(const void *input, void *target, int32_t *signal,
                             const int32_t *send_counts, int32_t *recv_counts, int32_t P,
                             int32_t S, int64_t in_slab, int64_t tgt_slab, int64_t core_num,
                             int32_t dtype, int64_t capacity, int32_t nblk);
+int a2av_oracle_run_bias(const void *input, void *target, int32_t *signal,
+                         const int32_t *send_counts, int32_t *recv_counts, int32_t P, int32_t S,
+                         int64_t in_slab, int64_t tgt_slab, int64_t core_num, int32_t dtype,
+                         int64_t capacity, int32_t nblk, const void *bias, int32_t hidden);
 int a2av_oracle_run_indexed(const void *input, void *target, int32_t *signal,
                             const int32_t *send_counts, int32_t *recv_counts,
                             const int32_t *index, int32_t P, int32_t S, int64_t in_slab,
@@ -52,7 +57,7 @@ static uint64_t next_u64(void)
     return z ^ (z >> 31);
 }
 
-enum { PLAIN = 0, BLOCKED = 1, INDEXED = 2 };
+enum { PLAIN = 0, BLOCKED = 1, INDEXED = 2, BIAS = 3 };
 
 typedef struct {
     const char *name;
@@ -61,25 +66,41 @@ typedef struct {
     int32_t dtype;
     int64_t core_num;
     int32_t max_units; /* a count is 0..max_units units */
-    int32_t unit;      /* elements per unit: nblk (blocked), row_elems (indexed), else 1 */
+    int32_t unit;      /* elements per unit: nblk (blocked), row_elems (indexed),
+                          nblk * hidden (bias), else 1 */
     int64_t chunk;     /* chunk_limit_bytes, 0 = default */
+    int32_t nblk;      /* bias: sub-blocks per segment */
+    int32_t hidden;    /* bias: row length */
 } Case;
 
 static const Case kCases[] = {
-    {"plain_fp32_cooperative", PLAIN, 8, A2AV_FP32, 64, 3000, 1, 0},
-    {"plain_int8_one_block", PLAIN, 4, A2AV_INT8, 1, 9000, 1, 0},
-    {"plain_int8_chunked", PLAIN, 5, A2AV_INT8, 10, 40000, 1, 65536},
-    {"plain_fp32_p64", PLAIN, 64, A2AV_FP32, 256, 300, 1, 0},
-    {"blocked_fp32_nblk4", BLOCKED, 8, A2AV_FP32, 16, 300, 4, 0},
-    {"indexed_int8_rows448", INDEXED, 8, A2AV_INT8, 64, 12, 448, 0},
+    {"plain_fp32_cooperative", PLAIN, 8, A2AV_FP32, 64, 3000, 1, 0, 0, 0},
+    {"plain_int8_one_block", PLAIN, 4, A2AV_INT8, 1, 9000, 1, 0, 0, 0},
+    {"plain_int8_chunked", PLAIN, 5, A2AV_INT8, 10, 40000, 1, 65536, 0, 0},
+    {"plain_fp32_p64", PLAIN, 64, A2AV_FP32, 256, 300, 1, 0, 0, 0},
+    {"blocked_fp32_nblk4", BLOCKED, 8, A2AV_FP32, 16, 300, 4, 0, 0, 0},
+    {"indexed_int8_rows448", INDEXED, 8, A2AV_INT8, 64, 12, 448, 0, 0, 0},
+    {"bias_bf16_nblk2_h64", BIAS, 8, A2AV_BF16, 16, 10, 2 * 64, 0, 2, 64},
+    {"bias_fp16_nblk3_h24_chunked", BIAS, 5, A2AV_FP16, 5, 12, 3 * 24, 1024, 3, 24},
 };
+
+/* A finite 16-bit value: random sign and mantissa, exponent kept well inside
+ * the type's range (no NaN, infinity or overflow in the sums). */
+static uint16_t finite16(int32_t dtype)
+{
+    const uint64_t r = next_u64();
+    const uint16_t sign = (uint16_t)((r >> 20) & 1u) << 15;
+    if (dtype == A2AV_BF16)
+        return (uint16_t)(sign | (uint16_t)((100 + r % 55) << 7) | (uint16_t)((r >> 8) & 0x7Fu));
+    return (uint16_t)(sign | (uint16_t)((5 + r % 20) << 10) | (uint16_t)((r >> 8) & 0x3FFu));
+}
 
 static int64_t round16(int64_t x) { return (x + 15) / 16 * 16; }
 
 static int run_case(const Case *c, uint64_t seed)
 {
     const int32_t P = c->P;
-    const int64_t e = c->dtype == A2AV_FP32 ? 4 : 1;
+    const int64_t e = c->dtype == A2AV_FP32 ? 4 : c->dtype == A2AV_INT8 ? 1 : 2;
     rng = seed;
 
     int32_t *counts = malloc(sizeof(int32_t) * (size_t)(P * P));
@@ -113,30 +134,51 @@ static int run_case(const Case *c, uint64_t seed)
     const size_t sig_bytes = sizeof(int32_t) * (size_t)P * (size_t)S;
     const size_t cnt_bytes = sizeof(int32_t) * (size_t)(P * P);
     const size_t idx_bytes = sizeof(int32_t) * (size_t)(P * (stride > 0 ? stride : 1));
+    const size_t nbias = c->kind == BIAS ? (size_t)P * (size_t)c->nblk * (size_t)c->hidden : 1;
+    const size_t bias_bytes = nbias * (c->dtype == A2AV_BF16 ? 4u : 2u);
     uint8_t *h_in = malloc(in_bytes), *h_tgt = malloc(tgt_bytes), *o_tgt = malloc(tgt_bytes);
     int32_t *h_sig = calloc((size_t)P * (size_t)S, sizeof(int32_t));
     int32_t *o_sig = calloc((size_t)P * (size_t)S, sizeof(int32_t));
     int32_t *h_recv = malloc(cnt_bytes), *o_recv = malloc(cnt_bytes);
     int32_t *h_idx = malloc(idx_bytes);
-    for (size_t i = 0; i < in_bytes; ++i) h_in[i] = (uint8_t)next_u64();
+    if (c->kind == BIAS) {
+        for (size_t i = 0; i + 1 < in_bytes; i += 2) {
+            const uint16_t v = finite16(c->dtype);
+            memcpy(h_in + i, &v, 2);
+        }
+    } else {
+        for (size_t i = 0; i < in_bytes; ++i) h_in[i] = (uint8_t)next_u64();
+    }
+    uint8_t *h_bias = malloc(bias_bytes);
+    for (size_t i = 0; i < nbias && c->kind == BIAS; ++i) {
+        if (c->dtype == A2AV_BF16) {
+            const float b = (float)((int64_t)(next_u64() % 64000u) - 32000) / 1000.0f;
+            memcpy(h_bias + 4 * i, &b, 4);
+        } else {
+            const uint16_t b = finite16(A2AV_FP16);
+            memcpy(h_bias + 2 * i, &b, 2);
+        }
+    }
     memset(o_tgt, 0xA5, tgt_bytes);
     for (int32_t i = 0; i < P * P; ++i) o_recv[i] = -7;
     for (int64_t i = 0; i < P * (stride > 0 ? stride : 1); ++i)
         h_idx[i] = table_rows > 0 ? (int32_t)(next_u64() % (uint64_t)table_rows) : 0;
 
-    void *d_in, *d_tgt, *d_sig, *d_send, *d_recv, *d_idx;
+    void *d_in, *d_tgt, *d_sig, *d_send, *d_recv, *d_idx, *d_bias;
     HIP_OK(hipMalloc(&d_in, in_bytes));
     HIP_OK(hipMalloc(&d_tgt, tgt_bytes));
     HIP_OK(hipMalloc(&d_sig, sig_bytes));
     HIP_OK(hipMalloc(&d_send, cnt_bytes));
     HIP_OK(hipMalloc(&d_recv, cnt_bytes));
     HIP_OK(hipMalloc(&d_idx, idx_bytes));
+    HIP_OK(hipMalloc(&d_bias, bias_bytes));
     HIP_OK(hipMemcpy(d_in, h_in, in_bytes, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(d_tgt, o_tgt, tgt_bytes, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(d_sig, o_sig, sig_bytes, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(d_send, counts, cnt_bytes, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(d_recv, o_recv, cnt_bytes, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(d_idx, h_idx, idx_bytes, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(d_bias, h_bias, bias_bytes, hipMemcpyHostToDevice));
 
     a2av_config cfg;
     memset(&cfg, 0, sizeof(cfg));
@@ -162,6 +204,9 @@ static int run_case(const Case *c, uint64_t seed)
         else if (c->kind == BLOCKED)
             gpu_st = a2av_run_blocked(h, d_in, d_tgt, d_sig, d_send, d_recv, P, c->core_num,
                                       c->dtype, c->unit, stream);
+        else if (c->kind == BIAS)
+            gpu_st = a2av_run_bias(h, d_in, d_tgt, d_sig, d_send, d_recv, d_bias, P, c->core_num,
+                                   c->dtype, c->nblk, c->hidden, stream);
         else
             gpu_st = a2av_run_indexed(h, d_in, d_tgt, d_sig, d_send, d_recv, d_idx, P,
                                       c->core_num, c->dtype, c->unit, stride, stream);
@@ -185,6 +230,10 @@ static int run_case(const Case *c, uint64_t seed)
         else if (c->kind == BLOCKED)
             o_st = a2av_oracle_run_blocked(h_in, o_tgt, o_sig, counts, o_recv, P, S, in_slab,
                                            tgt_slab, c->core_num, c->dtype, 0, c->unit);
+        else if (c->kind == BIAS)
+            o_st = a2av_oracle_run_bias(h_in, o_tgt, o_sig, counts, o_recv, P, S, in_slab,
+                                        tgt_slab, c->core_num, c->dtype, 0, c->nblk, h_bias,
+                                        c->hidden);
         else
             o_st = a2av_oracle_run_indexed(h_in, o_tgt, o_sig, counts, o_recv, h_idx, P, S,
                                            in_slab, tgt_slab, c->core_num, c->dtype, 0, c->unit,
@@ -192,6 +241,11 @@ static int run_case(const Case *c, uint64_t seed)
     }
 
     int ok = 1;
+    if (gpu_st != A2AV_OK) {  /* every case is a valid exchange */
+        fprintf(stderr, "%s: status %d (%s), expected A2AV_OK\n", c->name, gpu_st,
+                a2av_status_string(gpu_st));
+        ok = 0;
+    }
     if (gpu_st != o_st) {
         fprintf(stderr, "%s: status %d, oracle %d\n", c->name, gpu_st, o_st);
         ok = 0;
@@ -220,6 +274,7 @@ static int run_case(const Case *c, uint64_t seed)
     HIP_OK(hipFree(d_send));
     HIP_OK(hipFree(d_recv));
     HIP_OK(hipFree(d_idx));
+    HIP_OK(hipFree(d_bias));
     free(counts);
     free(h_in);
     free(h_tgt);
@@ -229,6 +284,7 @@ static int run_case(const Case *c, uint64_t seed)
     free(h_recv);
     free(o_recv);
     free(h_idx);
+    free(h_bias);
     return ok;
 }
 

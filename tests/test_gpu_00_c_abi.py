@@ -1,8 +1,9 @@
 """The library's C ABI driven from a C program: tests/c_abi/a2av_c_driver.c
 allocates the operands with hipMalloc, runs plain (FP32 and INT8, one block,
-cooperative, chunked, P = 64), blocked and indexed exchanges twice each on a
-stream of its own, and compares target, signal and recv_counts byte for byte
-with the C oracle.  The driver is built with the library; it runs here as a
+cooperative, chunked, P = 64), blocked, bias (BF16 with an FP32 bias, FP16
+with an FP16 bias, chunked) and indexed exchanges twice each on a stream of
+its own, and compares target, signal and recv_counts byte for byte with the C
+oracle.  The driver is built with the library; it runs here as a
 child process.
 
 On ROCm, once a process has made a cooperative launch, another process's
