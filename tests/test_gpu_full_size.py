@@ -63,6 +63,23 @@ def test_p64_against_oracle():
         ex.close()
 
 
+@pytest.mark.parametrize("seed", [41, 42])
+def test_c4_shape_other_counts_against_oracle(seed):
+    # c4's shape (P = 32 FP32, counts uniform in [0, 2^19] with 205 of 1024
+    # zeroed, 64 MiB slabs, B = 256) with other count matrices and payloads.
+    rng = np.random.default_rng(seed)
+    C = wl.uniform_counts(rng, 32, 1 << 19, 205 / 1024)
+    w = wl.custom(32, wl.FP32, C, core_num=256, S=256, in_slab=64 << 20, tgt_slab=64 << 20,
+                  seed=seed)
+    say("c4 shape, seed", seed, w.payload_bytes)
+    c = Case(w, host_input=False)
+    ex = exchange_for(w)
+    try:
+        c.assert_matches(c.run_gpu(ex), c.run_oracle())
+    finally:
+        ex.close()
+
+
 def test_c4_with_small_chunks_against_oracle():
     # The chunked path the c4 text intends: 256 MiB per launch (about 4 launches).
     w = wl.workload(4)

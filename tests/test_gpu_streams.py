@@ -1,0 +1,58 @@
+"""Two handles on two streams at once: each handle owns its workspace, so
+exchanges enqueued alternately on two torch streams (no ordering between
+them) must each match the oracle.  B = 1 on both (regular launches, no
+cooperative residency needed), several runs each, different shapes and
+dtypes; the signal of each counts its own runs."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from all_movement_amd import workloads as wl  # noqa: E402
+from tests.gpu_harness import Case, exchange_for, say  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _gpu_or_skip():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _workload(P, dtype, hi, seed):
+    rng = np.random.default_rng(seed)
+    C = wl.uniform_counts(rng, P, hi, 0.2)
+    return wl.custom(P, dtype, C, core_num=1, S=1, seed=seed)
+
+
+@pytest.mark.parametrize("runs", [1, 4])
+def test_two_handles_on_two_streams(runs):
+    w1 = _workload(8, wl.FP32, 1 << 16, 21)      # ~10 MiB, 4-byte ragged
+    w2 = _workload(5, wl.INT8, 1 << 20, 22)      # ~10 MiB, odd byte phases
+    say("streams", runs, w1.payload_bytes, w2.payload_bytes)
+    c1, c2 = Case(w1), Case(w2)
+    e1, e2 = exchange_for(w1), exchange_for(w2)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    try:
+        torch.cuda.synchronize()
+        for _ in range(runs):
+            with torch.cuda.stream(s1):
+                e1.run(c1.input, c1.target, c1.signal, c1.send, c1.recv, w1.core_num, w1.dtype)
+            with torch.cuda.stream(s2):
+                e2.run(c2.input, c2.target, c2.signal, c2.send, c2.recv, w2.core_num, w2.dtype)
+        torch.cuda.synchronize()
+        for c, e in ((c1, e1), (c2, e2)):
+            st = e.query_error()
+            exp = None
+            for _ in range(runs):
+                exp = c.run_oracle()
+                c.signal_np0 = exp[2].copy()
+            c.assert_matches(st, exp)
+    finally:
+        torch.cuda.synchronize()
+        e1.close()
+        e2.close()
