@@ -964,9 +964,22 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   RunPlan* plan = p.ws.plan;
-  // The flag and the payload size are loaded together (one round trip).
+  const int nseg = p.nseg;
+  auto stage_tables = [&]() {
+    for (int i = tid; i <= nseg; i += NT) tab.prefix[i] = p.ws.prefix[i];
+    for (int i = tid; i < nseg; i += NT) {
+      tab.src[i] = p.ws.src_off[i];
+      tab.dst[i] = p.ws.dst_off[i];
+    }
+    if (tid < p.P) tab.sstride[tid] = p.ws.sstride[tid];
+  };
+  // The flag and the payload size are loaded together (one round trip).  The
+  // final launch has payload whenever the run has any, so it stages the
+  // segment tables in the same round trip; earlier launches first learn
+  // whether their chunk holds payload.
   const int valid = plan->valid;
   const int64_t T = plan->total_bytes;
+  if (p.last) stage_tables();
   if (valid == 0) return;  // the run failed its device checks: write nothing
 
   // Launch c claims tiles on plan->claim[c & 1]; the launch before it in the
@@ -981,13 +994,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   // A chunk past the run's payload has nothing to copy (the final launch
   // still arrives, even with no payload).
   if (c_lo >= c_hi && !p.last) return;
-  const int nseg = p.nseg;
-  for (int i = tid; i <= nseg; i += NT) tab.prefix[i] = p.ws.prefix[i];
-  for (int i = tid; i < nseg; i += NT) {
-    tab.src[i] = p.ws.src_off[i];
-    tab.dst[i] = p.ws.dst_off[i];
-  }
-  if (tid < p.P) tab.sstride[tid] = p.ws.sstride[tid];
+  if (!p.last) stage_tables();
   __syncthreads();
 
   // Tile size: at most kTileBytes, chosen so W workgroups take the same number
