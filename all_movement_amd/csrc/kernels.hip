@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     for (int s2 = 0; s2 < P; ++s2) {
       const int64_t rows = rowsum[s2] / unit;
       const int32_t* list = p.index + int64_t(s2) * p.index_stride;
-#pragma unroll 4
+#pragma unroll 8
       for (int64_t k = tid; k < rows; k += kCountThreads)
         bad_row |= uint32_t(list[k]) >= limit ? 16 : 0;
     }
