@@ -13,10 +13,18 @@ struct alignas(64) RunPlan {
   int32_t valid;        // 1 when the run's counts and signal passed the device checks
   int32_t base_signal;  // common value of signal[r][b] (r < P, b < B) at entry
   int64_t total_bytes;  // payload bytes T of the run
-  uint32_t arrived;     // admitted blocks that have raised their flags
   int32_t error;        // latched status (first failure since the last query)
   uint32_t claim[2];    // dynamic tile counters; K2 launch c uses claim[c & 1]
 };
+
+// The arrival counter of the final launch is kept in kArriveReplicas copies,
+// kArriveStride words (256 bytes) apart: every arriving block adds 1 to each
+// copy (one lane per copy) and workgroup w polls copy w % kArriveReplicas.
+// With a single counter the polls of the waiting workgroups all landed on one
+// memory channel and slowed the copies still running (gfx950, c4's 256-block
+// launch: 324 -> 308 us).
+constexpr int kArriveReplicas = 64;
+constexpr int kArriveStride = 64;
 
 // Device workspace layout, carved out of one allocation by the host.
 struct Workspace {
@@ -27,6 +35,8 @@ struct Workspace {
   int64_t* dst_off;  // [P*P] byte offset inside `target` of each segment, flattened order
   uint32_t* blk_cnt; // [max blocks] workgroups of each block that finished copying
   int64_t* sstride;  // [P] bytes per source block-row (blocked exchange)
+  uint32_t* arrived; // [kArriveReplicas * kArriveStride] admitted blocks that have raised
+                     // their flags, copy k at arrived[k * kArriveStride]
 };
 
 struct CountParams {

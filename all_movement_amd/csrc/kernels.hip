@@ -25,7 +25,7 @@
 // the indexed exchange.  On the run's final launch every admitted block
 // raises its flag in every rank's signal row, and when B > 1 (a cooperative
 // launch) every workgroup waits, with a bounded spin, until all B blocks have
-// arrived.  The block/flag protocol is the block-aware exchange barrier of
+// arrived (polling one of several copies of the arrival counter).  The block/flag protocol is the block-aware exchange barrier of
 // the PyPTO "LowerL2TensorCollectives Pass" page ("Launch width": all
 // admitted blocks co-resident; a refused launch rather than a partial one)
 // with per-peer sequence counters as in the start barrier of the "vccl
@@ -241,11 +241,11 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     p.recv_counts[i] = C[lds_at(lo, hi)];
   }
   for (int b = tid; b < p.B; b += kCountThreads) p.ws.blk_cnt[b] = 0u;
+  if (tid < kArriveReplicas) p.ws.arrived[int64_t(tid) * kArriveStride] = 0u;
   if (tid == 0) {
     p.ws.prefix[PP] = rowbase[kMaxP];
     p.ws.plan->total_bytes = rowbase[kMaxP];
     p.ws.plan->base_signal = base;
-    p.ws.plan->arrived = 0u;
     p.ws.plan->claim[0] = 0u;
     p.ws.plan->claim[1] = 0u;
     p.ws.plan->valid = 1;
@@ -1074,27 +1074,33 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   // and the barrier keep the compiler from hoisting the atomics above it.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (tid == 0) {
+  if (wave == 0) {
     const int b = int(blockIdx.x) / p.G;
     // A block of one workgroup needs no count (and saves its round trip).
-    const uint32_t done =
-        p.G == 1 ? 0u
-                 : __hip_atomic_fetch_add(&p.ws.blk_cnt[b], 1u, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t done = 0u;
+    if (lane == 0 && p.G != 1)
+      done = __hip_atomic_fetch_add(&p.ws.blk_cnt[b], 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    done = __builtin_amdgcn_readfirstlane(done);
     if (done == uint32_t(p.G - 1)) {
-      for (int r = 0; r < p.P; ++r)
+      // One lane per rank raises the flags, one lane per copy counts the
+      // block, each a single wave-wide atomic.
+      for (int r = lane; r < p.P; r += kWave)
         __hip_atomic_fetch_add(&p.signal[int64_t(r) * p.S + b], 1, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&plan->arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int k = lane; k < kArriveReplicas; k += kWave)
+        __hip_atomic_fetch_add(&p.ws.arrived[int64_t(k) * kArriveStride], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (p.wait) {
+    if (p.wait && lane == 0) {
       // All admitted blocks are co-resident (cooperative launch); wait until
       // every one has arrived.  Polls are relaxed device-scope loads (no
       // cache invalidation per poll); nothing is read after the wait.  The
       // wait is bounded: a lost arrival latches TIMEOUT instead of hanging.
+      const uint32_t* mine =
+          p.ws.arrived + int64_t(blockIdx.x % kArriveReplicas) * kArriveStride;
       int spins = 0;
-      while (__hip_atomic_load(&plan->arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-             uint32_t(p.B)) {
+      while (__hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < uint32_t(p.B)) {
         if (++spins > p.spin_limit) {
           int expected = 0;
           __hip_atomic_compare_exchange_strong(&plan->error, &expected, int(A2AV_ERR_TIMEOUT),

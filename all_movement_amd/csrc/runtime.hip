@@ -155,7 +155,8 @@ int a2av_create(a2av_handle** out, const a2av_config* cfg) {
   h->spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
 
   // Workspace: plan words, prefix[P*P+1], src_off[P*P], dst_off[P*P],
-  // blk_cnt[max(1, capacity)], sstride[P], each 256-byte aligned.
+  // blk_cnt[max(1, capacity)], sstride[P], the arrival counter copies, each
+  // 256-byte aligned.
   const size_t PP = size_t(cfg->P) * size_t(cfg->P);
   const size_t max_blocks = size_t(h->capacity > 1 ? h->capacity : 1);
   size_t off = 0;
@@ -165,6 +166,8 @@ int a2av_create(a2av_handle** out, const a2av_config* cfg) {
   const size_t o_dst = off; off = round_up(off + PP * sizeof(int64_t), 256);
   const size_t o_cnt = off; off = round_up(off + max_blocks * sizeof(uint32_t), 256);
   const size_t o_str = off; off = round_up(off + size_t(cfg->P) * sizeof(int64_t), 256);
+  const size_t o_arr = off;
+  off = round_up(off + size_t(a2av::kArriveReplicas) * a2av::kArriveStride * sizeof(uint32_t), 256);
   e = hipMalloc(&h->ws_mem, off);
   if (e != hipSuccess) { delete h; return A2AV_ERR_HIP; }
   e = hipMemset(h->ws_mem, 0, off);
@@ -176,6 +179,7 @@ int a2av_create(a2av_handle** out, const a2av_config* cfg) {
   h->ws.dst_off = reinterpret_cast<int64_t*>(base + o_dst);
   h->ws.blk_cnt = reinterpret_cast<uint32_t*>(base + o_cnt);
   h->ws.sstride = reinterpret_cast<int64_t*>(base + o_str);
+  h->ws.arrived = reinterpret_cast<uint32_t*>(base + o_arr);
 
   h->profile = (cfg->flags & A2AV_FLAG_PROFILE) != 0;
   if (h->profile) {
