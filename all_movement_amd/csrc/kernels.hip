@@ -1008,12 +1008,10 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   // to workgroup t mod W.  The rest go to whichever workgroup asks first, so
   // workgroups that stream slower take fewer tiles and the launch ends when
   // the last tile does, not when the slowest workgroup's share does
-  // (measured on gfx950: c5 5.79 -> 6.11 TB/s in-kernel, c3 5.25 -> 5.75).
-  // The row gather keeps the static deal: its tiles start with a dependent
-  // list load, and the two workgroup barriers per claimed tile cost it more
-  // than the balance gains (4.88 -> 4.70 TB/s).  With 16-byte rows it runs
-  // software-pipelined over the static tiles (gather_static).
-  const int64_t rounds_static = MODE == 3 ? rounds : (rounds + 3) / 4;
+  // (measured on gfx950: c5 5.79 -> 6.11 TB/s in-kernel, c3 5.25 -> 5.75,
+  // the row gather 186 -> 179 us on c3i).  With 16-byte rows the row gather
+  // runs software-pipelined over its static tiles (gather_static).
+  const int64_t rounds_static = (rounds + 3) / 4;
   const int64_t nstatic = W * rounds_static < ntiles ? W * rounds_static : ntiles;
 
   int small = 0;  // small pieces met so far (see wg_copy_piece)
