@@ -8,7 +8,7 @@
 // and the prefix of the flattened payload that K2 partitions.
 //
 // K2 (copy_kernel, W = B * G workgroups): the flattened payload is cut into
-// tiles of at most 128 KiB; the first quarter is dealt round-robin to the
+// tiles of at most 128 KiB; the first eighth is dealt round-robin to the
 // workgroups, the rest are claimed from a counter.  Inside a segment the copy
 // is destination-aligned: 128-bit streaming buffer loads and device-scope
 // streaming buffer stores in the body, numbered from the destination's
@@ -1004,14 +1004,15 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   const int64_t rounds = (len + W * kTileBytes - 1) / (W * kTileBytes);
   const int64_t tile = rounds > 0 ? ((len + W * rounds - 1) / (W * rounds) + 15) & ~int64_t(15) : 1;
   const int64_t ntiles = (len + tile - 1) / tile;
-  // The first quarter of the rounds (rounded up) is dealt statically: tile t
+  // The first eighth of the rounds (rounded up) is dealt statically: tile t
   // to workgroup t mod W.  The rest go to whichever workgroup asks first, so
   // workgroups that stream slower take fewer tiles and the launch ends when
   // the last tile does, not when the slowest workgroup's share does
   // (measured on gfx950: c5 5.79 -> 6.11 TB/s in-kernel, c3 5.25 -> 5.75,
-  // the row gather 186 -> 179 us on c3i).  With 16-byte rows the row gather
-  // runs software-pipelined over its static tiles (gather_static).
-  const int64_t rounds_static = (rounds + 3) / 4;
+  // the row gather 186 -> 179 us on c3i; an eighth static rather than a
+  // quarter, c5 -0.7 %, c5b -0.6 %).  With 16-byte rows the row gather runs
+  // software-pipelined over its static tiles (gather_static).
+  const int64_t rounds_static = (rounds + 7) / 8;
   const int64_t nstatic = W * rounds_static < ntiles ? W * rounds_static : ntiles;
 
   int small = 0;  // small pieces met so far (see wg_copy_piece)

@@ -1,10 +1,10 @@
-"""GPU parity of K2's claimed tiles: a launch deals the first quarter of its
+"""GPU parity of K2's claimed tiles: a launch deals the first eighth of its
 tile rounds statically and hands the rest out from a counter, two counters
 alternating between the launches of a run and reused by the next run.  These
 cases make every launch large enough to claim (more than one round of 128 KiB
 tiles per workgroup), with odd and even numbers of launches, several runs on
 one handle, several workgroups per block, and every body (plain, blocked,
-bias).  Bit-exact against the oracle after every run."""
+bias, row gather).  Bit-exact against the oracle after every run."""
 import numpy as np
 import pytest
 
@@ -107,3 +107,29 @@ def test_claimed_tiles_blocked_and_bias_bodies():
             cb.signal_np0 = exp[2].copy()
     finally:
         exb.close()
+
+
+@pytest.mark.parametrize("R,chunk_mib", [(1792, 0), (1792, 40), (1000, 40)])
+def test_claimed_tiles_row_gather_body(R, chunk_mib):
+    # int8 rows of R bytes gathered through the lists (1792: the 16-byte word
+    # path; 1000: whole rows through the byte-exact copy), about 4 rounds of
+    # tiles in one launch, or 1-2 rounds in each of several 40 MiB launches.
+    P, table_rows = 8, 4096
+    rng = np.random.default_rng(R + chunk_mib)
+    rows = rng.integers(800, 1600, size=(P, P))
+    C = (rows * R).astype(np.int32)
+    in_slab = (table_rows * R + 15) // 16 * 16
+    w = wl.custom(P, wl.INT8, C, core_num=64, S=64, in_slab=in_slab, seed=R)
+    stride = int(rows.sum(axis=1).max()) + 3
+    index = rng.integers(0, table_rows, size=(P, stride)).astype(np.int32)
+    c = Case(w)
+    ex = exchange_for(w, chunk_limit_bytes=chunk_mib * MiB)
+    try:
+        say("R", R, "payload", w.payload_bytes, "launches", ex.launch_info(w.core_num).chunk_launches)
+        for _ in range(2):
+            st = c.run_gpu(ex, index=upload(index), row_elems=R)
+            exp = c.run_oracle(index=index, row_elems=R)
+            c.assert_matches(st, exp)
+            c.signal_np0 = exp[2].copy()
+    finally:
+        ex.close()
