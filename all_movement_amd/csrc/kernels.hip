@@ -4,8 +4,9 @@
 // the signal on the device, writes recv_counts as the transpose of
 // send_counts, and derives every segment's source and target byte offsets
 // (exclusive prefixes along d on the send side and along s on the receive
-// side, one thread per row or column walking the LDS copy of the matrix),
-// and the prefix of the flattened payload that K2 partitions.
+// side, one wave scanning each row or column of the LDS copy of the matrix
+// with DPP lane moves), and the prefix of the flattened payload that K2
+// partitions.
 //
 // K2 (copy_kernel, W = B * G workgroups): the flattened payload is cut into
 // tiles of at most 128 KiB; the first eighth is dealt round-robin to the
@@ -64,13 +65,36 @@ constexpr int kStorePolicy = 2 | 16;
 constexpr int kPitch = kMaxP + 1;
 __device__ inline int lds_at(int r, int c) { return r * kPitch + c; }
 
+// v moved across lanes by one DPP pattern, each 32-bit half on its own;
+// lanes the pattern gives no source, or outside kRowMask, read 0.
+template <int kCtrl, int kRowMask>
+__device__ inline int64_t dpp_move(int64_t v) {
+  const uint64_t u = uint64_t(v);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(u)), kCtrl, kRowMask, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(u >> 32)), kCtrl, kRowMask, 0xf, false);
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+// Inclusive prefix sum of v over the 64 lanes of a wave (all lanes active):
+// shifts by 1, 2, 4 and 8 lanes within each row of 16 (row_shr), then the
+// last lane of row 0 (and of row 2) is added to row 1 (row 3) and the last
+// lane of row 1 to rows 2 and 3 (row_bcast:15, row_bcast:31).
+__device__ inline int64_t wave_inclusive_scan(int64_t v) {
+  v += dpp_move<0x111, 0xf>(v);
+  v += dpp_move<0x112, 0xf>(v);
+  v += dpp_move<0x114, 0xf>(v);
+  v += dpp_move<0x118, 0xf>(v);
+  v += dpp_move<0x142, 0xa>(v);
+  v += dpp_move<0x143, 0xc>(v);
+  return v;
+}
+
 __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   __shared__ int32_t C[kMaxP * kPitch];     // C[lds_at(s, d)] = send_counts[s][d]
   __shared__ int64_t soff[kMaxP * kPitch];  // staged outputs, written back coalesced
   __shared__ int64_t pre[kMaxP * kPitch];
   __shared__ int64_t doff[kMaxP * kPitch];
   __shared__ int64_t rowsum[kMaxP];        // elements each source sends
-  __shared__ int64_t colsum[kMaxP];        // elements each destination receives
   __shared__ int64_t rowbase[kMaxP + 1];   // bytes before source s (s-major order)
   __shared__ int64_t colbase[kMaxP];       // bytes before destination d (d-major order)
   __shared__ int flags;
@@ -108,37 +132,35 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   __syncthreads();
 
   // Row sums (what each source sends) in wave 0 and column sums (what each
-  // destination receives) in wave 1: one thread walks its row or column of
-  // the LDS matrix (at most 64 entries; cheaper than a cross-lane scan).
-  if (wave == 0 && lane < P) {
+  // destination receives) in wave 1: lane s (or d) walks its row (column) of
+  // the LDS matrix, then the wave scans the byte totals across its lanes into
+  // the row bases, the exclusive prefix of the row totals (rowbase[kMaxP] =
+  // T), and the column bases, that of the column totals.  Lanes at or past P
+  // add nothing.  Then the capacity checks: a source overflows its input
+  // slab or, in the indexed exchange, sends more rows than its gather list
+  // holds; a destination overflows its target slab.
+  if (wave < 2) {
     int64_t acc = 0;
-    for (int d = 0; d < P; ++d) acc += C[lds_at(lane, d)];
-    rowsum[lane] = acc;
-  } else if (wave == 1 && lane < P) {
-    int64_t acc = 0;
-    for (int s2 = 0; s2 < P; ++s2) acc += C[lds_at(s2, lane)];
-    colsum[lane] = acc;
-  }
-  __syncthreads();
-  if (tid < P) {
-    // A source overflows its input slab, or, in the indexed exchange, sends
-    // more rows than its gather list holds.
-    const bool src_over = p.index != nullptr ? rowsum[tid] / unit > p.index_stride
-                                             : rowsum[tid] * p.elem > p.in_slab;
-    if (src_over || colsum[tid] * p.elem > p.tgt_slab) atomicOr(&flags, 2);
-  } else if (tid == kWave) {
-    // Row bases, the exclusive prefix of the row byte totals (rowbase[kMaxP]
-    // = T), and column bases, that of the column byte totals.
-    int64_t acc = 0;
-    for (int s2 = 0; s2 < P; ++s2) {
-      rowbase[s2] = acc;
-      acc += rowsum[s2] * p.elem;
+    if (lane < P) {
+      if (wave == 0) {
+        for (int d = 0; d < P; ++d) acc += C[lds_at(lane, d)];
+      } else {
+        for (int s2 = 0; s2 < P; ++s2) acc += C[lds_at(s2, lane)];
+      }
     }
-    rowbase[kMaxP] = acc;
-    acc = 0;
-    for (int d = 0; d < P; ++d) {
-      colbase[d] = acc;
-      acc += colsum[d] * p.elem;
+    const int64_t bytes = acc * p.elem;
+    const int64_t incl = wave_inclusive_scan(bytes);
+    if (wave == 0) {
+      if (lane < P) {
+        rowsum[lane] = acc;
+        rowbase[lane] = incl - bytes;
+        if (p.index != nullptr ? acc / unit > p.index_stride : bytes > p.in_slab)
+          atomicOr(&flags, 2);
+      }
+      if (lane == kWave - 1) rowbase[kMaxP] = incl;
+    } else if (lane < P) {
+      colbase[lane] = incl - bytes;
+      if (bytes > p.tgt_slab) atomicOr(&flags, 2);
     }
   }
   __syncthreads();
@@ -185,45 +207,35 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   // faster for it.
   const bool dmajor = p.index == nullptr;
 
-  // Send side (wave 0, one thread per source): the exclusive prefix along d
-  // (input packed by destination); the source offset is the prefix of the
-  // sub-block sizes (the segment's sub-block in block-row 0; block-rows are
-  // sstride[s] bytes apart; nblk = 1 is the plain exchange).  Receive side
-  // (wave 1, one thread per destination): the exclusive prefix along s
-  // (target packed by source).  Each side writes the flattened prefix in
-  // its own order.
-  if (wave == 0 && lane < P) {
-    const int s2 = lane;
-    const int64_t in0 = int64_t(s2) * p.in_slab;
-    const int64_t rb = rowbase[s2];
-    int64_t ex = 0;
-    if (p.nblk == 1) {
-      for (int d = 0; d < P; ++d) {
-        soff[lds_at(s2, d)] = in0 + ex;
-        if (!dmajor) pre[lds_at(s2, d)] = rb + ex;
-        ex += int64_t(C[lds_at(s2, d)]) * p.elem;
-      }
-      p.ws.sstride[s2] = ex;
-    } else {
-      int64_t sub_ex = 0;
-      for (int d = 0; d < P; ++d) {
-        const int32_t c = C[lds_at(s2, d)];
-        soff[lds_at(s2, d)] = in0 + sub_ex;
-        if (!dmajor) pre[lds_at(s2, d)] = rb + ex;
-        ex += int64_t(c) * p.elem;
-        sub_ex += int64_t(c / p.nblk) * p.elem;
-      }
-      p.ws.sstride[s2] = sub_ex;
+  // Send side, one wave per source row s (lane d): the exclusive prefix
+  // along d of the row's bytes (input packed by destination) gives the
+  // source offsets; with nblk > 1 the source offset is instead the prefix of
+  // the sub-block sizes (the segment's sub-block in block-row 0; block-rows
+  // are sstride[s] bytes apart).  Receive side, one wave per destination
+  // column d (lane s): the exclusive prefix along s (target packed by
+  // source).  Each side writes the flattened prefix in its own order.
+  for (int s2 = wave; s2 < P; s2 += kWaves) {
+    const int32_t c = lane < P ? C[lds_at(s2, lane)] : 0;
+    const int64_t v = int64_t(c) * p.elem;
+    const int64_t ex = wave_inclusive_scan(v) - v;
+    int64_t sv = v;
+    int64_t sex = ex;
+    if (p.nblk != 1) {
+      sv = int64_t(c / p.nblk) * p.elem;
+      sex = wave_inclusive_scan(sv) - sv;
     }
-  } else if (wave == 1 && lane < P) {
-    const int d = lane;
-    const int64_t t0 = int64_t(d) * p.tgt_slab;
-    const int64_t cb = colbase[d];
-    int64_t ex = 0;
-    for (int s2 = 0; s2 < P; ++s2) {
-      doff[lds_at(s2, d)] = t0 + ex;
-      if (dmajor) pre[lds_at(d, s2)] = cb + ex;
-      ex += int64_t(C[lds_at(s2, d)]) * p.elem;
+    if (lane < P) {
+      soff[lds_at(s2, lane)] = int64_t(s2) * p.in_slab + sex;
+      if (!dmajor) pre[lds_at(s2, lane)] = rowbase[s2] + ex;
+    }
+    if (lane == P - 1) p.ws.sstride[s2] = sex + sv;
+  }
+  for (int d = wave; d < P; d += kWaves) {
+    const int64_t v = lane < P ? int64_t(C[lds_at(lane, d)]) * p.elem : 0;
+    const int64_t ex = wave_inclusive_scan(v) - v;
+    if (lane < P) {
+      doff[lds_at(lane, d)] = int64_t(d) * p.tgt_slab + ex;
+      if (dmajor) pre[lds_at(d, lane)] = colbase[d] + ex;
     }
   }
   __syncthreads();
