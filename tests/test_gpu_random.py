@@ -16,7 +16,7 @@ from all_movement_amd import a2av  # noqa: E402
 from all_movement_amd import workloads as wl  # noqa: E402
 from tests.gpu_harness import DEV, Case, exchange_for, say, upload  # noqa: E402
 
-N_CASES = 200
+N_CASES = 400
 
 
 @pytest.fixture(autouse=True)
