@@ -10,27 +10,28 @@
 //
 // K2 (copy_kernel, W = B * G workgroups): the flattened payload is cut into
 // tiles of at most 128 KiB; the first eighth is dealt round-robin to the
-// workgroups, the rest are claimed from a counter.  Inside a segment the copy
-// is destination-aligned: 128-bit streaming buffer loads and device-scope
-// streaming buffer stores in the body, numbered from the destination's
-// 128-byte line so every wave store writes whole lines, and byte stores for
-// the at most 15 bytes at either end, so no byte outside a segment is ever
-// written.  When source and destination differ by an odd number of bytes
-// mod 4 the body is realigned through LDS: each wave stages a row of 64
-// aligned source words, then every lane funnels its word and its right
-// neighbour's with v_alignbyte; a whole number of dwords apart, the source is
-// read directly with dword-aligned 16-byte loads.  Pieces of at most 8 KiB are copied by one wave each, dealt to
-// the waves in turn, so a tile of many small segments costs about one memory
-// round trip instead of one per segment.  Separate instantiations add the
-// bias (BF16 with an FP32 bias, FP16 with an FP16 bias) or gather the rows of
-// the indexed exchange.  On the run's final launch every admitted block
-// raises its flag in every rank's signal row, and when B > 1 (a cooperative
-// launch) every workgroup waits, with a bounded spin, until all B blocks have
-// arrived (polling one of several copies of the arrival counter).  The block/flag protocol is the block-aware exchange barrier of
-// the PyPTO "LowerL2TensorCollectives Pass" page ("Launch width": all
-// admitted blocks co-resident; a refused launch rather than a partial one)
-// with per-peer sequence counters as in the start barrier of the "vccl
-// alltoallv dev log" page (section 6.1).
+// workgroups, the rest are claimed from a counter.  Inside a segment the
+// copy is destination-aligned: 128-bit streaming buffer loads and
+// device-scope streaming buffer stores in the body, numbered from the
+// destination's 128-byte line so every wave store writes whole lines, and
+// byte stores for the at most 15 bytes at either end, so no byte outside a
+// segment is ever written.  When source and destination differ by an odd
+// number of bytes mod 4 the body is realigned through LDS: each wave stages
+// a row of 64 aligned source words, then every lane funnels its word and its
+// right neighbour's with v_alignbyte; a whole number of dwords apart, the
+// source is read directly with dword-aligned 16-byte loads.  Pieces of at
+// most 8 KiB are copied by one wave each, dealt to the waves in turn, so a
+// tile of many small segments costs about one memory round trip instead of
+// one per segment.  Separate instantiations add the bias (BF16 with an FP32
+// bias, FP16 with an FP16 bias) or gather the rows of the indexed exchange.
+// On the run's final launch every admitted block raises its flag in every
+// rank's signal row, and when B > 1 (a cooperative launch) every workgroup
+// waits, with a bounded spin, until all B blocks have arrived (polling one
+// of several copies of the arrival counter).  The block/flag protocol is the
+// block-aware exchange barrier of the PyPTO "LowerL2TensorCollectives Pass"
+// page ("Launch width": all admitted blocks co-resident; a refused launch
+// rather than a partial one) with per-peer sequence counters as in the start
+// barrier of the "vccl alltoallv dev log" page (section 6.1).
 #include "a2av.h"
 #include "kernels.h"
 #include "plan.h"
