@@ -14,6 +14,7 @@ struct alignas(64) RunPlan {
   int32_t base_signal;  // common value of signal[r][b] (r < P, b < B) at entry
   int64_t total_bytes;  // payload bytes T of the run
   int32_t error;        // latched status (first failure since the last query)
+  uint32_t claim[2];    // dynamic tile counters; K2 launch c uses claim[c & 1]
 };
 
 // The arrival counter of the final launch is kept in kArriveReplicas copies,
@@ -34,7 +35,6 @@ struct Workspace {
   int64_t* dst_off;  // [P*P] byte offset inside `target` of each segment, flattened order
   uint32_t* blk_cnt; // [max blocks] workgroups of each block that finished copying
   int64_t* sstride;  // [P] bytes per source block-row (blocked exchange)
-  uint32_t* claims;  // [launches] tile-claim counter of each K2 launch of a run (chunk c: claims[c])
   uint32_t* arrived; // [kArriveReplicas * kArriveStride] admitted blocks that have raised
                      // their flags, copy k at arrived[k * kArriveStride]
 };
@@ -51,7 +51,6 @@ struct CountParams {
   int32_t B;
   int32_t elem;
   int32_t nblk;       // sub-blocks per segment (1 = plain exchange)
-  int32_t launches;   // K2 launches of a run (their claim counters are cleared)
   int64_t unit;       // every count must be a multiple of this (nblk, nblk * hidden, or a row)
   // Indexed exchange only (index != nullptr): the gather lists, their
   // stride, and the whole rows each input table holds.

@@ -255,11 +255,12 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   }
   for (int b = tid; b < p.B; b += kCountThreads) p.ws.blk_cnt[b] = 0u;
   if (tid < kArriveReplicas) p.ws.arrived[int64_t(tid) * kArriveStride] = 0u;
-  for (int c = tid; c < p.launches; c += kCountThreads) p.ws.claims[c] = 0u;
   if (tid == 0) {
     p.ws.prefix[PP] = rowbase[kMaxP];
     p.ws.plan->total_bytes = rowbase[kMaxP];
     p.ws.plan->base_signal = base;
+    p.ws.plan->claim[0] = 0u;
+    p.ws.plan->claim[1] = 0u;
     p.ws.plan->valid = 1;
   }
 }
@@ -994,6 +995,13 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   if (p.last) stage_tables();
   if (valid == 0) return;  // the run failed its device checks: write nothing
 
+  // Launch c claims tiles on plan->claim[c & 1]; the launch before it in the
+  // stream (c + 1) has finished with the other counter, which launch c - 1
+  // will use: clear it now.  K1 cleared both for the run's first launch.
+  if (tid == 0 && blockIdx.x == 0)
+    __hip_atomic_store(&plan->claim[(p.chunk + 1) & 1], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+
   const int64_t c_lo = p.chunk_lo < T ? p.chunk_lo : T;
   const int64_t c_hi = p.chunk_hi < T ? p.chunk_hi : T;
   // A chunk past the run's payload has nothing to copy (the final launch
@@ -1045,7 +1053,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   // once they pass ntiles, and each tile is copied exactly once.
   if (nstatic < ntiles) {
     __shared__ int64_t s_claim;
-    uint32_t* ctr = &p.ws.claims[p.chunk];
+    uint32_t* ctr = &plan->claim[p.chunk & 1];
     if (tid == 0)
       s_claim = nstatic + int64_t(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT));

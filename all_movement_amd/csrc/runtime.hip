@@ -36,12 +36,6 @@ struct a2av_handle {
   void* ws_mem = nullptr;
   a2av::Workspace ws{};
   hipStream_t last_stream = nullptr;
-  // With three or more K2 launches per run: a second stream for every other
-  // chunk launch, and the events that fork it from the caller's stream after
-  // K1 and join it back before the final launch.
-  hipStream_t aux = nullptr;
-  hipEvent_t fork_ev = nullptr;
-  hipEvent_t join_ev = nullptr;
   bool profile = false;
   // Event sets of the last kProfileRuns runs: per run [0] before K1, [1] after
   // K1, [2] after the last K2 launch (one marker per K2 launch cost c5 ~1 %).
@@ -161,8 +155,8 @@ int a2av_create(a2av_handle** out, const a2av_config* cfg) {
   h->spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
 
   // Workspace: plan words, prefix[P*P+1], src_off[P*P], dst_off[P*P],
-  // blk_cnt[max(1, capacity)], sstride[P], the arrival counter copies, the
-  // claim counters claims[launches], each 256-byte aligned.
+  // blk_cnt[max(1, capacity)], sstride[P], the arrival counter copies, each
+  // 256-byte aligned.
   const size_t PP = size_t(cfg->P) * size_t(cfg->P);
   const size_t max_blocks = size_t(h->capacity > 1 ? h->capacity : 1);
   size_t off = 0;
@@ -174,7 +168,6 @@ int a2av_create(a2av_handle** out, const a2av_config* cfg) {
   const size_t o_str = off; off = round_up(off + size_t(cfg->P) * sizeof(int64_t), 256);
   const size_t o_arr = off;
   off = round_up(off + size_t(a2av::kArriveReplicas) * a2av::kArriveStride * sizeof(uint32_t), 256);
-  const size_t o_clm = off; off = round_up(off + size_t(h->launches) * sizeof(uint32_t), 256);
   e = hipMalloc(&h->ws_mem, off);
   if (e != hipSuccess) { delete h; return A2AV_ERR_HIP; }
   e = hipMemset(h->ws_mem, 0, off);
@@ -187,14 +180,6 @@ int a2av_create(a2av_handle** out, const a2av_config* cfg) {
   h->ws.blk_cnt = reinterpret_cast<uint32_t*>(base + o_cnt);
   h->ws.sstride = reinterpret_cast<int64_t*>(base + o_str);
   h->ws.arrived = reinterpret_cast<uint32_t*>(base + o_arr);
-  h->ws.claims = reinterpret_cast<uint32_t*>(base + o_clm);
-
-  if (h->launches >= 3) {
-    e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming);
-    if (e != hipSuccess) { a2av_destroy(h); return A2AV_ERR_HIP; }
-  }
 
   h->profile = (cfg->flags & A2AV_FLAG_PROFILE) != 0;
   if (h->profile) {
@@ -215,9 +200,6 @@ int a2av_destroy(a2av_handle* h) {
   (void)hipDeviceSynchronize();
   for (auto& ev : h->events)
     if (ev) (void)hipEventDestroy(ev);
-  if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
-  if (h->join_ev) (void)hipEventDestroy(h->join_ev);
-  if (h->aux) (void)hipStreamDestroy(h->aux);
   if (h->ws_mem) (void)hipFree(h->ws_mem);
   delete h;
   return A2AV_OK;
@@ -287,7 +269,6 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   cp.B = int32_t(li.blocks);
   cp.elem = int32_t(a2av::elem_bytes(dtype));
   cp.nblk = nblk;
-  cp.launches = h->launches;
   const int64_t elem = a2av::elem_bytes(dtype);
   if (mode == 3) {
     cp.unit = x.row_elems;
@@ -340,39 +321,16 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   // Chunks are issued from the highest to chunk 0.  Chunks past the run's
   // payload cost only a plain launch that exits at once, and the final launch
   // (the one that raises the flags, cooperative when B > 1) is chunk 0, which
-  // holds payload whenever the run has any.  The chunks before it copy
-  // disjoint byte ranges, each with a claim counter of its own, so with three
-  // or more launches every other one goes to the handle's second stream: one
-  // launch's last tiles then overlap the next launch's first.  The final
-  // launch waits for both streams.  A stream being captured into a graph
-  // keeps every launch.
-  bool split = false;
-  if (h->aux) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if ((e = hipStreamIsCapturing(s, &cs)) != hipSuccess)
-      return hip_fail(h, e, "hipStreamIsCapturing");
-    split = cs == hipStreamCaptureStatusNone;
-  }
-  if (split) {
-    if ((e = hipEventRecord(h->fork_ev, s)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
-    if ((e = hipStreamWaitEvent(h->aux, h->fork_ev, 0)) != hipSuccess)
-      return hip_fail(h, e, "hipStreamWaitEvent");
-  }
+  // holds payload whenever the run has any.
   for (int32_t n = 0; n < h->launches; ++n) {
     const int32_t c = h->launches - 1 - n;
     const bool last = (c == 0);
-    if (split && last) {
-      if ((e = hipEventRecord(h->join_ev, h->aux)) != hipSuccess)
-        return hip_fail(h, e, "hipEventRecord");
-      if ((e = hipStreamWaitEvent(s, h->join_ev, 0)) != hipSuccess)
-        return hip_fail(h, e, "hipStreamWaitEvent");
-    }
     kp.chunk_lo = int64_t(c) * h->chunk_limit;
     kp.chunk_hi = (c == h->launches - 1) ? INT64_MAX : int64_t(c + 1) * h->chunk_limit;
     kp.chunk = c;
     kp.last = last ? 1 : 0;
     kp.wait = (last && li.blocks > 1) ? 1 : 0;
-    e = a2av::launch_copy(kp, li.workgroups, kp.wait != 0, split && !last && (n & 1) ? h->aux : s);
+    e = a2av::launch_copy(kp, li.workgroups, kp.wait != 0, s);
     if (e != hipSuccess) return hip_fail(h, e, "copy_kernel launch");
   }
   if (ev) {

@@ -40,8 +40,7 @@
  * process.
  *
  * Graphs: a run enqueues only kernel launches on its stream (no copies, no
- * memsets, no synchronization; while the stream is capturing, every launch
- * stays on it), so a run may be captured into a HIP graph;
+ * memsets, no synchronization), so a run may be captured into a HIP graph;
  * every replay is one more run over the buffers' contents at replay time,
  * ordered with the handle's other runs like any run.  A handle created with
  * A2AV_FLAG_PROFILE records no events while its stream is capturing.
@@ -144,13 +143,8 @@ int a2av_create(a2av_handle **out, const a2av_config *cfg);
  * failure writes nothing, is latched in the handle and is reported by
  * a2av_query_error; a2av_run itself has already returned A2AV_OK.
  * The call does not synchronize: results are visible to later work on
- * `stream`.  With three or more copy launches per run (a payload bound above
- * twice the chunk limit) every other launch before the final one runs on a
- * stream of the handle's own, forked from `stream` after the count kernel
- * and joined back before the final launch, so `stream` still orders the
- * whole run; a stream being captured into a graph keeps every launch.
- * Returns A2AV_ERR_HIP if a launch fails; K1 may then have run, so
- * recv_counts may be written while the target and the signal are not.
+ * `stream`.  Returns A2AV_ERR_HIP if a launch fails; K1 may then have run,
+ * so recv_counts may be written while the target and the signal are not.
  */
 int a2av_run(a2av_handle *h, const void *input, void *target, int32_t *signal,
              const int32_t *send_counts, int32_t *recv_counts, int32_t P, int64_t core_num,

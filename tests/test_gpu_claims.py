@@ -1,12 +1,10 @@
 """GPU parity of K2's claimed tiles: a launch deals the first eighth of its
-tile rounds statically and hands the rest out from a counter of its own,
-cleared for every run.  With three or more launches per run, every other
-launch before the final one runs on the handle's second stream, overlapping
-its neighbours.  These cases make every launch large enough to claim (more
-than one round of 128 KiB tiles per workgroup), with odd and even numbers of
-launches, several runs on one handle, several workgroups per block, and every
-body (plain, blocked, bias, row gather).  Bit-exact against the oracle after
-every run."""
+tile rounds statically and hands the rest out from a counter, two counters
+alternating between the launches of a run and reused by the next run.  These
+cases make every launch large enough to claim (more than one round of 128 KiB
+tiles per workgroup), with odd and even numbers of launches, several runs on
+one handle, several workgroups per block, and every body (plain, blocked,
+bias, row gather).  Bit-exact against the oracle after every run."""
 import numpy as np
 import pytest
 
