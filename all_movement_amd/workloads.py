@@ -280,7 +280,8 @@ def bias_workload(dtype: int = BF16, scale: int = 1) -> Workload:
     C = np.full((P, P), n, dtype=np.int32)
     slab = P * n * 2
     tag = "bf16_fp32bias" if dtype == BF16 else "fp16_fp16bias"
-    return Workload(f"c5b_p8_{tag}_bmm_rs_a2a", f"P=8 {tag} equal counts 2^25, bias Add fused, "
+    key = "c5b" if dtype == BF16 else "c5h"
+    return Workload(f"{key}_p8_{tag}_bmm_rs_a2a", f"P=8 {tag} equal counts 2^25, bias Add fused, "
                     "(E/ep=8, ep*C=8*2048, H/tp=2048) -> (E=64, C=2048, H/tp=2048), core_num 256",
                     P, dtype, 256, 256, slab, slab, C, 1005,
                     extra={"E_over_ep": A, "ep": 8, "C": 2048 // scale, "H_over_tp": H,

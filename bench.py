@@ -34,7 +34,7 @@ PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
 # The workloads bench.py can time.  c1..c5 are the plain exchange.  c5u is
 # c5's exchange taken on the source's own temp3 layout (E/ep, ep*C, H/tp):
 # the blocked exchange with nblk = E/ep = 8.  c5b is that exchange in BF16
-# with the bias Add fused in front.  c3i is c3's MoE dispatch as the indexed
+# with the bias Add fused in front (FP32 bias), c5h in FP16 (FP16 bias).  c3i is c3's MoE dispatch as the indexed
 # exchange: token tables stored once, the routing as gather lists.
 # cpu_scale: the size divisor of the oracle sample for the CPU baseline.
 @dataclass(frozen=True)
@@ -45,6 +45,7 @@ class Spec:
     cpu_scale: int = 1
     cold_runs: int = 50  # runs of the cache-cold protocol (each after a 1 GiB flush)
     graph: bool = False  # also time replays of one run captured into a HIP graph
+    half: bool = False   # bias workloads: FP16 payload and bias instead of BF16 + FP32
 
 
 WORKLOADS = {"c1": Spec("plain", 1, graph=True), "c2": Spec("plain", 2, graph=True), "c3": Spec("plain", 3, cpu_scale=4),
@@ -52,6 +53,7 @@ WORKLOADS = {"c1": Spec("plain", 1, graph=True), "c2": Spec("plain", 2, graph=Tr
              "c5": Spec("plain", 5, cpu_scale=8, cold_runs=5),
              "c5u": Spec("blocked", 5, nblk=8, cpu_scale=8, cold_runs=5),
              "c5b": Spec("bias", nblk=8, cpu_scale=16, cold_runs=5),
+             "c5h": Spec("bias", nblk=8, cpu_scale=16, cold_runs=5, half=True),
              "c3i": Spec("indexed", cpu_scale=4)}
 FLUSH_BYTES = 1 << 30       # written before each cache-cold run: above the 256 MB MALL
 # The library's profiling events cost a few microseconds each on the stream;
@@ -97,7 +99,7 @@ def make_workload(spec: Spec, scale: int = 1):
     if spec.kind == "indexed":
         return wl.indexed_workload(scale=scale)
     if spec.kind == "bias":
-        return wl.bias_workload(wl.BF16, scale=scale)
+        return wl.bias_workload(wl.FP16 if spec.half else wl.BF16, scale=scale)
     w = wl.workload(spec.k, scale=scale)
     if spec.kind == "blocked":
         w.name += f"_temp3_layout_nblk{spec.nblk}"
@@ -314,7 +316,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="c1,c2,c3,c4,c5u,c5b,c3i",
+    ap.add_argument("--also", default="c1,c2,c3,c4,c5u,c5b,c5h,c3i",
                     help="other workloads reported beside it")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-cold", action="store_true",

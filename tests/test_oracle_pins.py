@@ -402,6 +402,7 @@ def test_bias_workload_shape():
     assert wl.bias_np(w, A, H).shape == (w.P, A, H) and wl.bias_np(w, A, H).dtype == np.float32
     w16 = wl.bias_workload(wl.FP16, scale=64)
     assert wl.bias_np(w16, A, H).dtype == np.uint16
+    assert w.name.startswith("c5b_") and w16.name.startswith("c5h_")
 
 
 def test_workload_shapes():
