@@ -756,133 +756,6 @@ __device__ inline void tile_bounds(const SegTables& tab, int nseg, const uint8_t
   i = a < b ? seg_of(tab.prefix, nseg, a) : 0;
 }
 
-// Row gather over a workgroup's static tiles, software-pipelined: a pass
-// (at most kGatherUnroll * NT words of one segment) loads its payload words,
-// then the gather-list entries of the next pass are loaded while those words
-// are in flight, then the words are stored.  A pass then waits for one
-// dependent round trip (its payload) instead of two (list, then payload),
-// and never for the previous pass's stores.
-struct GatherPass {
-  const uint8_t* table;  // source s's token table
-  const int32_t* list;   // the segment's gather list, from its first row
-  uint8_t* dst;          // target bytes of the pass
-  int64_t off;           // byte offset of the pass in its segment
-  int64_t n;             // bytes of the pass, a multiple of 16
-};
-
-// The list loads of a pass: where this thread's words start in the table.
-__device__ inline void gather_pass_rows(const GatherPass& g, int64_t RB, int tid,
-                                        int64_t (&src)[kGatherUnroll]) {
-  constexpr int NT = kCopyThreads;
-  const int64_t K = g.n >> 4;
-  const int64_t step_r = (int64_t(NT) * 16) / RB;
-  const int64_t step_w = int64_t(NT) * 16 - step_r * RB;
-  const int64_t off = g.off + 16 * int64_t(tid);
-  int64_t r = off / RB;
-  int64_t w = off - r * RB;
-#pragma unroll
-  for (int j = 0; j < kGatherUnroll; ++j) {
-    const int64_t k = int64_t(j) * NT + tid;
-    src[j] = k < K ? int64_t(g.list[r]) * RB + w : 0;
-    w += step_w;
-    r += step_r;
-    if (w >= RB) {
-      w -= RB;
-      ++r;
-    }
-  }
-}
-
-__device__ void gather_static(const CopyParams& p, const SegTables& tab, int nseg, int64_t c_lo,
-                              int64_t c_hi, int64_t tile, int64_t nstatic, int tid, int lane) {
-  constexpr int NT = kCopyThreads;
-  constexpr int64_t kPassBytes = int64_t(NT) * 16 * kGatherUnroll;
-  const int64_t W = gridDim.x;
-  const int64_t RB = wave_uniform(p.row_bytes);
-
-  // Cursor over the static tiles blockIdx.x, + W, ...: batches of 64 tiles
-  // whose bounds lane l holds for tile l of the batch (as in the copy loop).
-  int64_t t0 = blockIdx.x;
-  int j = 0;
-  int64_t la = 0, lb = 0;
-  int li = 0;
-  int64_t x = 0, b = 0;
-  int i = 0;
-  bool more = t0 < nstatic;
-  auto load_batch = [&]() {
-    const int64_t tl = t0 + int64_t(lane) * W;
-    la = 0;
-    lb = 0;
-    li = 0;
-    if (tl < nstatic) tile_bounds(tab, nseg, p.target, c_lo, c_hi, tile, tl, la, lb, li);
-  };
-  if (more) load_batch();
-  auto next_pass = [&](GatherPass& g) -> bool {
-    for (;;) {
-      if (x < b) {
-        const int64_t seg_hi = wave_uniform(tab.prefix[i + 1]);
-        if (seg_hi <= x) {
-          ++i;
-          continue;
-        }
-        int64_t pe = b < seg_hi ? b : seg_hi;
-        if (pe > x + kPassBytes) pe = x + kPassBytes;
-        const int s = source_of<3>(i, p.P);
-        const int64_t src_i = wave_uniform(tab.src[i]);
-        const int64_t row0 = (src_i - int64_t(s) * p.in_slab) / RB;
-        g.table = wave_uniform(p.input + int64_t(s) * p.in_slab);
-        g.list = wave_uniform(p.index + int64_t(s) * p.index_stride + row0);
-        g.dst = wave_uniform(p.target + wave_uniform(tab.dst[i]));
-        g.off = x - wave_uniform(tab.prefix[i]);
-        g.n = pe - x;
-        x = pe;
-        return true;
-      }
-      if (!more) return false;
-      if (j >= kWave || t0 + int64_t(j) * W >= nstatic) {
-        t0 += int64_t(kWave) * W;
-        j = 0;
-        if (t0 >= nstatic) {
-          more = false;
-          return false;
-        }
-        load_batch();
-      }
-      x = readlane64(la, j);
-      b = readlane64(lb, j);
-      i = __builtin_amdgcn_readlane(li, j);
-      ++j;
-    }
-  };
-
-  GatherPass cur{}, nxt{};
-  int64_t src[kGatherUnroll], nsrc[kGatherUnroll];
-  bool have = next_pass(cur);
-  if (have) gather_pass_rows(cur, RB, tid, src);
-  while (have) {
-    const int64_t K = cur.n >> 4;
-    u32x4 v[kGatherUnroll];
-#pragma unroll
-    for (int q = 0; q < kGatherUnroll; ++q) {
-      const int64_t k = int64_t(q) * NT + tid;
-      v[q] = u32x4{0u, 0u, 0u, 0u};
-      if (k < K) v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cur.table + src[q]));
-    }
-    const bool have_next = next_pass(nxt);
-    if (have_next) gather_pass_rows(nxt, RB, tid, nsrc);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(cur.dst + cur.off, cur.n);
-#pragma unroll
-    for (int q = 0; q < kGatherUnroll; ++q) {
-      const int64_t k = int64_t(q) * NT + tid;
-      if (k < K) store16(rd, k, v[q]);
-    }
-    cur = nxt;
-#pragma unroll
-    for (int q = 0; q < kGatherUnroll; ++q) src[q] = nsrc[q];
-    have = have_next;
-  }
-}
-
 // Copy the flattened bytes [x, b) that start in segment i, piece by piece.
 // The target side of a segment is contiguous.  In the blocked exchange the
 // source side is nblk sub-blocks, sub-block a at tab.src[i] + a * sstride[s],
@@ -1021,11 +894,11 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   // to workgroup t mod W.  The rest go to whichever workgroup asks first, so
   // workgroups that stream slower take fewer tiles and the launch ends when
   // the last tile does, not when the slowest workgroup's share does
-  // (measured on gfx950: c5 5.79 -> 6.11 TB/s in-kernel, c3 5.25 -> 5.75,
-  // the row gather 186 -> 179 us on c3i; an eighth static rather than a
-  // quarter, c5 -0.7 %, c5b -0.6 %).  With 16-byte rows the row gather runs
-  // software-pipelined over its static tiles (gather_static).
-  const int64_t rounds_static = (rounds + 7) / 8;
+  // (measured on gfx950: c5 5.79 -> 6.11 TB/s in-kernel, c3 5.25 -> 5.75;
+  // an eighth static rather than a quarter, c5 -0.7 %, c5b -0.6 %).  The row
+  // gather claims every tile: its tiles start with a dependent gather-list
+  // load, and it ran fastest with no static deal (c3i 180.4 -> 177.8 us).
+  const int64_t rounds_static = MODE == 3 ? 0 : (rounds + 7) / 8;
   const int64_t nstatic = W * rounds_static < ntiles ? W * rounds_static : ntiles;
 
   int small = 0;  // small pieces met so far (see wg_copy_piece)
@@ -1034,9 +907,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   // 64 at a time: lane l first finds the bounds and first segment of the l-th
   // tile of the batch, then the wave walks the batch, reading them with
   // readlane.
-  const bool pipelined = MODE == 3 && p.gather_words;
-  if (pipelined) gather_static(p, tab, nseg, c_lo, c_hi, tile, nstatic, tid, lane);
-  for (int64_t t0 = blockIdx.x; !pipelined && t0 < nstatic; t0 += int64_t(kWave) * W) {
+  for (int64_t t0 = blockIdx.x; t0 < nstatic; t0 += int64_t(kWave) * W) {
     const int64_t tl = t0 + int64_t(lane) * W;
     int64_t la = 0;
     int64_t lb = 0;
