@@ -301,3 +301,25 @@ def test_generator_on_gpu_matches_numpy():
     t = torch.empty(10_000_003, dtype=torch.uint8, device=DEV)
     wl.fill_random_(t, 4242, chunk_words=1 << 18)
     np.testing.assert_array_equal(t.cpu().numpy(), wl.random_bytes_np(4242, 0, t.numel()))
+
+
+def test_block_count_changes_between_runs_on_one_handle():
+    # One handle, runs with core_num giving B = 64, 1, 8, 3, 64, 16 in turn: the
+    # per-block counters and the arrival counter copies are reset by every
+    # run's count kernel, whatever B the run before used.  The signal is set
+    # back to zeros before each run, so each run's precondition holds.
+    P = 8
+    C = np.random.default_rng(77).integers(0, 1 << 18, size=(P, P)).astype(np.int32)
+    w = wl.custom(P, wl.FP32, C, core_num=64, S=80, seed=77)
+    c = Case(w)
+    ex = exchange_for(w)
+    try:
+        for L in (64, 1, 8, 3, 64, 16):
+            c.signal.zero_()
+            c.signal_np0 = np.zeros_like(c.signal_np0)
+            c.target.fill_(wl.SENTINEL)
+            c.recv.fill_(-7)
+            say("core_num", L, "B", oracle.blocks(P, L))
+            c.assert_matches(c.run_gpu(ex, core_num=L), c.run_oracle(core_num=L))
+    finally:
+        ex.close()
