@@ -125,6 +125,54 @@ def finite16_from_words(words: np.ndarray, dtype: int) -> np.ndarray:
     return (sign | (exp << 10) | (w & 0x3FF)).astype(np.uint16)
 
 
+def edge16_from_words(words: np.ndarray, dtype: int) -> np.ndarray:
+    """Map random 16-bit words to a mixture that reaches every IEEE class of a
+    16-bit format (as uint16 bits): the top three bits pick the class, the
+    rest fill sign and fraction.
+
+    class 0-2: the word itself (any exponent, so also NaN and infinity);
+    3: the largest finite magnitude; 4: the top binade (overflows when two
+    such values are added); 5: +-infinity; 6: a NaN (quiet or signalling,
+    random payload, all-ones fraction included); 7: zero or a subnormal.
+    """
+    w = words.astype(np.uint32)
+    cls = w >> 13
+    sign = (w << 3) & 0x8000                            # bit 12 -> sign
+    frac_bits = 7 if dtype == BF16 else 10
+    emax = 0xFF if dtype == BF16 else 0x1F              # all-ones exponent field
+    fmask = (1 << frac_bits) - 1
+    frac = w & fmask
+    out = w.copy()
+    out = np.where(cls == 3, sign | ((emax - 1) << frac_bits) | fmask, out)
+    out = np.where(cls == 4, sign | ((emax - 1) << frac_bits) | frac, out)
+    out = np.where(cls == 5, sign | (emax << frac_bits), out)
+    out = np.where(cls == 6, sign | (emax << frac_bits) | np.maximum(frac, 1), out)
+    out = np.where(cls == 7, sign | (frac & (fmask >> (w >> 11 & 1))), out)
+    return out.astype(np.uint16)
+
+
+def edge_bias_values(seed: int, P: int, nblk: int, hidden: int, dtype: int) -> np.ndarray:
+    """Bias [P, nblk, hidden] reaching every IEEE class: float32 for BF16
+    payloads (random bit patterns, the largest finite values, infinities,
+    NaNs, subnormals, moderate values), binary16 bits from
+    :func:`edge16_from_words` for FP16."""
+    n = P * nblk * hidden
+    if dtype == BF16:
+        u = random_bytes_np(seed, 0, 4 * n).view(np.uint32)
+        cls = u & 7
+        sign = u & 0x80000000
+        out = u.copy()                                   # class 0-1: any pattern
+        out = np.where(cls == 2, sign | 0x7F7FFFFF, out)                 # largest finite
+        out = np.where(cls == 3, sign | 0x7F000000 | (u >> 9 & 0x7FFFFF), out)  # top binades
+        out = np.where(cls == 4, sign | 0x7F800000, out)                 # infinity
+        out = np.where(cls == 5, sign | 0x7F800000 | np.maximum(u >> 9 & 0x7FFFFF, 1), out)  # NaN
+        out = np.where(cls == 6, sign | (u >> 9 & 0x7FFFFF), out)        # zero or subnormal
+        out = np.where(cls == 7, sign | 0x3F800000 | (u >> 9 & 0x7FFFFF), out)  # [1, 2)
+        return out.astype(np.uint32).view(np.float32).reshape(P, nblk, hidden)
+    w = random_bytes_np(seed, 0, 2 * n).view(np.uint16)
+    return edge16_from_words(w, FP16).reshape(P, nblk, hidden)
+
+
 def finite16_(t, dtype: int, chunk: int = 1 << 26) -> None:
     """In place on a torch tensor of 16-bit words (any 2-byte dtype, CPU or GPU):
     the same mapping as :func:`finite16_from_words`, integer ops only."""

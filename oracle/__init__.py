@@ -16,8 +16,9 @@ Semantics follow the five-operand ``all_to_all_v(input, target, signal,
 send_counts, recv_counts, core_num)`` of the PyPTO "LowerL2TensorCollectives
 Pass" page (section "Behavior"); segment addressing follows the ncclx
 ``ctranAllToAllvIbImpl`` pseudocode on the "vccl alltoallv dev log" page
-(section 5).  Parity status per function is stated in ``a2av_oracle.c``; the
-signal's +1-per-exchange value is "parity unpinned" (the pages do not fix it).
+(section 5).  What pins each function is stated in ``a2av_oracle.c``; the
+signal's +1-per-exchange value, a reading of the barrier the pages describe,
+is pinned against the event model in ``tests/barrier_model.py``.
 """
 from __future__ import annotations
 
@@ -80,14 +81,15 @@ def lib() -> ctypes.CDLL:
         L.a2av_oracle_run_indexed.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i64,
                                               i32, i64, i32, i64]
         L.a2av_oracle_run_indexed.restype = ctypes.c_int
-        L.a2av_oracle_f32_to_bf16.argtypes = [ctypes.c_float]
-        L.a2av_oracle_f32_to_bf16.restype = ctypes.c_uint16
-        L.a2av_oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
-        L.a2av_oracle_bf16_to_f32.restype = ctypes.c_float
-        L.a2av_oracle_f32_to_f16.argtypes = [ctypes.c_float]
-        L.a2av_oracle_f32_to_f16.restype = ctypes.c_uint16
-        L.a2av_oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
-        L.a2av_oracle_f16_to_f32.restype = ctypes.c_float
+        u16, u32 = ctypes.c_uint16, ctypes.c_uint32
+        L.a2av_oracle_f32_to_bf16.argtypes = [u32]
+        L.a2av_oracle_f32_to_bf16.restype = u16
+        L.a2av_oracle_bf16_to_f32.argtypes = [u16]
+        L.a2av_oracle_bf16_to_f32.restype = u32
+        L.a2av_oracle_f32_to_f16.argtypes = [u32]
+        L.a2av_oracle_f32_to_f16.restype = u16
+        L.a2av_oracle_f16_to_f32.argtypes = [u16]
+        L.a2av_oracle_f16_to_f32.restype = u32
         L.a2av_oracle_displacements.argtypes = [vp, i32, i32, vp, vp]
         L.a2av_oracle_displacements.restype = None
         L.a2av_oracle_move.argtypes = [vp, vp, vp, i32, i32, i64, i64]
@@ -178,20 +180,46 @@ def run_indexed(input_bytes: np.ndarray, target_bytes: np.ndarray, signal: np.nd
         row_elems, index_stride))
 
 
-def f32_to_bf16(x: float) -> int:
-    return int(lib().a2av_oracle_f32_to_bf16(x))
+# The 16-bit conversions take and return bit patterns (binary32 bits as a
+# uint32, 16-bit values as a uint16), so NaN payloads are not changed on the
+# way through Python floats.  The array forms apply them element by element.
+
+def f32_to_bf16(bits: int) -> int:
+    return int(lib().a2av_oracle_f32_to_bf16(bits))
 
 
-def bf16_to_f32(h: int) -> float:
-    return float(lib().a2av_oracle_bf16_to_f32(h))
+def bf16_to_f32(h: int) -> int:
+    return int(lib().a2av_oracle_bf16_to_f32(h))
 
 
-def f32_to_f16(x: float) -> int:
-    return int(lib().a2av_oracle_f32_to_f16(x))
+def f32_to_f16(bits: int) -> int:
+    return int(lib().a2av_oracle_f32_to_f16(bits))
 
 
-def f16_to_f32(h: int) -> float:
-    return float(lib().a2av_oracle_f16_to_f32(h))
+def f16_to_f32(h: int) -> int:
+    return int(lib().a2av_oracle_f16_to_f32(h))
+
+
+def _map(fn, a: np.ndarray, out_dtype) -> np.ndarray:
+    return np.array([fn(int(v)) for v in np.asarray(a).ravel()], out_dtype)
+
+
+def f32_to_bf16_array(bits: np.ndarray) -> np.ndarray:
+    """uint32 binary32 patterns -> uint16 bfloat16 patterns."""
+    return _map(lib().a2av_oracle_f32_to_bf16, bits, np.uint16)
+
+
+def bf16_to_f32_array(h: np.ndarray) -> np.ndarray:
+    return _map(lib().a2av_oracle_bf16_to_f32, h, np.uint32)
+
+
+def f32_to_f16_array(bits: np.ndarray) -> np.ndarray:
+    """uint32 binary32 patterns -> uint16 binary16 patterns."""
+    return _map(lib().a2av_oracle_f32_to_f16, bits, np.uint16)
+
+
+def f16_to_f32_array(h: np.ndarray) -> np.ndarray:
+    return _map(lib().a2av_oracle_f16_to_f32, h, np.uint32)
 
 
 def check(input_ptr, target_ptr, signal_ptr, send_ptr, recv_ptr, *, P, S, in_slab,

@@ -25,11 +25,13 @@
  * typeSize bytes move.  The displacements are the exclusive prefix sums of the
  * counts (no displacement operand exists in the five-operand statement).
  *
- * Parity status of every function here is recorded at its definition.  One
- * part is "parity unpinned": the signal update (arrive), whose +1 per exchange
- * the pages do not fix; the tests hold the GPU path to this definition only.
- * The plain, blocked and indexed exchanges move raw bytes; the fused-bias
- * exchange adds in binary32 and rounds to the 16-bit payload type.
+ * What pins each function is recorded at its definition.  The signal update
+ * (arrive) is this implementation's reading of the barrier the pages
+ * describe; it is pinned against an event model of that block and
+ * sequence-counter barrier, written apart from this file.  The plain, blocked
+ * and indexed exchanges move raw bytes; the fused-bias exchange adds in
+ * binary32 and rounds to the 16-bit payload type under IEEE 754's rules,
+ * infinities and NaNs included.
  */
 #include <math.h>
 #include <stdint.h>
@@ -262,8 +264,13 @@ static void move_segments(const uint8_t *input, uint8_t *target, const int32_t *
  * alone.  The pages fix only that the signal is [NR, S] with S >= B and that
  * reusing it orders exchanges; the +1-per-exchange value is this
  * implementation's reading of the per-peer sequence-counter barrier on the
- * "vccl alltoallv dev log" page (section 6.1).  Parity unpinned by the pages:
- * the tests check this definition, nothing more.
+ * "vccl alltoallv dev log" page (section 6.1) and the block-aware barrier of
+ * the LowerL2TensorCollectives page ("Launch width").
+ * Pinned by: an event model of that barrier (every admitted block of every
+ * rank posts its own wrapping counter once and waits for all to move past
+ * the common entry value, in random interleavings), over random P, S and B,
+ * entry values at the int32 edges and sequences of exchanges whose block
+ * count changes; the model also decides which exchanges are refused.
  */
 static void arrive(int32_t *signal, int32_t P, int32_t S, int64_t B)
 {
@@ -374,66 +381,131 @@ static uint32_t bits_from_f32(float f)
     return u;
 }
 
-/* bfloat16 is the upper half of a binary32: widening appends 16 zero bits. */
-float a2av_oracle_bf16_to_f32(uint16_t h)
+/*
+ * The 16-bit formats, from IEEE 754-2008 (binary16: 1 sign, 5 exponent and
+ * 10 fraction bits, bias 15) and the bfloat16 layout (the upper half of a
+ * binary32: 1 sign, 8 exponent and 7 fraction bits, bias 127).  Every
+ * conversion takes and returns bit patterns, so NaN payloads cross the
+ * boundary untouched.
+ *
+ * Narrowing (binary32 -> 16 bits) rounds to nearest, ties to even, the
+ * default rounding of IEEE 754 (section 4.3.1):
+ *   - a finite value is scaled into the grid of its binade (the subnormal
+ *     grid below the format's smallest normal binade), the scaled value is
+ *     rounded to an integer with ties to even, and the fields are assembled;
+ *     a result at or past the largest finite value's next binade is an
+ *     overflow, which under this rounding gives the infinity of the sign
+ *     (section 7.4);
+ *   - an infinity stays the infinity of the same sign;
+ *   - a NaN becomes a quiet NaN (section 6.2): the sign and the leading
+ *     payload bits are kept and the quiet bit is set.  IEEE 754 does not fix
+ *     which NaN an operation returns, so the tests compare NaN-ness only.
+ * Widening (16 bits -> binary32) is exact for every input: subnormals become
+ * normals, infinities stay infinities, and a NaN keeps its sign and payload.
+ */
+
+/* bfloat16 -> binary32: the bits move to the upper half (exact, NaN payload
+ * kept).  Pinned by: torch's CPU bfloat16 -> float32 on all 65,536 patterns. */
+uint32_t a2av_oracle_bf16_to_f32(uint16_t h)
 {
-    return f32_from_bits((uint32_t)h << 16);
+    return (uint32_t)h << 16;
 }
 
-/* binary32 -> bfloat16, round to nearest, ties to even: add half an ulp of
- * the kept part (minus one when the kept part is even), then truncate.
- * Finite inputs only (the payloads here are finite).
- * Pinned by: torch's CPU float32 -> bfloat16 conversion on every test value. */
-uint16_t a2av_oracle_f32_to_bf16(float f)
+/* Round the non-negative finite value a to nearest, ties to even, in a format
+ * with `sig` significand bits (implicit bit included) whose smallest normal
+ * binade is 2^emin; e is a's binade from its binary32 exponent field.  Returns
+ * the rounded significand m (in [0, 2^sig]) and sets *binade to the binade
+ * of its grid (emin for the subnormal grid). */
+static int64_t round_to_grid(double a, int e, int emin, int sig, int *binade)
 {
-    uint32_t u = bits_from_f32(f);
-    uint32_t lsb = (u >> 16) & 1u;
-    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
-}
-
-/* binary16 -> binary32, exact (normal, subnormal, zero; finite inputs). */
-float a2av_oracle_f16_to_f32(uint16_t h)
-{
-    uint32_t sign = (uint32_t)(h >> 15) & 1u;
-    uint32_t exp = (uint32_t)(h >> 10) & 0x1Fu;
-    uint32_t man = (uint32_t)h & 0x3FFu;
-    float mag;
-    if (exp == 0)
-        mag = (float)man * (1.0f / 16777216.0f); /* man * 2^-24 */
-    else
-        mag = f32_from_bits(((exp + 112u) << 23) | (man << 13)); /* rebias 15 -> 127 */
-    return sign ? -mag : mag;
-}
-
-/* binary32 -> binary16, round to nearest, ties to even, from the definition:
- * scale into the binary16 grid of the value's binade (the subnormal grid
- * below 2^-14), round the scaled value to an integer with ties to even, and
- * assemble the fields.  Finite inputs whose result is finite.
- * Pinned by: numpy's float32 -> float16 conversion on every test value. */
-uint16_t a2av_oracle_f32_to_f16(float f)
-{
-    uint32_t u = bits_from_f32(f);
-    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
-    double a = fabs((double)f);
-    if (a == 0.0)
-        return sign;
-    int e = (int)((u >> 23) & 0xFFu) - 127;            /* binade of |f| */
-    if (e < -14)
-        e = -14;                                       /* subnormal grid */
-    double step = ldexp(1.0, e - 10);                  /* ulp in that binade */
+    if (e < emin)
+        e = emin;                                      /* subnormal grid */
+    double step = ldexp(1.0, e - (sig - 1));           /* one ulp in binade e */
     double q = a / step;                               /* exact: a power-of-2 scale */
     double r = floor(q);
     double frac = q - r;
     if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) == 1.0))
         r += 1.0;
-    /* r in [0, 2048]; 2048 means the value rounded up into the next binade. */
-    int64_t m = (int64_t)r;
-    int64_t biased = (int64_t)e + 15;
-    if (m >= 2048) {
+    *binade = e;
+    return (int64_t)r;
+}
+
+/* binary32 -> bfloat16, round to nearest, ties to even, as stated above.
+ * Pinned by: torch's CPU float32 -> bfloat16 conversion on random bit
+ * patterns of every exponent, ties, subnormals, the overflow edge, the
+ * infinities and NaNs (NaN-ness only). */
+uint16_t a2av_oracle_f32_to_bf16(uint32_t u)
+{
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t efield = (u >> 23) & 0xFFu;
+    uint32_t frac = u & 0x7FFFFFu;
+    if (efield == 0xFFu) {
+        if (frac == 0)
+            return (uint16_t)(sign | 0x7F80u);                      /* +-Inf */
+        return (uint16_t)(sign | 0x7FC0u | (uint16_t)(frac >> 16)); /* quiet NaN */
+    }
+    double a = fabs((double)f32_from_bits(u));
+    if (a == 0.0)
+        return sign;
+    int binade;
+    int64_t m = round_to_grid(a, (int)efield - 127, -126, 8, &binade);
+    int64_t biased = (int64_t)binade + 127;
+    if (m >= 256) {                                    /* rounded into the next binade */
         m >>= 1;
         biased += 1;
     }
-    if (m < 1024)                                      /* subnormal result */
+    if (biased >= 255)                                 /* overflow */
+        return (uint16_t)(sign | 0x7F80u);
+    if (m < 128)                                       /* subnormal (or zero) result */
+        return (uint16_t)(sign | (uint16_t)m);
+    return (uint16_t)(sign | (uint16_t)(biased << 7) | (uint16_t)(m & 0x7F));
+}
+
+/* binary16 -> binary32, exact.  Pinned by: numpy's float16 -> float32 on all
+ * 65,536 patterns (NaN-ness only for NaNs). */
+uint32_t a2av_oracle_f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) & 1u;
+    uint32_t exp = (uint32_t)(h >> 10) & 0x1Fu;
+    uint32_t man = (uint32_t)h & 0x3FFu;
+    if (exp == 0x1Fu)                                  /* +-Inf, or NaN with its payload */
+        return (sign << 31) | 0x7F800000u | (man << 13);
+    float mag;
+    if (exp == 0)
+        mag = (float)man * (1.0f / 16777216.0f);       /* man * 2^-24, exact */
+    else
+        mag = f32_from_bits(((exp + 112u) << 23) | (man << 13)); /* rebias 15 -> 127 */
+    return bits_from_f32(sign ? -mag : mag);
+}
+
+/* binary32 -> binary16, round to nearest, ties to even, as stated above.
+ * Pinned by: numpy's float32 -> float16 conversion on random bit patterns of
+ * every exponent, ties in the normal and subnormal ranges, the overflow edge
+ * (65504, 65519, 65520, 70000, 131008), the infinities and NaNs (NaN-ness
+ * only). */
+uint16_t a2av_oracle_f32_to_f16(uint32_t u)
+{
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t efield = (u >> 23) & 0xFFu;
+    uint32_t frac = u & 0x7FFFFFu;
+    if (efield == 0xFFu) {
+        if (frac == 0)
+            return (uint16_t)(sign | 0x7C00u);                      /* +-Inf */
+        return (uint16_t)(sign | 0x7E00u | (uint16_t)(frac >> 13)); /* quiet NaN */
+    }
+    double a = fabs((double)f32_from_bits(u));
+    if (a == 0.0)
+        return sign;
+    int binade;
+    int64_t m = round_to_grid(a, (int)efield - 127, -14, 11, &binade);
+    int64_t biased = (int64_t)binade + 15;
+    if (m >= 2048) {                                   /* rounded into the next binade */
+        m >>= 1;
+        biased += 1;
+    }
+    if (biased >= 31)                                  /* overflow */
+        return (uint16_t)(sign | 0x7C00u);
+    if (m < 1024)                                      /* subnormal (or zero) result */
         return (uint16_t)(sign | (uint16_t)m);
     return (uint16_t)(sign | (uint16_t)(biased << 10) | (uint16_t)(m & 0x3FF));
 }
@@ -449,13 +521,17 @@ uint16_t a2av_oracle_f32_to_f16(float f)
  * `hidden` (= H/tp) elements; element h of a row in block-row a of source s
  * gets bias[(s * nblk + a) * hidden + h].  Each sum is formed in binary32
  * (the FLOAT16 case widened the same way, a reading) and rounded once, to
- * nearest even, back to 16 bits.  Payload and bias are finite.
+ * nearest even, back to 16 bits.  Every IEEE class is taken as IEEE 754
+ * gives it: a sum past the format's largest finite value is an infinity,
+ * inf + (-inf) and any NaN operand give a NaN, subnormals add exactly.
  * The checks are check_args's with: bias a sixth operand (NULLPTR when
  * missing, in the pairwise-distinct rule with P*nblk*hidden values), dtype
  * FP16 or BF16 only, hidden >= 1 with the geometry, and every count a
  * multiple of hidden * nblk (whole rows of every sub-block; check 9b).
  * Pinned by: the conversion pins above; a zero bias reduces it to the
- * blocked exchange; the CANN layout relation against numpy / torch adds.
+ * blocked exchange; the CANN layout relation against numpy / torch adds, on
+ * moderate values and on values of every IEEE class (NaN-ness compared where
+ * the result is a NaN).
  */
 int a2av_oracle_run_bias(const void *input, void *target, int32_t *signal,
                          const int32_t *send_counts, int32_t *recv_counts, int32_t P, int32_t S,
@@ -490,12 +566,13 @@ int a2av_oracle_run_bias(const void *input, void *target, int32_t *signal,
                     int64_t bi = ((int64_t)s * nblk + a) * hidden + h;
                     float sum;
                     if (dtype == OR_DTYPE_BF16) {
-                        sum = a2av_oracle_bf16_to_f32(x[src + k]) + ((const float *)bias)[bi];
-                        y[dst + k] = a2av_oracle_f32_to_bf16(sum);
+                        sum = f32_from_bits(a2av_oracle_bf16_to_f32(x[src + k])) +
+                              ((const float *)bias)[bi];
+                        y[dst + k] = a2av_oracle_f32_to_bf16(bits_from_f32(sum));
                     } else {
-                        sum = a2av_oracle_f16_to_f32(x[src + k]) +
-                              a2av_oracle_f16_to_f32(((const uint16_t *)bias)[bi]);
-                        y[dst + k] = a2av_oracle_f32_to_f16(sum);
+                        sum = f32_from_bits(a2av_oracle_f16_to_f32(x[src + k])) +
+                              f32_from_bits(a2av_oracle_f16_to_f32(((const uint16_t *)bias)[bi]));
+                        y[dst + k] = a2av_oracle_f32_to_f16(bits_from_f32(sum));
                     }
                 }
             }

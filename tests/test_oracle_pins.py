@@ -530,41 +530,114 @@ def test_blocked_diagnostics():
 
 # ------------------------------------------------------------------- fused bias Add
 
-def test_bf16_conversions_match_torch():
+def _f32_test_patterns(seed):
+    """binary32 bit patterns for the narrowing pins: random patterns of every
+    exponent, exact ties, f32 subnormals, the 16-bit formats' overflow edges,
+    the infinities and NaNs (quiet, signalling, all-ones fraction, both signs)."""
+    rng = np.random.default_rng(seed)
+    rand = rng.integers(0, 2**32, 60000, dtype=np.uint64).astype(np.uint32)
+    # every exponent field with random sign and fraction
+    expo = (np.arange(256, dtype=np.uint32) << 23)[:, None] | \
+        rng.integers(0, 2**23, (256, 40), dtype=np.uint32) | \
+        (rng.integers(0, 2, (256, 40), dtype=np.uint32) << 31)
+    ties_bf16 = np.concatenate([(np.arange(1, 300, dtype=np.uint32) << 16) | 0x8000,
+                                (np.arange(1, 300, dtype=np.uint32) << 16) | 0x18000])
+    ties_f16 = np.concatenate([
+        ((np.arange(1, 300, dtype=np.float64) + 0.5) * 2.0 ** -24).astype(np.float32).view(np.uint32),
+        (np.arange(1024, 1400, dtype=np.float64) + 0.5).astype(np.float32).view(np.uint32)])
+    vals = np.array([0.0, -0.0, 1.0, -1.0, 65504.0, 65519.0, 65519.99, 65520.0, 65535.0,
+                     70000.0, 131008.0, -65520.0, -70000.0, 1e10, 3.0e38, 3.4028235e38,
+                     6.1e-5, 5.96e-8, 2.98e-8, 2.9802322e-8, 1e-40, -1e-40],
+                    np.float32).view(np.uint32)
+    special = np.array([0x7F800000, 0xFF800000,                 # +-Inf
+                        0x7FC00000, 0xFFC00000,                 # quiet NaNs
+                        0x7F800001, 0xFF800001, 0x7FA00000,     # signalling NaNs
+                        0x7FFFFFFF, 0xFFFFFFFF, 0x7FBFFFFF,     # all-ones fractions
+                        0x00000001, 0x80000001, 0x007FFFFF, 0x807FFFFF, 0x00400000,  # subnormals
+                        0x7F7FFFFF, 0xFF7FFFFF,                 # largest finite binary32
+                        0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001,     # bf16 overflow edge
+                        0x7F7E8000, 0xFF7F8000], np.uint32)
+    return np.concatenate([rand, expo.ravel(), ties_bf16, ties_f16, vals, special])
+
+
+def _assert_same_or_both_nan(got, want, is_nan):
+    nan_g, nan_w = is_nan(got), is_nan(want)
+    np.testing.assert_array_equal(nan_g, nan_w)
+    np.testing.assert_array_equal(got[~nan_w], want[~nan_w])
+
+
+def _bf16_is_nan(h):
+    h = np.asarray(h, np.uint32)
+    return ((h >> 7) & 0xFF == 0xFF) & (h & 0x7F != 0)
+
+
+def _f16_is_nan(h):
+    h = np.asarray(h, np.uint32)
+    return ((h >> 10) & 0x1F == 0x1F) & (h & 0x3FF != 0)
+
+
+def _f32_is_nan(u):
+    u = np.asarray(u, np.uint32)
+    return ((u >> 23) & 0xFF == 0xFF) & (u & 0x7FFFFF != 0)
+
+
+def test_bf16_narrowing_matches_torch():
+    # torch's CPU float32 -> bfloat16 rounds to nearest even, overflows to
+    # infinity and returns a NaN for a NaN: the same results as IEEE 754's
+    # rules applied to the bfloat16 layout (NaN-ness compared for NaNs).
     import torch
-    rng = np.random.default_rng(5)
-    vals = np.concatenate([
-        rng.standard_normal(4000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 4000),
-        # exact ties: kept part even and odd
-        (np.arange(1, 200, dtype=np.uint32) << 16 | 0x8000).view(np.float32),
-        ((np.arange(1, 200, dtype=np.uint32) << 16) | 0x18000).view(np.float32),
-        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, 1e-40, -1e-40], np.float32),
-    ]).astype(np.float32)
-    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    got = np.array([oracle.f32_to_bf16(float(v)) for v in vals], np.uint16)
-    np.testing.assert_array_equal(got, want)
-    back = torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().numpy()
-    got_back = np.array([oracle.bf16_to_f32(int(h)) for h in want], np.float32)
-    np.testing.assert_array_equal(got_back.view(np.uint32), back.view(np.uint32))
+    bits = _f32_test_patterns(5)
+    want = torch.from_numpy(bits.view(np.float32)).to(torch.bfloat16).view(torch.int16)
+    want = want.numpy().view(np.uint16)
+    got = oracle.f32_to_bf16_array(bits)
+    _assert_same_or_both_nan(got, want, _bf16_is_nan)
+    # The named edges, stated: the largest finite bfloat16 is 0x7F7F; half an
+    # ulp above it is a tie that rounds to the even neighbour, infinity.
+    assert oracle.f32_to_bf16(0x7F7F7FFF) == 0x7F7F
+    assert oracle.f32_to_bf16(0x7F7F8000) == 0x7F80
+    assert oracle.f32_to_bf16(0xFF7F8000) == 0xFF80
+    assert oracle.f32_to_bf16(0x7F800000) == 0x7F80 and oracle.f32_to_bf16(0xFF800000) == 0xFF80
+    for nan in (0x7FFFFFFF, 0xFFFFFFFF, 0x7F800001, 0xFF800001):
+        h = oracle.f32_to_bf16(nan)
+        assert _bf16_is_nan(h) and (h >> 15) == (nan >> 31) and h & 0x40, hex(h)
 
 
-def test_f16_conversions_match_numpy():
-    rng = np.random.default_rng(6)
-    vals = np.concatenate([
-        rng.standard_normal(4000).astype(np.float32) * 2.0 ** rng.integers(-26, 15, 4000),
-        # exact ties in the normal and subnormal ranges
-        (np.arange(1, 300, dtype=np.float64) + 0.5).astype(np.float32) * np.float32(2.0 ** -24),
-        (np.arange(1024, 1400, dtype=np.float64) + 0.5).astype(np.float32),
-        np.array([0.0, -0.0, 65504.0, 6.1e-5, 5.96e-8, 2.98e-8, 65519.0], np.float32),
-    ]).astype(np.float32)
-    want = vals.astype(np.float16).view(np.uint16)
-    got = np.array([oracle.f32_to_f16(float(v)) for v in vals], np.uint16)
-    np.testing.assert_array_equal(got, want)
-    halves = np.concatenate([np.arange(0, 0x7C00, 7, dtype=np.uint16),
-                             np.arange(0x8000, 0xFC00, 13, dtype=np.uint16)])
-    back = np.array([oracle.f16_to_f32(int(h)) for h in halves], np.float32)
-    np.testing.assert_array_equal(back.view(np.uint32),
-                                  halves.view(np.float16).astype(np.float32).view(np.uint32))
+def test_bf16_widening_exhaustive_against_torch():
+    import torch
+    halves = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = torch.from_numpy(halves.view(np.int16)).view(torch.bfloat16).float().numpy()
+    got = oracle.bf16_to_f32_array(halves)
+    _assert_same_or_both_nan(got, want.view(np.uint32), _f32_is_nan)
+
+
+def test_f16_narrowing_matches_numpy():
+    # numpy's float32 -> float16 follows IEEE 754: round to nearest even,
+    # overflow to infinity, NaN to NaN (NaN-ness compared for NaNs).
+    bits = _f32_test_patterns(6)
+    with np.errstate(over="ignore", invalid="ignore"):
+        want = bits.view(np.float32).astype(np.float16).view(np.uint16)
+    got = oracle.f32_to_f16_array(bits)
+    _assert_same_or_both_nan(got, want, _f16_is_nan)
+    f = lambda v: oracle.f32_to_f16(int(np.array([v], np.float32).view(np.uint32)[0]))
+    assert f(65504.0) == 0x7BFF and f(65519.0) == 0x7BFF    # largest finite binary16
+    assert f(65520.0) == 0x7C00 and f(70000.0) == 0x7C00    # the tie and beyond: overflow
+    assert f(131008.0) == 0x7C00 and f(-70000.0) == 0xFC00
+    assert oracle.f32_to_f16(0x7F800000) == 0x7C00 and oracle.f32_to_f16(0xFF800000) == 0xFC00
+    for nan in (0x7FFFFFFF, 0xFFFFFFFF, 0x7F800001, 0xFF800001):
+        h = oracle.f32_to_f16(nan)
+        assert _f16_is_nan(h) and (h >> 15) == (nan >> 31) and h & 0x200, hex(h)
+    assert oracle.f32_to_f16(0x00000001) == 0 and oracle.f32_to_f16(0x80000001) == 0x8000
+
+
+def test_f16_widening_exhaustive_against_numpy():
+    halves = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = halves.view(np.float16).astype(np.float32).view(np.uint32)
+    got = oracle.f16_to_f32_array(halves)
+    _assert_same_or_both_nan(got, want, _f32_is_nan)
+    # Non-NaN results are exact, and NaN keeps its sign and payload.
+    assert oracle.f16_to_f32(0x7C00) == 0x7F800000 and oracle.f16_to_f32(0xFC00) == 0xFF800000
+    assert oracle.f16_to_f32(0x7DFF) == 0x7F800000 | (0x1FF << 13)
+    assert oracle.f16_to_f32(0xFFFF) == 0xFF800000 | (0x3FF << 13)
 
 
 def _bias_case(P, nblk, hidden, rows, dtype, seed=3, bias=None, pad=32):
@@ -635,6 +708,46 @@ def test_bias_cann_flow_against_torch(dtype):
     y = temp3.view(P, A, P, Cr * Hd).permute(2, 0, 1, 3).contiguous()
     want = y.view(torch.int16).numpy().reshape(-1).view(np.uint8)
     np.testing.assert_array_equal(tgt, want)
+
+
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP16])
+def test_bias_every_ieee_class_against_torch(dtype):
+    # [CANN]'s flow (fp32 add, round to the payload type, permute) computed by
+    # torch on payloads and biases that reach every IEEE class: overflowing
+    # sums (65504 + 65504 in FP16, the top binade of BF16 plus a large FP32
+    # bias) become infinities, inf + (-inf) and any NaN operand give a NaN,
+    # subnormals add exactly.  Non-NaN elements bit for bit; NaN elements
+    # NaN on both sides.
+    import torch
+    P, A, Cr, Hd = 4, 2, 3, 64
+    C = np.full((P, P), A * Cr * Hd, np.int32)
+    slab = P * A * Cr * Hd * 2
+    words = wl.random_bytes_np(91, 0, P * slab).view(np.uint16)
+    x16 = wl.edge16_from_words(words, dtype)
+    bias = wl.edge_bias_values(92, P, A, Hd, dtype)
+    st, tgt, _, _ = _run_bias(C, P, slab, slab, x16.view(np.uint8).copy(), bias, dtype, A, Hd)
+    assert st == oracle.OK
+    tdt = torch.bfloat16 if dtype == oracle.BF16 else torch.float16
+    x = torch.from_numpy(x16.view(np.int16)).view(tdt).float().view(P, A, P * Cr, Hd)
+    if dtype == oracle.BF16:
+        b = torch.from_numpy(bias)
+    else:
+        b = torch.from_numpy(bias.view(np.int16)).view(torch.float16).float()
+    temp3 = (x + b.view(P, A, 1, Hd)).to(tdt)
+    y = temp3.view(P, A, P, Cr * Hd).permute(2, 0, 1, 3).contiguous()
+    want = y.view(torch.int16).numpy().reshape(-1).view(np.uint16)
+    got = tgt.view(np.uint16)
+    is_nan = _bf16_is_nan if dtype == oracle.BF16 else _f16_is_nan
+    _assert_same_or_both_nan(got, want, is_nan)
+    # The classes were all met: infinities from finite operands (overflow),
+    # NaNs, subnormal results.
+    xb = x.numpy()
+    bb = np.broadcast_to(b.view(P, A, 1, Hd).numpy(), xb.shape)
+    t3 = temp3.float().numpy()
+    assert (np.isinf(t3) & np.isfinite(xb) & np.isfinite(bb)).any()
+    assert np.isnan(t3).any()
+    tiny = 2.0 ** -126 if dtype == oracle.BF16 else 2.0 ** -14
+    assert ((t3 != 0) & (np.abs(t3) < tiny)).any()
 
 
 def test_bias_diagnostics():
