@@ -270,13 +270,19 @@ class Exchange:
 
     def run(self, input, target, signal, send_counts, recv_counts, core_num: int, dtype: int,
             stream=None, nblk: int = 1, bias=None, hidden: int = 0, index=None,
-            row_elems: int = 0) -> None:
+            row_elems: int = 0, check: bool = False) -> None:
         """One exchange; ``nblk`` > 1 runs the blocked exchange (a2av_run_blocked);
         a ``bias`` tensor (float32 for BF16 payloads, float16 for FP16, [P, nblk,
         hidden] elements) runs the exchange with the bias Add fused in
         (a2av_run_bias); an ``index`` tensor (int32 [P, index_stride] gather
         lists of rows of ``row_elems`` elements) runs the indexed exchange
-        (a2av_run_indexed)."""
+        (a2av_run_indexed).
+
+        The count and signal checks run on the device, so by default a
+        failure is latched and reported by :meth:`query_error`.  With
+        ``check=True`` the call waits for the run and raises on a device-side
+        failure (ValueError for INVALID_ARGS / OVER_CAPACITY, A2avError for
+        TIMEOUT), as if the checks had run before the call returned."""
         import torch
         c = self.cfg
         P = c.P
@@ -308,6 +314,8 @@ class Exchange:
             st = a2av_run_blocked(self.h, ip, tp, sp, scp, rcp, P, core_num, dtype, nblk,
                                   stream.cuda_stream)
         _raise(st, "a2av_run", self.h)
+        if check:
+            _raise(self.query_error(), "a2av_run (device-side checks)", self.h)
 
     def query_error(self) -> int:
         return a2av_query_error(self.h)

@@ -57,6 +57,7 @@ struct CountParams {
   const int32_t* index;
   int64_t index_stride;
   int64_t table_rows;
+  int64_t payload_cap;  // bytes the run's launches cover; a larger payload is refused
 };
 
 struct CopyParams {

@@ -158,7 +158,12 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
         if (p.index != nullptr ? acc / unit > p.index_stride : bytes > p.in_slab)
           atomicOr(&flags, 2);
       }
-      if (lane == kWave - 1) rowbase[kMaxP] = incl;
+      if (lane == kWave - 1) {
+        rowbase[kMaxP] = incl;
+        // Never reached when every row and column fits (the launches cover
+        // P times the smaller slab, or P target slabs for the row gather).
+        if (incl > p.payload_cap) atomicOr(&flags, 2);
+      }
     } else if (lane < P) {
       colbase[lane] = incl - bytes;
       if (bytes > p.tgt_slab) atomicOr(&flags, 2);

@@ -50,13 +50,17 @@ int check_indexed_args(const a2av_config* cfg, int64_t capacity, const void* inp
                        const int32_t* recv_counts, const int32_t* index, int32_t P,
                        int64_t core_num, int32_t dtype, int32_t row_elems, int64_t index_stride);
 
-// Upper bound of the payload of any valid run: every row fits its input slab
-// and every column its target slab, so T <= P * min(in_slab, tgt_slab).
-int64_t max_payload(const a2av_config* cfg);
+// Upper bound of the payload of any valid run.  Every destination column
+// fits its target slab, so T <= P * tgt_slab always; in the exchanges that
+// read each input byte at most once every source row also fits its input
+// slab, so T <= P * min(in_slab, tgt_slab).  The row gather (`gather`) may
+// name a row any number of times: only the target bound holds there.
+int64_t max_payload(const a2av_config* cfg, bool gather = false);
 
 // K2 launches per run: enough chunks of `limit` bytes to cover max_payload.
-// The device skips the part of a chunk past the run's real payload.
-int32_t chunk_launches(const a2av_config* cfg, int64_t limit);
+// Launch c copies the flattened payload bytes [c * limit, (c + 1) * limit);
+// the device skips the part of a chunk past the run's real payload.
+int32_t chunk_launches(const a2av_config* cfg, int64_t limit, bool gather = false);
 
 // Workgroups that execute one admitted block.  `requested` > 0 is taken as
 // is (clamped to the capacity); 0 picks enough to cover `target_wgs`

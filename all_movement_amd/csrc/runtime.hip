@@ -40,6 +40,7 @@ struct a2av_handle {
   // Event sets of the last kProfileRuns runs: per run [0] before K1, [1] after
   // K1, [2] after the last K2 launch (one marker per K2 launch cost c5 ~1 %).
   std::vector<hipEvent_t> events;
+  std::vector<int32_t> run_launches;  // K2 launches of each recorded run
   int32_t events_per_run = 0;
   int64_t profiled_runs = 0;  // runs recorded since the last a2av_profile_read
   int64_t run_counter = 0;    // runs recorded
@@ -81,6 +82,34 @@ int hip_fail(a2av_handle* h, hipError_t e, const char* what) {
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// The workspace of a run for P ranks and up to `capacity` admitted blocks:
+// plan words, prefix[P*P+1], src_off[P*P], dst_off[P*P], blk_cnt[max(1,
+// capacity)], sstride[P], the arrival counter copies, each 256-byte aligned.
+// Returns its size in bytes; with a base address, also fills *ws.
+size_t carve_workspace(char* base, int32_t P, int64_t capacity, a2av::Workspace* ws) {
+  const size_t PP = size_t(P) * size_t(P);
+  const size_t max_blocks = size_t(capacity > 1 ? capacity : 1);
+  size_t off = 0;
+  const size_t o_plan = off; off = round_up(off + sizeof(a2av::RunPlan), 256);
+  const size_t o_prefix = off; off = round_up(off + (PP + 1) * sizeof(int64_t), 256);
+  const size_t o_src = off; off = round_up(off + PP * sizeof(int64_t), 256);
+  const size_t o_dst = off; off = round_up(off + PP * sizeof(int64_t), 256);
+  const size_t o_cnt = off; off = round_up(off + max_blocks * sizeof(uint32_t), 256);
+  const size_t o_str = off; off = round_up(off + size_t(P) * sizeof(int64_t), 256);
+  const size_t o_arr = off;
+  off = round_up(off + size_t(a2av::kArriveReplicas) * a2av::kArriveStride * sizeof(uint32_t), 256);
+  if (base && ws) {
+    ws->plan = reinterpret_cast<a2av::RunPlan*>(base + o_plan);
+    ws->prefix = reinterpret_cast<int64_t*>(base + o_prefix);
+    ws->src_off = reinterpret_cast<int64_t*>(base + o_src);
+    ws->dst_off = reinterpret_cast<int64_t*>(base + o_dst);
+    ws->blk_cnt = reinterpret_cast<uint32_t*>(base + o_cnt);
+    ws->sstride = reinterpret_cast<int64_t*>(base + o_str);
+    ws->arrived = reinterpret_cast<uint32_t*>(base + o_arr);
+  }
+  return off;
+}
 
 }  // namespace
 
@@ -154,37 +183,18 @@ int a2av_create(a2av_handle** out, const a2av_config* cfg) {
   h->launches = a2av::chunk_launches(cfg, h->chunk_limit);
   h->spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
 
-  // Workspace: plan words, prefix[P*P+1], src_off[P*P], dst_off[P*P],
-  // blk_cnt[max(1, capacity)], sstride[P], the arrival counter copies, each
-  // 256-byte aligned.
-  const size_t PP = size_t(cfg->P) * size_t(cfg->P);
-  const size_t max_blocks = size_t(h->capacity > 1 ? h->capacity : 1);
-  size_t off = 0;
-  const size_t o_plan = off; off = round_up(off + sizeof(a2av::RunPlan), 256);
-  const size_t o_prefix = off; off = round_up(off + (PP + 1) * sizeof(int64_t), 256);
-  const size_t o_src = off; off = round_up(off + PP * sizeof(int64_t), 256);
-  const size_t o_dst = off; off = round_up(off + PP * sizeof(int64_t), 256);
-  const size_t o_cnt = off; off = round_up(off + max_blocks * sizeof(uint32_t), 256);
-  const size_t o_str = off; off = round_up(off + size_t(cfg->P) * sizeof(int64_t), 256);
-  const size_t o_arr = off;
-  off = round_up(off + size_t(a2av::kArriveReplicas) * a2av::kArriveStride * sizeof(uint32_t), 256);
-  e = hipMalloc(&h->ws_mem, off);
+  const size_t bytes = carve_workspace(nullptr, cfg->P, h->capacity, nullptr);
+  e = hipMalloc(&h->ws_mem, bytes);
   if (e != hipSuccess) { delete h; return A2AV_ERR_HIP; }
-  e = hipMemset(h->ws_mem, 0, off);
+  e = hipMemset(h->ws_mem, 0, bytes);
   if (e != hipSuccess) { (void)hipFree(h->ws_mem); delete h; return A2AV_ERR_HIP; }
-  char* base = static_cast<char*>(h->ws_mem);
-  h->ws.plan = reinterpret_cast<a2av::RunPlan*>(base + o_plan);
-  h->ws.prefix = reinterpret_cast<int64_t*>(base + o_prefix);
-  h->ws.src_off = reinterpret_cast<int64_t*>(base + o_src);
-  h->ws.dst_off = reinterpret_cast<int64_t*>(base + o_dst);
-  h->ws.blk_cnt = reinterpret_cast<uint32_t*>(base + o_cnt);
-  h->ws.sstride = reinterpret_cast<int64_t*>(base + o_str);
-  h->ws.arrived = reinterpret_cast<uint32_t*>(base + o_arr);
+  carve_workspace(static_cast<char*>(h->ws_mem), cfg->P, h->capacity, &h->ws);
 
   h->profile = (cfg->flags & A2AV_FLAG_PROFILE) != 0;
   if (h->profile) {
     h->events_per_run = 3;
     h->events.resize(size_t(h->events_per_run) * kProfileRuns, nullptr);
+    h->run_launches.assign(size_t(kProfileRuns), 0);
     for (auto& ev : h->events) {
       e = hipEventCreate(&ev);
       if (e != hipSuccess) { a2av_destroy(h); return A2AV_ERR_HIP; }
@@ -251,6 +261,11 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   a2av_launch_info li;
   int st = a2av_launch_info_get(h, core_num, &li);
   if (st != A2AV_OK) return st;
+  // The row gather's payload is bounded by the target slabs only (a row may
+  // be named many times), so it may need more launches than the handle's
+  // plan for the other exchanges.
+  const int32_t launches =
+      mode == 3 ? a2av::chunk_launches(&h->cfg, h->chunk_limit, true) : h->launches;
 
   DeviceGuard guard(h->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -278,6 +293,11 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   } else {
     cp.unit = int64_t(nblk) * (mode != 0 ? x.hidden : 1);
   }
+  // What the launches can cover; a payload beyond it (which the capacity
+  // checks already rule out) is refused on the device rather than copied in
+  // part.
+  cp.payload_cap = h->chunk_limit > INT64_MAX / launches ? INT64_MAX
+                                                         : int64_t(launches) * h->chunk_limit;
 
   // Profiling events are not recorded while the stream is being captured
   // into a graph: the host tally counts enqueued runs, and a graph's replays
@@ -321,12 +341,13 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   // Chunks are issued from the highest to chunk 0.  Chunks past the run's
   // payload cost only a plain launch that exits at once, and the final launch
   // (the one that raises the flags, cooperative when B > 1) is chunk 0, which
-  // holds payload whenever the run has any.
-  for (int32_t n = 0; n < h->launches; ++n) {
-    const int32_t c = h->launches - 1 - n;
+  // holds payload whenever the run has any.  Launch c copies at most the
+  // limit: the flattened bytes [c * limit, (c + 1) * limit).
+  for (int32_t n = 0; n < launches; ++n) {
+    const int32_t c = launches - 1 - n;
     const bool last = (c == 0);
     kp.chunk_lo = int64_t(c) * h->chunk_limit;
-    kp.chunk_hi = (c == h->launches - 1) ? INT64_MAX : int64_t(c + 1) * h->chunk_limit;
+    kp.chunk_hi = int64_t(c + 1) * h->chunk_limit;
     kp.chunk = c;
     kp.last = last ? 1 : 0;
     kp.wait = (last && li.blocks > 1) ? 1 : 0;
@@ -335,6 +356,7 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   }
   if (ev) {
     if ((e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+    h->run_launches[size_t(h->run_counter % kProfileRuns)] = launches;
     ++h->run_counter;
     ++h->profiled_runs;
   }
@@ -423,8 +445,10 @@ int a2av_profile_read(a2av_handle* h, double* k1_us, double* k2_us, int32_t* k2_
   DeviceGuard guard(h->device);
   const int64_t n = h->profiled_runs < kProfileRuns ? h->profiled_runs : kProfileRuns;
   double t1 = 0.0, t2 = 0.0;
+  int64_t nl = 0;
   for (int64_t k = 0; k < n; ++k) {
     const int64_t run = h->run_counter - 1 - k;
+    nl += h->run_launches[size_t(run % kProfileRuns)];
     hipEvent_t* ev = &h->events[size_t(run % kProfileRuns) * size_t(h->events_per_run)];
     hipError_t e = hipEventSynchronize(ev[h->events_per_run - 1]);
     if (e != hipSuccess) return hip_fail(h, e, "hipEventSynchronize");
@@ -438,7 +462,7 @@ int a2av_profile_read(a2av_handle* h, double* k1_us, double* k2_us, int32_t* k2_
   }
   *k1_us = t1;
   *k2_us = t2;
-  *k2_launches = int32_t(n * h->launches);
+  *k2_launches = int32_t(nl);
   *runs = int32_t(n);
   h->profiled_runs = 0;
   return A2AV_OK;
@@ -455,3 +479,4 @@ int a2av_profile_sample(a2av_handle* h, int32_t every) {
 const char* a2av_last_hip_error(a2av_handle* h) { return h ? h->last_error.c_str() : ""; }
 
 }  // extern "C"
+

@@ -230,7 +230,10 @@ int a2av_run_indexed(a2av_handle *h, const void *input, void *target, int32_t *s
                      int64_t index_stride, void *stream);
 
 /* Free the workspace and the handle (synchronizes the device first).
- * NULL is accepted and ignored. */
+ * NULL is accepted and ignored.  The end of the create/run/destroy life
+ * cycle: the CANN BatchMatMulReduceScatterAllToAll page ("Full example",
+ * step 4) frees the workspace memory once the two-phase calls are done and
+ * the stream has been synchronized. */
 int a2av_destroy(a2av_handle *h);
 
 /* CalAllToAllVBlocks(P, L): L when L < P, else the largest multiple of P not
@@ -263,10 +266,25 @@ int a2av_check_indexed_args(const a2av_config *cfg, int64_t capacity, const void
 
 /* Wait for the handle's last stream, then return and clear the latched
  * device-side status (A2AV_OK when every run since the last query was valid;
- * otherwise the first failure: INVALID_ARGS, OVER_CAPACITY or TIMEOUT). */
+ * otherwise the first failure: INVALID_ARGS, OVER_CAPACITY or TIMEOUT).
+ * The latch follows the runtime fallback of the PyPTO page ("Current
+ * limitations"): checks that can only run once the operands exist latch an
+ * INVALID_ARGS status at the first violation instead of failing the call
+ * that submitted the work.  Here the count and signal checks run on the
+ * device, so a2av_run returns before their outcome is known; a caller that
+ * needs it synchronously calls this function after the run.  This is a
+ * departure from checking the counts on the host before any write, made so
+ * that a run needs no device-to-host read-back. */
 int a2av_query_error(a2av_handle *h);
 
-/* Fill *out with what a run with `core_num` would launch.  Errors: NULLPTR,
+/* Fill *out with what a run of a2av_run, a2av_run_blocked or a2av_run_bias
+ * with `core_num` would launch: the admitted blocks B (CalAllToAllVBlocks,
+ * "Launch width" section of the PyPTO page, which also refuses a
+ * sync-start launch beyond the co-resident capacity instead of launching
+ * part of it), the workgroups that run them, and the chunk launches of at
+ * most chunk_limit_bytes each (the re-enqueue above 1 GB of section 2 of the
+ * vccl alltoallv dev log).  a2av_run_indexed may take more chunk launches:
+ * its payload is bounded by P target slabs only.  Errors: NULLPTR,
  * INVALID_ARGS (core_num out of range), LAUNCH_CAPACITY. */
 int a2av_launch_info_get(a2av_handle *h, int64_t core_num, a2av_launch_info *out);
 
@@ -287,7 +305,10 @@ int a2av_profile_read(a2av_handle *h, double *k1_us, double *k2_us, int32_t *k2_
  * INVALID_ARGS (every < 1, or a handle created without profiling). */
 int a2av_profile_sample(a2av_handle *h, int32_t every);
 
-/* Human-readable name of a status code (static storage). */
+/* Human-readable name of a status code (static storage), in the spirit of
+ * the aclnn error table on the CANN page ("Two-phase API": a named status
+ * per failure class, NULLPTR apart from INVALID).  Unknown codes give
+ * "A2AV_ERR_UNKNOWN". */
 const char *a2av_status_string(int status);
 
 /* Text of the last failing HIP call on this handle ("" if none). */

@@ -176,6 +176,51 @@ def test_bias_device_rejections_match_oracle(dtype):
     check_bias(w2, nblk, hidden)
 
 
+def _is_nan16(h: np.ndarray, dtype: int) -> np.ndarray:
+    h = h.astype(np.uint32)
+    if dtype == wl.BF16:
+        return ((h >> 7) & 0xFF == 0xFF) & (h & 0x7F != 0)
+    return ((h >> 10) & 0x1F == 0x1F) & (h & 0x3FF != 0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("P,hidden", [(3, 24), (8, 2048), (2, 8200)])
+def test_bias_every_ieee_class(P, hidden, dtype):
+    # Payloads and biases that reach every IEEE class: sums that overflow to
+    # infinity (65504 + 65504 in FP16; the top BF16 binade plus a large FP32
+    # bias), infinities of both signs, inf + (-inf), NaN operands (quiet,
+    # signalling, all-ones fractions), subnormals and zeros.  Against the
+    # oracle: every element bit for bit where the oracle's result is not a
+    # NaN, a NaN where it is (IEEE 754 leaves the NaN's payload open); the
+    # sentinel tails, the signal and recv_counts exactly.
+    nblk = 2
+    rows = 6 if hidden >= 2048 else 40
+    w = bias_case(P, nblk, hidden, rows, dtype, core_num=2 * P, seed=31 + P)
+    x = wl.edge16_from_words(wl.random_bytes_np(w.payload_seed, 0, w.in_bytes).view(np.uint16),
+                             dtype)
+    bn = wl.edge_bias_values(w.payload_seed + 7, P, nblk, hidden, dtype)
+    bt = torch.from_numpy(bn.view(np.float16) if dtype == wl.FP16 else bn).to(DEV)
+    c = Case(w, input_np=x.view(np.uint8))
+    ex = exchange_for(w)
+    try:
+        say("P", P, "hidden", hidden, "dtype", dtype, "payload", w.payload_bytes)
+        st = c.run_gpu(ex, nblk=nblk, bias=bt, hidden=hidden)
+    finally:
+        ex.close()
+    st_o, tgt_o, sig_o, rc_o = c.run_oracle(nblk=nblk, bias=bn, hidden=hidden)
+    assert st == st_o == a2av.OK
+    got = c.target.cpu().numpy().view(np.uint16)
+    want = tgt_o.view(np.uint16)
+    nan_w = _is_nan16(want, dtype)
+    np.testing.assert_array_equal(_is_nan16(got, dtype), nan_w)
+    bad = np.nonzero(got[~nan_w] != want[~nan_w])[0]
+    assert bad.size == 0, (bad.size, [hex(v) for v in got[~nan_w][bad[:4]]],
+                           [hex(v) for v in want[~nan_w][bad[:4]]])
+    np.testing.assert_array_equal(c.signal.cpu().numpy(), sig_o)
+    np.testing.assert_array_equal(c.recv.cpu().numpy(), rc_o)
+    assert nan_w.any() and (want == (0x7C00 if dtype == wl.FP16 else 0x7F80)).any()
+
+
 def _row_expected(x_row: np.ndarray, b_row: np.ndarray, dtype: int) -> np.ndarray:
     """One row plus its bias by the oracle: a one-rank, one-row exchange."""
     H = b_row.size
@@ -198,12 +243,14 @@ def test_bias_workload_scaled_full_oracle(dtype):
     check_bias(w, A, H)
 
 
-def test_bias_workload_full_size():
-    # 4 GiB of BF16 payload with the FP32 bias, the launch configuration the
-    # benchmark times.  Checked three ways: sampled rows against the oracle
-    # one row at a time; every element against torch's own fp32 add and
-    # round-to-nearest-even bf16 cast; counts and flags.
-    w = wl.bias_workload(wl.BF16)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bias_workload_full_size(dtype):
+    # 4 GiB of BF16 payload with the FP32 bias, or of FP16 payload with the
+    # FP16 bias, in the launch configuration the benchmark times.  Checked
+    # three ways: sampled rows against the oracle one row at a time; every
+    # element against torch's own fp32 add and round-to-nearest-even cast to
+    # the payload type; counts and flags.
+    w = wl.bias_workload(dtype)
     P, A, H, Cn = w.P, w.extra["nblk"], w.extra["hidden"], w.extra["C"]
     say(w.name, w.payload_bytes)
     inp = wl.input16_tensor(w, DEV)
@@ -234,10 +281,12 @@ def test_bias_workload_full_size():
         want = _row_expected(x_row, bn[s, a], w.dtype)
         got = tgt[dst:dst + row].cpu().numpy()
         assert np.array_equal(got, want), (d, s, a, r)
-    x = inp.view(torch.bfloat16).view(P, A, P, Cn, H)
-    y = tgt.view(torch.bfloat16).view(P, P, A, Cn, H)
+    tdt = torch.bfloat16 if dtype == wl.BF16 else torch.float16
+    x = inp.view(tdt).view(P, A, P, Cn, H)
+    y = tgt.view(tdt).view(P, P, A, Cn, H)
+    bf = bt.float().view(P, A, 1, H)
     for d in range(P):
-        want = (x[:, :, d].float() + bt.view(P, A, 1, H)).to(torch.bfloat16)
+        want = (x[:, :, d].float() + bf).to(tdt)
         assert torch.equal(y[d].view(torch.int16), want.view(torch.int16)), d
 
 

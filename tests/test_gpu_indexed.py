@@ -79,8 +79,24 @@ def test_indexed_sweep(P, R, dtype):
 @pytest.mark.parametrize("limit", [4096, 1000])
 def test_indexed_small_chunks_and_two_runs(limit):
     # 1000 is not a multiple of 16: the byte-exact path even for aligned rows.
+    # Rows are named up to twice, so the payload exceeds P * in_slab: the
+    # launches must still cover it at no more than `limit` bytes each (the
+    # plan covers P * tgt_slab, and launch c copies [c * limit, (c+1) * limit)).
     w, index = indexed_case(4, 64, wl.INT8, 40, 30, core_num=8, seed=limit)
-    check_indexed(w, index, 64, runs=2, chunk_limit_bytes=limit)
+    assert w.payload_bytes > w.P * w.in_slab
+    c = check_indexed(w, index, 64, runs=2, chunk_limit_bytes=limit, profile=True)
+    del c
+    ex = exchange_for(w, chunk_limit_bytes=limit, profile=True)
+    try:
+        c2 = Case(w)
+        c2.run_gpu(ex, index=upload(index), row_elems=64)
+        _, _, launches, runs = ex.profile()
+        assert runs == 1
+        say("payload", w.payload_bytes, "limit", limit, "launches", launches)
+        assert launches * limit >= w.payload_bytes
+        assert launches == -(-w.P * w.tgt_slab // limit)
+    finally:
+        ex.close()
 
 
 def test_indexed_unaligned_operands_and_partial_last_row():

@@ -191,6 +191,44 @@ def test_error_then_valid_run_reports_first_error_once():
         ex.close()
 
 
+def test_run_with_check_raises_on_device_side_errors():
+    # Exchange.run(check=True) waits for the run and raises on the latched
+    # device-side status: a negative count (INVALID_ARGS) and an over-full
+    # column (OVER_CAPACITY) raise ValueError with nothing written; a valid
+    # run returns normally and matches the oracle.
+    P = 4
+    good = wl.custom(P, wl.FP32, np.full((P, P), 2, np.int32), core_num=8)
+    ex = exchange_for(good)
+    try:
+        C = good.counts.copy()
+        C[1, 2] = -3
+        bad = wl.custom(P, wl.FP32, C, core_num=8, in_slab=good.in_slab, tgt_slab=good.tgt_slab)
+        cb = Case(bad)
+        with pytest.raises(ValueError, match="INVALID_ARGS"):
+            ex.run(cb.input, cb.target, cb.signal, cb.send, cb.recv, 8, wl.FP32, check=True)
+        C2 = good.counts.copy()
+        C2[3, 0] += 1                                   # column 0 past the target slab
+        over = wl.custom(P, wl.FP32, C2, core_num=8, in_slab=good.in_slab + 16,
+                         tgt_slab=good.tgt_slab)
+        assert int(C2[:, 0].sum()) * 4 > good.tgt_slab
+        co = Case(over)
+        ex2 = exchange_for(over)
+        try:
+            with pytest.raises(ValueError, match="OVER_CAPACITY"):
+                ex2.run(co.input, co.target, co.signal, co.send, co.recv, 8, wl.FP32, check=True)
+        finally:
+            ex2.close()
+        for c in (cb, co):
+            torch.cuda.synchronize()
+            assert (c.target.cpu().numpy() == wl.SENTINEL).all()
+            assert (c.signal.cpu().numpy() == 0).all()
+        cg = Case(good)
+        ex.run(cg.input, cg.target, cg.signal, cg.send, cg.recv, 8, wl.FP32, check=True)
+        cg.assert_matches(a2av.OK, cg.run_oracle())
+    finally:
+        ex.close()
+
+
 def test_tiny_spin_limit_latches_timeout_and_the_run_still_completes():
     # The arrival wait is bounded by the handle's spin limit.  With a limit of
     # 1 the first workgroups to arrive give up after two polls (they finish
