@@ -35,6 +35,7 @@ ELEM_SIZE = {FP32: 4, INT8: 1, FP16: 2, BF16: 2}
 FLAG_PROFILE = 1
 
 EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_run_bias", "a2av_run_indexed",
+           "a2av_run_noalloc",
            "a2av_check_bias_args", "a2av_check_indexed_args", "a2av_destroy",
            "a2av_blocks", "a2av_check_args", "a2av_query_error", "a2av_launch_info_get", "a2av_profile_read",
            "a2av_profile_sample", "a2av_status_string", "a2av_last_hip_error"]
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.a2av_run_bias.restype = ctypes.c_int
     L.a2av_run_indexed.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i64, vp]
     L.a2av_run_indexed.restype = ctypes.c_int
+    L.a2av_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i32, i64, i32, vp]
+    L.a2av_run_noalloc.restype = ctypes.c_int
     L.a2av_destroy.argtypes = [vp]
     L.a2av_destroy.restype = ctypes.c_int
     L.a2av_blocks.argtypes = [i64, i64]
@@ -139,6 +142,12 @@ def a2av_run_indexed(h, input, target, signal, send_counts, recv_counts, index, 
                      dtype, row_elems, index_stride, stream) -> int:
     return lib().a2av_run_indexed(h, input, target, signal, send_counts, recv_counts, index, P,
                                   core_num, dtype, row_elems, index_stride, stream)
+
+
+def a2av_run_noalloc(input, target, signal, send_counts, recv_counts, status, P, in_slab_bytes,
+                     tgt_slab_bytes, S, core_num, dtype, stream) -> int:
+    return lib().a2av_run_noalloc(input, target, signal, send_counts, recv_counts, status, P,
+                                  in_slab_bytes, tgt_slab_bytes, S, core_num, dtype, stream)
 
 
 def a2av_destroy(h) -> int:

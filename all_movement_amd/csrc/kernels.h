@@ -58,6 +58,7 @@ struct CountParams {
   int64_t index_stride;
   int64_t table_rows;
   int64_t payload_cap;  // bytes the run's launches cover; a larger payload is refused
+  int32_t* status_out;  // if set: receives the run's device-side status (0 = valid)
 };
 
 struct CopyParams {
@@ -85,6 +86,7 @@ struct CopyParams {
   int32_t last;       // 1 on the run's final launch: raise the block flags
   int32_t wait;       // 1 when the final launch is cooperative (B > 1): wait for all blocks
   int32_t spin_limit;
+  int32_t* status_out;  // if set: receives TIMEOUT when the block barrier times out
 };
 
 constexpr int kCountThreads = 1024;

@@ -201,6 +201,7 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
                                : A2AV_ERR_INVALID_ARGS;
       atomicCAS(&p.ws.plan->error, 0, code);
       p.ws.plan->valid = 0;
+      if (p.status_out) *p.status_out = code;
     }
     return;
   }
@@ -267,6 +268,7 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     p.ws.plan->claim[0] = 0u;
     p.ws.plan->claim[1] = 0u;
     p.ws.plan->valid = 1;
+    if (p.status_out) *p.status_out = A2AV_OK;
   }
 }
 
@@ -994,6 +996,9 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
           __hip_atomic_compare_exchange_strong(&plan->error, &expected, int(A2AV_ERR_TIMEOUT),
                                                __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
+          if (p.status_out)
+            __hip_atomic_store(p.status_out, int(A2AV_ERR_TIMEOUT), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
         __builtin_amdgcn_s_sleep(2);

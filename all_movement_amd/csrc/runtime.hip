@@ -16,6 +16,7 @@
 
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -47,6 +48,10 @@ struct a2av_handle {
   int32_t profile_every = 1;  // record one run in profile_every ...
   int64_t enqueued = 0;       // ... counting the runs enqueued since it was set
   std::string last_error;
+  // Runs of a2av_run_noalloc: the device word that receives each run's
+  // device-side status, and no stored error text (storing it allocates).
+  int32_t* status_out = nullptr;
+  bool keep_error_text = true;
 };
 
 namespace {
@@ -72,7 +77,7 @@ class DeviceGuard {
 };
 
 int hip_fail(a2av_handle* h, hipError_t e, const char* what) {
-  if (h) {
+  if (h && h->keep_error_text) {
     h->last_error = std::string(what) + ": " + hipGetErrorString(e);
   }
   // The status carries the failure: clear HIP's per-thread last error so a
@@ -296,6 +301,7 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   // What the launches can cover; a payload beyond it (which the capacity
   // checks already rule out) is refused on the device rather than copied in
   // part.
+  cp.status_out = h->status_out;
   cp.payload_cap = h->chunk_limit > INT64_MAX / launches ? INT64_MAX
                                                          : int64_t(launches) * h->chunk_limit;
 
@@ -338,6 +344,7 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
                     (uintptr_t(target) & 15u) == 0 && h->cfg.in_slab_bytes % 16 == 0 &&
                     h->cfg.tgt_slab_bytes % 16 == 0 && h->chunk_limit % 16 == 0;
   kp.spin_limit = h->spin_limit;
+  kp.status_out = h->status_out;
   // Chunks are issued from the highest to chunk 0.  Chunks past the run's
   // payload cost only a plain launch that exits at once, and the final launch
   // (the one that raises the flags, cooperative when B > 1) is chunk 0, which
@@ -480,3 +487,114 @@ const char* a2av_last_hip_error(a2av_handle* h) { return h ? h->last_error.c_str
 
 }  // extern "C"
 
+// ------------------------------------------------------------------ no-alloc entry point
+
+// The workspace of a2av_run_noalloc: one array per device that the library
+// runs on, held until the process ends.  Host code never uses the array's
+// name as an address (in host code it is a stand-in, not device memory): the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = 192 * 1024;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct NoallocDevice {
+  bool ready = false;
+  int status = A2AV_OK;   // set-up outcome (HIP errors are kept)
+  char* base = nullptr;   // device address of `scratch` on this device
+  int cus = 0;
+  int wgs_per_cu = 0;
+};
+
+NoallocDevice g_noalloc[kMaxDevices];
+std::mutex g_noalloc_mu;
+
+// Set-up on the first call on a device (that device current): the scratch
+// array's device address and the copy kernel's co-resident capacity.
+const NoallocDevice* noalloc_device(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  NoallocDevice& d = g_noalloc[dev];
+  if (d.ready) return &d;
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  hipDeviceProp_t prop;
+  if (e == hipSuccess) e = hipGetDeviceProperties(&prop, dev);
+  int per_cu = 0;
+  if (e == hipSuccess) e = a2av::copy_occupancy(&per_cu);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    d.status = A2AV_ERR_HIP;
+  } else {
+    d.base = static_cast<char*>(ptr);
+    d.cus = prop.multiProcessorCount;
+    d.wgs_per_cu = per_cu;
+    d.status = A2AV_OK;
+  }
+  d.ready = true;
+  return &d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int a2av_run_noalloc(const void* input, void* target, int32_t* signal,
+                     const int32_t* send_counts, int32_t* recv_counts, int32_t* status,
+                     int32_t P, int64_t in_slab_bytes, int64_t tgt_slab_bytes, int32_t S,
+                     int64_t core_num, int32_t dtype, void* stream) {
+  if (!status) return A2AV_ERR_NULLPTR;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return A2AV_ERR_HIP;
+  }
+  const NoallocDevice* d = noalloc_device(dev);
+  if (!d) return A2AV_ERR_INVALID_ARGS;
+  if (d->status != A2AV_OK) return d->status;
+
+  a2av_config cfg{};
+  cfg.device = dev;
+  cfg.P = P;
+  cfg.in_slab_bytes = in_slab_bytes;
+  cfg.tgt_slab_bytes = tgt_slab_bytes;
+  cfg.S = S;
+  const int64_t capacity = int64_t(d->wgs_per_cu) * d->cus;
+  int st = a2av::check_run_args(&cfg, capacity, input, target, signal, send_counts, recv_counts,
+                                P, core_num, dtype);
+  if (st != A2AV_OK) return st;
+  // The status word is a sixth operand: it may not share a byte with the others.
+  const uintptr_t sp = reinterpret_cast<uintptr_t>(status);
+  const uintptr_t lo[5] = {uintptr_t(input), uintptr_t(target), uintptr_t(signal),
+                           uintptr_t(send_counts), uintptr_t(recv_counts)};
+  const uint64_t len[5] = {uint64_t(P) * uint64_t(in_slab_bytes),
+                           uint64_t(P) * uint64_t(tgt_slab_bytes), uint64_t(P) * uint64_t(S) * 4u,
+                           uint64_t(P) * uint64_t(P) * 4u, uint64_t(P) * uint64_t(P) * 4u};
+  for (int i = 0; i < 5; ++i)
+    if (sp < lo[i] + len[i] && lo[i] < sp + 4u) return A2AV_ERR_INVALID_ARGS;
+  // The workspace must fit the array (P <= 64 and the device's co-resident
+  // capacity decide its size).
+  if (carve_workspace(nullptr, P, capacity, nullptr) > kScratchBytes)
+    return A2AV_ERR_INVALID_ARGS;
+
+  // A handle on the stack: nothing here allocates (its containers stay empty).
+  a2av_handle h;
+  h.cfg = cfg;
+  h.device = dev;
+  h.cus = d->cus;
+  h.wgs_per_cu = d->wgs_per_cu;
+  h.capacity = capacity;
+  h.chunk_limit = a2av::kDefaultChunkLimit;
+  h.launches = a2av::chunk_launches(&cfg, h.chunk_limit);
+  h.spin_limit = kDefaultSpinLimit;
+  h.keep_error_text = false;
+  h.status_out = status;
+  carve_workspace(d->base, P, capacity, &h.ws);
+  RunExtras x;
+  return enqueue_run(&h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, x,
+                     stream);
+}
+
+}  // extern "C"

@@ -229,6 +229,32 @@ int a2av_run_indexed(a2av_handle *h, const void *input, void *target, int32_t *s
                      int32_t P, int64_t core_num, int32_t dtype, int32_t row_elems,
                      int64_t index_stride, void *stream);
 
+/*
+ * a2av_run without a handle, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Nothing is allocated: the workspace is one array of 192 KiB per
+ * device, held by the library until the process ends, whose address is
+ * looked up on the first call on each device (the device current at the
+ * call).  Operands, layout, the exchange and the host checks are those of
+ * a2av_run with the handle's geometry passed in (in_slab_bytes,
+ * tgt_slab_bytes, S) and the defaults of a2av_create (1 GiB per launch, the
+ * device's co-resident capacity, workgroups per block chosen as there).
+ *   status  device int32, written by the run: A2AV_OK, or the device-side
+ *           failure a2av_query_error would report (INVALID_ARGS,
+ *           OVER_CAPACITY, TIMEOUT); caller-owned, a sixth operand that may
+ *           not overlap the others
+ * Errors returned by the call: NULLPTR (status or an operand NULL), the host
+ * checks of a2av_run, INVALID_ARGS when P is over 64 or the device's
+ * capacity needs a workspace larger than the array, HIP.
+ * Every call on a GPU uses that GPU's one array, and each run clears what
+ * must start at zero: calls whose runs overlap on one GPU (other threads,
+ * unordered streams) race and give undefined results; order them.
+ */
+int a2av_run_noalloc(const void *input, void *target, int32_t *signal,
+                     const int32_t *send_counts, int32_t *recv_counts, int32_t *status,
+                     int32_t P, int64_t in_slab_bytes, int64_t tgt_slab_bytes, int32_t S,
+                     int64_t core_num, int32_t dtype, void *stream);
+
 /* Free the workspace and the handle (synchronizes the device first).
  * NULL is accepted and ignored.  The end of the create/run/destroy life
  * cycle: the CANN BatchMatMulReduceScatterAllToAll page ("Full example",
