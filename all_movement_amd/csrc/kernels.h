@@ -41,7 +41,6 @@ struct Workspace {
 
 struct CountParams {
   const int32_t* send_counts;
-  int32_t* recv_counts;
   const int32_t* signal;
   Workspace ws;
   int64_t in_slab;
@@ -65,6 +64,8 @@ struct CopyParams {
   const uint8_t* input;
   uint8_t* target;
   int32_t* signal;
+  const int32_t* send_counts;
+  int32_t* recv_counts;  // written by the final launch, once the run's checks passed
   Workspace ws;
   int64_t chunk_lo;   // flattened payload range of this launch (clamped to T on device)
   int64_t chunk_hi;

@@ -1,8 +1,8 @@
 // kernels.hip -- the two gfx950 kernels of the all_to_all_v exchange.
 //
 // K1 (count_kernel, one 1024-thread workgroup): checks the count matrix and
-// the signal on the device, writes recv_counts as the transpose of
-// send_counts, and derives every segment's source and target byte offsets
+// the signal on the device and derives every segment's source and target
+// byte offsets
 // (exclusive prefixes along d on the send side and along s on the receive
 // side, one wave scanning each row or column of the LDS copy of the matrix
 // with DPP lane moves), and the prefix of the flattened payload that K2
@@ -16,15 +16,17 @@
 // destination's 128-byte line so every wave store writes whole lines, and
 // byte stores for the at most 15 bytes at either end, so no byte outside a
 // segment is ever written.  When source and destination differ by an odd
-// number of bytes mod 4 the body is realigned through LDS: each wave stages
-// a row of 64 aligned source words, then every lane funnels its word and its
-// right neighbour's with v_alignbyte; a whole number of dwords apart, the
-// source is read directly with dword-aligned 16-byte loads.  Pieces of at
+// number of bytes mod 4 the body is realigned in registers: each wave loads
+// a row of 64 aligned source words, every lane takes its right neighbour's
+// word by a DPP lane move and funnels the two with v_alignbyte; a whole
+// number of dwords apart, the source is read directly with dword-aligned
+// 16-byte loads.  Pieces of at
 // most 8 KiB are copied by one wave each, dealt to the waves in turn, so a
 // tile of many small segments costs about one memory round trip instead of
 // one per segment.  Separate instantiations add the bias (BF16 with an FP32
 // bias, FP16 with an FP16 bias) or gather the rows of the indexed exchange.
-// On the run's final launch every admitted block raises its flag in every
+// The run's final launch writes recv_counts, the transpose of send_counts,
+// and every admitted block raises its flag in every
 // rank's signal row, and when B > 1 (a cooperative launch) every workgroup
 // waits, with a bounded spin, until all B blocks have arrived (polling one
 // of several copies of the arrival counter).  The block/flag protocol is the
@@ -256,8 +258,6 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     p.ws.src_off[i] = soff[lds_at(s2, d)];
     p.ws.prefix[i] = pre[lds_at(hi, lo)];
     p.ws.dst_off[i] = doff[lds_at(s2, d)];
-    // recv_counts[d'][s'] = send_counts[s'][d'] with i = d'*P + s'.
-    p.recv_counts[i] = C[lds_at(lo, hi)];
   }
   for (int b = tid; b < p.B; b += kCountThreads) p.ws.blk_cnt[b] = 0u;
   if (tid < kArriveReplicas) p.ws.arrived[int64_t(tid) * kArriveStride] = 0u;
@@ -348,6 +348,18 @@ __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int
   if (k0 < K) guarded_pass(k0);  // the remainder, under NT * kUnroll words
 }
 
+// v moved one lane down the wave: lane l receives lane l + 1's value (DPP
+// wave_shl:1, which gfx9-family parts such as gfx950 provide); lane 63
+// receives 0.
+__device__ inline u32x4 wave_shl1(u32x4 v) {
+  u32x4 o;
+  o.x = uint32_t(__builtin_amdgcn_update_dpp(0, int(v.x), 0x130, 0xf, 0xf, false));
+  o.y = uint32_t(__builtin_amdgcn_update_dpp(0, int(v.y), 0x130, 0xf, 0xf, false));
+  o.z = uint32_t(__builtin_amdgcn_update_dpp(0, int(v.z), 0x130, 0xf, 0xf, false));
+  o.w = uint32_t(__builtin_amdgcn_update_dpp(0, int(v.w), 0x130, 0xf, 0xf, false));
+  return o;
+}
+
 // Body whose source sits phi = 4*Q + r bytes (r = 1..3) past a 16-byte boundary:
 // output word k is bytes [phi, phi+16) of aligned source words A[k], A[k+1].
 // Words A[0..K] all hold body bytes, so every load stays inside 16-byte words
@@ -355,16 +367,17 @@ __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int
 // in turn, each row one whole 1 KiB run of destination lines: row q holds
 // output words k = 64q + l - lp (lp = D's word within its 128-byte line; the
 // words with k < 0 are skipped).  Lane l of row q loads A[k], takes A[k + 1]
-// from its right neighbour through the wave's LDS slot (1 KiB, reused row
-// after row), and lane 63 uses A[64q + 64 - lp], which the whole wave loads
-// as one broadcast word.
+// from its right neighbour's register by a DPP lane move (no LDS round trip:
+// measured 1.5 % faster than exchanging the row through LDS on int8 data at
+// odd offsets, 339 -> 334 us per run for 791 MiB at P = 32), and lane 63
+// uses A[64q + 64 - lp], which the whole wave loads as one broadcast word.
 // One batch of kRealignUnroll rows per wave, starting at row r0.  Guarded
 // batches check every word against [0, K]; interior batches (every row whole
 // and inside the piece) run unpredicated, so their loads issue back to back.
 template <int Q, bool kGuard>
 __device__ inline void realign_batch(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rd,
                                      int64_t r0, int64_t nrows, int64_t K, int64_t lp,
-                                     uint32_t r, u32x4* slot, int lane, int wave, int NW) {
+                                     uint32_t r, int lane, int wave, int NW) {
   u32x4 v[kRealignUnroll];
   u32x4 x[kRealignUnroll];
 #pragma unroll
@@ -386,19 +399,16 @@ __device__ inline void realign_batch(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_
   for (int j = 0; j < kRealignUnroll; ++j) {
     const int64_t row = r0 + int64_t(j) * NW + wave;
     const int64_t k = row * kWave + lane - lp;
-    slot[lane] = v[j];
-    // Lanes read a word another lane wrote: keep the compiler from moving
-    // LDS accesses across these points (a wave's LDS operations run in order).
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    u32x4 hi = slot[(lane + 1) & (kWave - 1)];
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // The right neighbour's word, moved across lanes by DPP (wave_shl:1:
+    // lane l reads lane l + 1; every lane of the wave is active here).
+    u32x4 hi = wave_shl1(v[j]);
     if (lane == kWave - 1) hi = x[j];
     if (!kGuard || (row < nrows && k >= 0 && k < K)) store16(rd, k, funnel<Q>(v[j], hi, r));
   }
 }
 
 template <int Q>
-__device__ void grp_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r, u32x4* slot,
+__device__ void grp_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r,
                                  int lane, int wave, int ng) {
   const int NW = ng / kWave;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(A, (K + 1) * 16);
@@ -412,9 +422,9 @@ __device__ void grp_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r
     // inside A[0..K].
     const bool interior = (r0 > 0 || lp == 0) && (r0 + batch) * kWave - lp <= K;
     if (interior)
-      realign_batch<Q, false>(rs, rd, r0, nrows, K, lp, r, slot, lane, wave, NW);
+      realign_batch<Q, false>(rs, rd, r0, nrows, K, lp, r, lane, wave, NW);
     else
-      realign_batch<Q, true>(rs, rd, r0, nrows, K, lp, r, slot, lane, wave, NW);
+      realign_batch<Q, true>(rs, rd, r0, nrows, K, lp, r, lane, wave, NW);
   }
 }
 
@@ -424,7 +434,7 @@ __device__ void grp_copy_realign(const u32x4* A, u32x4* D, int64_t K, uint32_t r
 // is ever stored.  Those edge bytes are loaded before the body and stored
 // after it, so their round trip overlaps the body's instead of preceding it.
 __device__ void grp_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int t, int lane,
-                               int gw, int ng, u32x4* slot) {
+                               int gw, int ng) {
   const uintptr_t d0 = uintptr_t(dst);
   const uintptr_t body_lo = (d0 + 15u) & ~uintptr_t(15);
   const uintptr_t body_hi = (d0 + uintptr_t(n)) & ~uintptr_t(15);
@@ -450,18 +460,19 @@ __device__ void grp_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int 
   // A source a whole number of dwords past a 16-byte boundary (FP32 data,
   // or any type at such an offset) is read with 16-byte loads at its own,
   // dword-aligned address: the body needs no realignment (measured on c4:
-  // 364 -> 352 us per run against the LDS funnel).  Only sources at odd byte
-  // phases take the funnel.
+  // 364 -> 352 us per run against a funnel through LDS, and 347.6 -> 340.2
+  // against the register funnel below).  Only sources at odd byte phases
+  // take the funnel.
   if ((phi & 3u) == 0) {
     grp_copy_aligned(reinterpret_cast<const u32x4*>(sb), D, K, t, ng);
   } else {
     const u32x4* A = reinterpret_cast<const u32x4*>(sb - phi);
     const uint32_t r = phi & 3u;
     switch (phi >> 2) {
-      case 0: grp_copy_realign<0>(A, D, K, r, slot, lane, gw, ng); break;
-      case 1: grp_copy_realign<1>(A, D, K, r, slot, lane, gw, ng); break;
-      case 2: grp_copy_realign<2>(A, D, K, r, slot, lane, gw, ng); break;
-      default: grp_copy_realign<3>(A, D, K, r, slot, lane, gw, ng); break;
+      case 0: grp_copy_realign<0>(A, D, K, r, lane, gw, ng); break;
+      case 1: grp_copy_realign<1>(A, D, K, r, lane, gw, ng); break;
+      case 2: grp_copy_realign<2>(A, D, K, r, lane, gw, ng); break;
+      default: grp_copy_realign<3>(A, D, K, r, lane, gw, ng); break;
     }
   }
   if (edge) __builtin_amdgcn_raw_buffer_store_b8(ev, rb, int(ek), 0, kStorePolicy);
@@ -476,7 +487,7 @@ __device__ void grp_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int 
 constexpr int64_t kSmallPiece = int64_t(kWave) * kUnroll * 16;
 
 __device__ inline void wg_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int tid,
-                                     int lane, int wave, u32x4* slot, int& small) {
+                                     int lane, int wave, int& small) {
   constexpr int NW = kCopyThreads / kWave;
   const bool one = n <= kSmallPiece;
   if (one) {
@@ -485,8 +496,7 @@ __device__ inline void wg_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n
     if (!mine) return;
   }
   // One call site, so the bodies are inlined once.
-  grp_copy_piece(src, dst, n, one ? lane : tid, lane, one ? 0 : wave, one ? kWave : kCopyThreads,
-                 slot);
+  grp_copy_piece(src, dst, n, one ? lane : tid, lane, one ? 0 : wave, one ? kWave : kCopyThreads);
 }
 
 // ------------------------------------------------ K2, fused bias Add path
@@ -769,7 +779,7 @@ __device__ inline void tile_bounds(const SegTables& tab, int nseg, const uint8_t
 // so a piece is also cut where a sub-block ends.
 template <int MODE>
 __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int64_t x, int64_t b,
-                                  int i, int tid, int lane, int wave, u32x4* slot, int& small) {
+                                  int i, int tid, int lane, int wave, int& small) {
   while (x < b) {
     const int64_t seg_lo = tab.prefix[i];
     const int64_t seg_hi = tab.prefix[i + 1];
@@ -795,7 +805,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
             const int64_t end = (r + 1) * RB < pe - seg_lo ? (r + 1) * RB : pe - seg_lo;
             const int64_t row = __builtin_amdgcn_readfirstlane(list[r]);
             wg_copy_piece(wave_uniform(table + row * RB + w), wave_uniform(dseg + off),
-                          wave_uniform(end - off), tid, lane, wave, slot, small);
+                          wave_uniform(end - off), tid, lane, wave, small);
             off = end;
           }
         }
@@ -820,7 +830,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
       } else if (p.nblk == 1) {
         const int64_t off = x - seg_lo;
         wg_copy_piece(p.input + tab.src[i] + off, p.target + tab.dst[i] + off, pe - x, tid,
-                      lane, wave, slot, small);
+                      lane, wave, small);
       } else {
         const int64_t sub = (seg_hi - seg_lo) / p.nblk;
         const int64_t stride = tab.sstride[source_of<MODE>(i, p.P)];
@@ -829,7 +839,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
           const int64_t w = off - a * sub;
           const int64_t end = (a + 1) * sub < pe - seg_lo ? (a + 1) * sub : pe - seg_lo;
           wg_copy_piece(p.input + tab.src[i] + a * stride + w, p.target + tab.dst[i] + off,
-                        end - off, tid, lane, wave, slot, small);
+                        end - off, tid, lane, wave, small);
           off = end;
         }
       }
@@ -849,9 +859,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
 // LDS tables, so static tiles need no workgroup barrier.
 template <int NT, int MODE>
 __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
-  constexpr int NW = NT / kWave;
   __shared__ SegTables tab;
-  __shared__ u32x4 slots[NW][kWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -889,6 +897,12 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   if (c_lo >= c_hi && !p.last) return;
   if (!p.last) stage_tables();
   __syncthreads();
+  // The final launch writes recv_counts[d][s] = send_counts[s][d] (entry
+  // d*P + s): the run's checks have passed, so a run that fails them, or whose
+  // launches fail before the final one is enqueued, leaves it untouched.
+  if (p.last && blockIdx.x == 0)
+    for (int i = tid; i < nseg; i += NT)
+      p.recv_counts[i] = p.send_counts[(i % p.P) * p.P + i / p.P];
 
   // Tile size: at most kTileBytes, chosen so W workgroups take the same number
   // of rounds (with the static deal, no workgroup is left with one extra tile).
@@ -922,7 +936,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
     if (tl < nstatic) tile_bounds(tab, nseg, p.target, c_lo, c_hi, tile, tl, la, lb, li);
     for (int j = 0; j < kWave && t0 + int64_t(j) * W < nstatic; ++j) {
       copy_range<MODE>(p, tab, readlane64(la, j), readlane64(lb, j), __builtin_amdgcn_readlane(li, j),
-                 tid, lane, wave, slots[wave], small);
+                 tid, lane, wave, small);
     }
   }
 
@@ -947,7 +961,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
       if (a < b)
         copy_range<MODE>(p, tab, wave_uniform(a), wave_uniform(b),
                          __builtin_amdgcn_readfirstlane(seg_of(tab.prefix, nseg, a)), tid, lane,
-                         wave, slots[wave], small);
+                         wave, small);
       __syncthreads();  // every wave is done with s_claim's tile
       if (tid == 0) s_claim = nstatic + int64_t(next);
       __syncthreads();

@@ -2,8 +2,8 @@
 // the chunk plan, and the K1 + K2 launch sequence of one exchange.
 //
 // One run enqueues, on the caller's stream and without synchronizing:
-//   K1  count_kernel            (1 workgroup)       device checks, recv_counts,
-//                                                   segment offsets, payload prefix
+//   K1  count_kernel            (1 workgroup)       device checks, segment offsets,
+//                                                   payload prefix (workspace only)
 //   K2  copy_kernel x launches  (B*G workgroups)    launch c copies payload bytes
 //                                                   [c*limit, (c+1)*limit) of the
 //                                                   flattened payload order
@@ -11,7 +11,8 @@
 // P * min(in_slab, tgt_slab)), so the host never reads the counts back; a
 // launch whose range lies past the run's payload does no copying.  Launches
 // go from the highest chunk down to chunk 0; only the final one (chunk 0)
-// raises the signal flags, and it is cooperative when B > 1.
+// writes recv_counts and raises the signal flags, and it is cooperative when
+// B > 1.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -279,7 +280,6 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
 
   a2av::CountParams cp{};
   cp.send_counts = send_counts;
-  cp.recv_counts = recv_counts;
   cp.signal = signal;
   cp.ws = h->ws;
   cp.in_slab = h->cfg.in_slab_bytes;
@@ -324,6 +324,8 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   kp.input = static_cast<const uint8_t*>(input);
   kp.target = static_cast<uint8_t*>(target);
   kp.signal = signal;
+  kp.send_counts = send_counts;
+  kp.recv_counts = recv_counts;
   kp.ws = h->ws;
   kp.nseg = P * P;
   kp.P = P;

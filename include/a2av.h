@@ -143,8 +143,12 @@ int a2av_create(a2av_handle **out, const a2av_config *cfg);
  * failure writes nothing, is latched in the handle and is reported by
  * a2av_query_error; a2av_run itself has already returned A2AV_OK.
  * The call does not synchronize: results are visible to later work on
- * `stream`.  Returns A2AV_ERR_HIP if a launch fails; K1 may then have run,
- * so recv_counts may be written while the target and the signal are not.
+ * `stream`.  Returns A2AV_ERR_HIP if a launch fails.  recv_counts and the
+ * signal are written only by the run's final launch, so a run of one copy
+ * launch (payload up to the chunk limit) whose launch is refused writes
+ * nothing, as "Launch width" asks of a refused start; in a run of several
+ * chunk launches the chunks copied before the failing launch stay in the
+ * target.
  */
 int a2av_run(a2av_handle *h, const void *input, void *target, int32_t *signal,
              const int32_t *send_counts, int32_t *recv_counts, int32_t P, int64_t core_num,

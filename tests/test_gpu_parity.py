@@ -277,6 +277,37 @@ def test_launch_capacity_refused_not_partial():
         ex.close()
 
 
+def test_refused_launch_writes_nothing():
+    # A launch the runtime refuses: the handle is told the device holds 8,192
+    # workgroups at once (capacity_override), so 2,048 blocks pass the host
+    # check, but the cooperative launch of 2,048 one-per-CU workgroups cannot
+    # be resident together and the runtime refuses it before anything runs.
+    # The run has one K2 launch; the count kernel before it writes only the
+    # workspace, so a2av_run returns A2AV_ERR_HIP and target, signal and
+    # recv_counts keep their contents.  The handle works normally afterwards.
+    P = 8
+    w = wl.custom(P, wl.FP32, np.full((P, P), 64, np.int32), core_num=2048, S=2048)
+    # A short barrier bound, so that even a launch the runtime did not refuse
+    # would end at once (with TIMEOUT) rather than wait on absent blocks.
+    ex = exchange_for(w, capacity_override=8192, wg_per_block=1, spin_limit=1 << 12)
+    c = Case(w)
+    try:
+        info = ex.launch_info(2048)
+        assert info.blocks == 2048 and info.workgroups == 2048 and info.cooperative == 1
+        assert info.chunk_launches == 1
+        say("refused launch", info.workgroups, "workgroups")
+        with pytest.raises(a2av.A2avError, match="A2AV_ERR_HIP"):
+            c.run_gpu(ex)
+        torch.cuda.synchronize()
+        assert ex.query_error() == a2av.OK
+        assert (c.target.cpu().numpy() == wl.SENTINEL).all()
+        assert (c.signal.cpu().numpy() == 0).all()
+        assert (c.recv.cpu().numpy() == -7).all()
+        c.assert_matches(c.run_gpu(ex, core_num=8), c.run_oracle(core_num=8))
+    finally:
+        ex.close()
+
+
 def test_host_errors_raise_before_enqueue():
     P = 4
     w = wl.custom(P, wl.FP32, np.ones((P, P), np.int32), core_num=4)
