@@ -41,6 +41,14 @@ EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_run_bias", "a2av
            "a2av_profile_sample", "a2av_status_string", "a2av_last_hip_error"]
 
 
+# Streaming probes (include/a2av_probe.h): measurement of the copy kernel's
+# instructions alone, not part of the exchange.
+PROBE_READ = 0
+PROBE_WRITE = 1
+PROBE_COPY = 2
+PROBE_EXPORTS = ["a2av_probe_stream"]
+
+
 class a2av_config(ctypes.Structure):
     _fields_ = [("device", ctypes.c_int32), ("P", ctypes.c_int32),
                 ("in_slab_bytes", ctypes.c_int64), ("tgt_slab_bytes", ctypes.c_int64),
@@ -83,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.a2av_run_indexed.restype = ctypes.c_int
     L.a2av_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i32, i64, i32, vp]
     L.a2av_run_noalloc.restype = ctypes.c_int
+    L.a2av_probe_stream.argtypes = [i32, vp, vp, i64, i32, vp]
+    L.a2av_probe_stream.restype = ctypes.c_int
     L.a2av_destroy.argtypes = [vp]
     L.a2av_destroy.restype = ctypes.c_int
     L.a2av_blocks.argtypes = [i64, i64]
@@ -148,6 +158,10 @@ def a2av_run_noalloc(input, target, signal, send_counts, recv_counts, status, P,
                      tgt_slab_bytes, S, core_num, dtype, stream) -> int:
     return lib().a2av_run_noalloc(input, target, signal, send_counts, recv_counts, status, P,
                                   in_slab_bytes, tgt_slab_bytes, S, core_num, dtype, stream)
+
+
+def a2av_probe_stream(kind, src, dst, nbytes, workgroups, stream) -> int:
+    return lib().a2av_probe_stream(kind, src, dst, nbytes, workgroups, stream)
 
 
 def a2av_destroy(h) -> int:

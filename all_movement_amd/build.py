@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liba2av.so")
-SOURCES = ["runtime.hip", "kernels.hip", "plan.cpp"]
+SOURCES = ["runtime.hip", "kernels.hip", "plan.cpp", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

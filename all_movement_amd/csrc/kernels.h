@@ -11,7 +11,7 @@ namespace a2av {
 // Words written by K1 for one run and read by every K2 launch of that run.
 struct alignas(64) RunPlan {
   int32_t valid;        // 1 when the run's counts and signal passed the device checks
-  int32_t base_signal;  // common value of signal[r][b] (r < P, b < B) at entry
+  uint32_t kstate;      // K1's verdict word: flags << 16 | workgroups done (0 between runs)
   int64_t total_bytes;  // payload bytes T of the run
   int32_t error;        // latched status (first failure since the last query)
   uint32_t claim[2];    // dynamic tile counters; K2 launch c uses claim[c & 1]
@@ -94,7 +94,7 @@ constexpr int kCountThreads = 1024;
 constexpr int kCopyThreads = 1024;
 
 // Launch helpers (defined in kernels.hip).
-hipError_t launch_count(const CountParams& p, hipStream_t stream);
+hipError_t launch_count(const CountParams& p, int workgroups, hipStream_t stream);
 hipError_t launch_copy(const CopyParams& p, int workgroups, bool cooperative, hipStream_t stream);
 hipError_t copy_occupancy(int* wgs_per_cu);
 

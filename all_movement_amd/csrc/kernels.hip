@@ -125,11 +125,15 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     bad |= c < 0 ? 1 : 0;
     bad |= (unit > kInt32Max ? c != 0 : c % int32_t(unit) != 0) ? 8 : 0;
   }
+  // The signal is checked by workgroup 0 (the others check gather-list
+  // slices of the row gather).
   const int32_t base = p.signal[0];
-  for (int r = wave; r < P; r += kWaves) {
-    const int32_t* row = p.signal + int64_t(r) * p.S;
+  if (blockIdx.x == 0) {
+    for (int r = wave; r < P; r += kWaves) {
+      const int32_t* row = p.signal + int64_t(r) * p.S;
 #pragma unroll 4
-    for (int b = lane; b < p.B; b += kWave) bad |= row[b] != base ? 4 : 0;
+      for (int b = lane; b < p.B; b += kWave) bad |= row[b] != base ? 4 : 0;
+    }
   }
   if (bad) atomicOr(&flags, bad);
   __syncthreads();
@@ -173,40 +177,73 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   }
   __syncthreads();
 
-  // Indexed exchange, counts valid: every gather-list entry in use must name
-  // a whole row of its table (bit 4 of the flags word: 16).
-  if (p.index != nullptr && flags == 0) {
+  // Indexed exchange, counts valid (no negative or partial-row count, no
+  // source over its gather list): every gather-list entry in use must name a
+  // whole row of its table (bit 4 of the flags word: 16).  The entries in
+  // use, source by source, are split evenly among the launch's workgroups,
+  // each checking its own slice; reads stay inside each source's list, which
+  // the capacity check bounds.
+  if (p.index != nullptr && (flags & (1 | 2 | 8)) == 0) {
     // Unsigned compare: a negative entry is a huge value.  Entries are int32,
     // so a table of 2^31 rows or more admits every non-negative entry.
     const uint32_t limit = uint32_t(p.table_rows < (int64_t(1) << 31) ? p.table_rows
                                                                       : (int64_t(1) << 31));
+    int64_t total = 0;
+    for (int s2 = 0; s2 < P; ++s2) total += rowsum[s2] / unit;
+    const int64_t per = (total + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = per * blockIdx.x;
+    const int64_t hi = lo + per < total ? lo + per : total;
     int bad_row = 0;
-    for (int s2 = 0; s2 < P; ++s2) {
+    int64_t start = 0;  // first entry of source s2 in the concatenation
+    for (int s2 = 0; s2 < P && start < hi; ++s2) {
       const int64_t rows = rowsum[s2] / unit;
+      const int64_t k0 = lo > start ? lo - start : 0;
+      const int64_t k1 = hi < start + rows ? hi - start : rows;
       const int32_t* list = p.index + int64_t(s2) * p.index_stride;
 #pragma unroll 8
-      for (int64_t k = tid; k < rows; k += kCountThreads)
+      for (int64_t k = k0 + tid; k < k1; k += kCountThreads)
         bad_row |= uint32_t(list[k]) >= limit ? 16 : 0;
+      start += rows;
     }
     if (bad_row) atomicOr(&flags, bad_row);
     __syncthreads();
   }
 
+  // The run's verdict: every workgroup adds its flags to one word of the
+  // plan (flags in the high half, then a count of workgroups in the low
+  // half: both on one address, so the last workgroup's count sees every
+  // workgroup's flags), and the last one to count latches the status or
+  // marks the run valid.
   const int f = flags;
-  if (f != 0) {
-    if (tid == 0) {
-      // Order: negative count, count not whole sub-blocks or rows,
-      // over-capacity, gather index outside its table, unequal signal.
-      const int code = (f & 1) ? A2AV_ERR_INVALID_ARGS
-                     : (f & 8) ? A2AV_ERR_INVALID_ARGS
-                     : (f & 2) ? A2AV_ERR_OVER_CAPACITY
-                               : A2AV_ERR_INVALID_ARGS;
-      atomicCAS(&p.ws.plan->error, 0, code);
-      p.ws.plan->valid = 0;
-      if (p.status_out) *p.status_out = code;
+  if (tid == 0) {
+    RunPlan* plan = p.ws.plan;
+    __hip_atomic_fetch_or(&plan->kstate, uint32_t(f) << 16, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old =
+        __hip_atomic_fetch_add(&plan->kstate, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((old & 0xFFFFu) == gridDim.x - 1u) {
+      const int all = int(old >> 16);
+      if (all != 0) {
+        // Order: negative count, count not whole sub-blocks or rows,
+        // over-capacity, gather index outside its table, unequal signal.
+        const int code = (all & 1) ? A2AV_ERR_INVALID_ARGS
+                       : (all & 8) ? A2AV_ERR_INVALID_ARGS
+                       : (all & 2) ? A2AV_ERR_OVER_CAPACITY
+                                   : A2AV_ERR_INVALID_ARGS;
+        atomicCAS(&plan->error, 0, code);
+        plan->valid = 0;
+        if (p.status_out) *p.status_out = code;
+      } else {
+        plan->total_bytes = rowbase[kMaxP];
+        plan->valid = 1;
+        if (p.status_out) *p.status_out = A2AV_OK;
+      }
+      __hip_atomic_store(&plan->kstate, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    return;
   }
+  // Workgroup 0 writes the tables and clears the run's counters; the other
+  // workgroups are done.  The tables of a run that fails are never read.
+  if (f != 0 || blockIdx.x != 0) return;
 
   // The flattened order K2 partitions.  The copy and bias bodies take it
   // destination-major (segment j = d*P + s): the tiles in flight then write
@@ -263,12 +300,8 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   if (tid < kArriveReplicas) p.ws.arrived[int64_t(tid) * kArriveStride] = 0u;
   if (tid == 0) {
     p.ws.prefix[PP] = rowbase[kMaxP];
-    p.ws.plan->total_bytes = rowbase[kMaxP];
-    p.ws.plan->base_signal = base;
     p.ws.plan->claim[0] = 0u;
     p.ws.plan->claim[1] = 0u;
-    p.ws.plan->valid = 1;
-    if (p.status_out) *p.status_out = A2AV_OK;
   }
 }
 
@@ -1024,10 +1057,10 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
 
 }  // namespace
 
-hipError_t launch_count(const CountParams& p, hipStream_t stream) {
+hipError_t launch_count(const CountParams& p, int workgroups, hipStream_t stream) {
   // The launch's own status (hipGetLastError could report an earlier call's).
   void* args[] = {const_cast<CountParams*>(&p)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&count_kernel), dim3(1),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&count_kernel), dim3(workgroups),
                          dim3(kCountThreads), args, 0, stream);
 }
 

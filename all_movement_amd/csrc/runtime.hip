@@ -15,6 +15,7 @@
 // B > 1.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -317,7 +318,15 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
       ev = &h->events[size_t(h->run_counter % kProfileRuns) * size_t(h->events_per_run)];
   }
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
-  if ((e = a2av::launch_count(cp, s)) != hipSuccess) return hip_fail(h, e, "count_kernel launch");
+  // The row gather's K1 checks every gather-list entry in use: its launch
+  // spreads them over up to 64 workgroups, about 8,192 entries each.
+  int k1_wgs = 1;
+  if (mode == 3) {
+    const int64_t entries = int64_t(P) * x.index_stride;
+    k1_wgs = int(std::min<int64_t>(64, std::max<int64_t>(1, (entries + 8191) / 8192)));
+  }
+  if ((e = a2av::launch_count(cp, k1_wgs, s)) != hipSuccess)
+    return hip_fail(h, e, "count_kernel launch");
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
 
   a2av::CopyParams kp{};

@@ -241,6 +241,43 @@ def copy_probe(nbytes: int, steps: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": steps}), flush=True)
 
 
+def stream_ceiling(nbytes: int = 1 << 30, reps: int = 10, warmup: int = 3):
+    """The rates the copy kernel's own memory instructions reach when they
+    only read, only write, or copy (the library's streaming probes, same
+    launch shape and tile claims), over `nbytes`, timed with HIP events on
+    the stream the probes are launched on."""
+    import torch
+    from all_movement_amd import a2av
+    dev = torch.device("cuda:0")
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    out = {"bytes": nbytes}
+    for name, kind, moved in [("read_only", a2av.PROBE_READ, nbytes),
+                              ("write_only", a2av.PROBE_WRITE, nbytes),
+                              ("copy", a2av.PROBE_COPY, 2 * nbytes)]:
+        def launch():
+            st = a2av.a2av_probe_stream(kind, src.data_ptr(), dst.data_ptr(), nbytes, 0,
+                                        stream.cuda_stream)
+            if st != a2av.OK:
+                raise RuntimeError(f"a2av_probe_stream: {a2av.a2av_status_string(st)}")
+        for _ in range(warmup):
+            launch()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out[name] = {"gbps": round(moved / us / 1e3, 1), "us_per_launch": round(us, 2)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(spec: Spec, min_seconds: float = 10.0):
     """The oracle (as it stands) on a bounded sample of the workload on the host."""
     import numpy as np
@@ -321,6 +358,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cache-cold runs (profiler runs that count only the timed runs)")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="only time the streaming probes (read-only, write-only, copy of 1 GiB "
+                         "with the copy kernel's instructions) and print them")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming probes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain torch device copy of MIB MiB --steps times (the "
                          "known-size reference for HBM byte counters) and exit")
@@ -333,6 +374,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe << 20, args.steps)
+        return
+    if args.ceiling_only:
+        print(json.dumps({"ceiling": stream_ceiling(reps=args.steps)}), flush=True)
         return
     spec = WORKLOADS[args.workload]
     main_res = run_gpu(spec, args.steps, args.warmup, cold=not args.no_cold)
@@ -364,6 +408,12 @@ def main():
         "event_steps": f"{main_res['profiled_steps']} of {args.steps} timed steps carry the "
                        f"events (one in {EVENTS_EVERY})",
     }
+    if not args.no_ceiling:
+        ceiling = stream_ceiling()
+        roofline["ceiling"] = ceiling["copy"]["gbps"]
+        roofline["frac_of_ceiling"] = round(roofline["achieved"] / ceiling["copy"]["gbps"], 4)
+    else:
+        ceiling = None
     out = {
         "metric": METRIC, "value": round(main_res["gbps"], 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
@@ -378,6 +428,7 @@ def main():
         "roofline": roofline,
         "cold": main_res["cold"],
         "graph": main_res["graph"],
+        "ceiling": ceiling,
         "also": also,
     }
     if not args.no_cpu:

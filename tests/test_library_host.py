@@ -17,15 +17,17 @@ from all_movement_amd import workloads as wl
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    text = open(os.path.join(ROOT, "include", "a2av.h")).read()
+def _declared_functions(header="a2av.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(a2av_[a-z_]+)\s*\(", text)))
 
 
-def test_library_exports_every_declared_symbol():
-    names = _declared_functions()
-    assert set(names) == set(a2av.EXPORTS)
+@pytest.mark.parametrize("header,exports", [("a2av.h", "EXPORTS"),
+                                            ("a2av_probe.h", "PROBE_EXPORTS")])
+def test_library_exports_every_declared_symbol(header, exports):
+    names = _declared_functions(header)
+    assert set(names) == set(getattr(a2av, exports))
     L = a2av.lib()
     for n in names:
         assert hasattr(L, n), n
