@@ -33,9 +33,10 @@ FP16 = 2
 BF16 = 3
 ELEM_SIZE = {FP32: 4, INT8: 1, FP16: 2, BF16: 2}
 FLAG_PROFILE = 1
+FLAG_NO_BLOCK_WAIT = 2
 
 EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_run_bias", "a2av_run_indexed",
-           "a2av_run_noalloc",
+           "a2av_run_noalloc", "a2av_run_host_counts", "a2av_check_host_counts",
            "a2av_check_bias_args", "a2av_check_indexed_args", "a2av_destroy",
            "a2av_blocks", "a2av_check_args", "a2av_query_error", "a2av_launch_info_get", "a2av_profile_read",
            "a2av_profile_sample", "a2av_status_string", "a2av_last_hip_error"]
@@ -89,6 +90,10 @@ def lib() -> ctypes.CDLL:
     L.a2av_run_bias.restype = ctypes.c_int
     L.a2av_run_indexed.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i64, vp]
     L.a2av_run_indexed.restype = ctypes.c_int
+    L.a2av_run_host_counts.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, vp]
+    L.a2av_run_host_counts.restype = ctypes.c_int
+    L.a2av_check_host_counts.argtypes = [cfgp, vp, i32, ctypes.POINTER(i64), ctypes.POINTER(i32)]
+    L.a2av_check_host_counts.restype = ctypes.c_int
     L.a2av_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i32, i64, i32, vp]
     L.a2av_run_noalloc.restype = ctypes.c_int
     L.a2av_probe_stream.argtypes = [i32, vp, vp, i64, i32, vp]
@@ -152,6 +157,27 @@ def a2av_run_indexed(h, input, target, signal, send_counts, recv_counts, index, 
                      dtype, row_elems, index_stride, stream) -> int:
     return lib().a2av_run_indexed(h, input, target, signal, send_counts, recv_counts, index, P,
                                   core_num, dtype, row_elems, index_stride, stream)
+
+
+def a2av_run_host_counts(h, input, target, signal, send_counts, recv_counts, host_send_counts,
+                         P, core_num, dtype, stream) -> int:
+    return lib().a2av_run_host_counts(h, input, target, signal, send_counts, recv_counts,
+                                      host_send_counts, P, core_num, dtype, stream)
+
+
+def a2av_check_host_counts(cfg: a2av_config, host_send_counts, dtype) -> tuple[int, int, int]:
+    """(status, payload bytes, chunk launches); host_send_counts is an int32
+    numpy array [P, P] (or a raw host address)."""
+    import numpy as np
+    ptr = host_send_counts
+    if isinstance(host_send_counts, np.ndarray):
+        if host_send_counts.dtype != np.int32 or not host_send_counts.flags.c_contiguous:
+            raise ValueError("host_send_counts must be a contiguous int32 array")
+        ptr = host_send_counts.ctypes.data
+    payload, launches = ctypes.c_int64(), ctypes.c_int32()
+    st = lib().a2av_check_host_counts(ctypes.byref(cfg), ptr, dtype, ctypes.byref(payload),
+                                      ctypes.byref(launches))
+    return st, payload.value, launches.value
 
 
 def a2av_run_noalloc(input, target, signal, send_counts, recv_counts, status, P, in_slab_bytes,
@@ -254,14 +280,16 @@ class Exchange:
 
     def __init__(self, P: int, in_slab_bytes: int, tgt_slab_bytes: int, S: int, *,
                  device: int | None = None, wg_per_block: int = 0, chunk_limit_bytes: int = 0,
-                 capacity_override: int = 0, profile: bool = False, spin_limit: int = 0):
+                 capacity_override: int = 0, profile: bool = False, spin_limit: int = 0,
+                 block_wait: bool = True):
         import torch
         if device is None:
             device = torch.cuda.current_device()
         self.device = int(device)
         self.cfg = a2av_config(self.device, P, in_slab_bytes, tgt_slab_bytes, S, wg_per_block,
                                chunk_limit_bytes, capacity_override,
-                               FLAG_PROFILE if profile else 0, spin_limit)
+                               (FLAG_PROFILE if profile else 0) |
+                               (0 if block_wait else FLAG_NO_BLOCK_WAIT), spin_limit)
         st, h = a2av_create(self.cfg)
         _raise(st, "a2av_create")
         self.h = h
@@ -293,13 +321,16 @@ class Exchange:
 
     def run(self, input, target, signal, send_counts, recv_counts, core_num: int, dtype: int,
             stream=None, nblk: int = 1, bias=None, hidden: int = 0, index=None,
-            row_elems: int = 0, check: bool = False) -> None:
+            row_elems: int = 0, check: bool = False, host_counts=None) -> None:
         """One exchange; ``nblk`` > 1 runs the blocked exchange (a2av_run_blocked);
         a ``bias`` tensor (float32 for BF16 payloads, float16 for FP16, [P, nblk,
         hidden] elements) runs the exchange with the bias Add fused in
         (a2av_run_bias); an ``index`` tensor (int32 [P, index_stride] gather
         lists of rows of ``row_elems`` elements) runs the indexed exchange
-        (a2av_run_indexed).
+        (a2av_run_indexed); a ``host_counts`` array (numpy int32 [P, P], the
+        same counts as ``send_counts``) runs a2av_run_host_counts: count
+        errors are raised before anything is enqueued, and the chunk plan
+        follows the payload.
 
         The count and signal checks run on the device, so by default a
         failure is latched and reported by :meth:`query_error`.  With
@@ -331,6 +362,16 @@ class Exchange:
                 bp = self._check(bias, P * nblk * hidden * be[1], "bias", be[0])
             st = a2av_run_bias(self.h, ip, tp, sp, scp, rcp, bp, P, core_num, dtype, nblk, hidden,
                                stream.cuda_stream)
+        elif host_counts is not None:
+            import numpy as np
+            hc = np.ascontiguousarray(host_counts, dtype=np.int32)
+            if hc.shape != (P, P) or hc is not host_counts:
+                raise ValueError("host_counts must be a contiguous int32 numpy array [P, P] "
+                                 "(the exchange never copies operands)")
+            if nblk != 1:
+                raise ValueError("host_counts is taken by the plain exchange only")
+            st = a2av_run_host_counts(self.h, ip, tp, sp, scp, rcp, hc.ctypes.data, P, core_num,
+                                      dtype, stream.cuda_stream)
         elif nblk == 1:
             st = a2av_run(self.h, ip, tp, sp, scp, rcp, P, core_num, dtype, stream.cuda_stream)
         else:

@@ -164,6 +164,31 @@ int32_t chunk_launches(const a2av_config* cfg, int64_t limit, bool gather) {
   return int32_t(std::max<int64_t>(1, n));
 }
 
+int check_host_counts(const a2av_config* cfg, const int32_t* counts, int64_t elem,
+                      int64_t* payload) {
+  const int32_t P = cfg->P;
+  for (int64_t i = 0; i < int64_t(P) * P; ++i)
+    if (counts[i] < 0) return A2AV_ERR_INVALID_ARGS;
+  int64_t total = 0;
+  for (int32_t s = 0; s < P; ++s) {
+    int64_t row = 0;
+    for (int32_t d = 0; d < P; ++d) row += counts[int64_t(s) * P + d];
+    if (row * elem > cfg->in_slab_bytes) return A2AV_ERR_OVER_CAPACITY;
+    total += row * elem;
+  }
+  for (int32_t d = 0; d < P; ++d) {
+    int64_t col = 0;
+    for (int32_t s = 0; s < P; ++s) col += counts[int64_t(s) * P + d];
+    if (col * elem > cfg->tgt_slab_bytes) return A2AV_ERR_OVER_CAPACITY;
+  }
+  *payload = total;
+  return A2AV_OK;
+}
+
+int32_t launches_for(int64_t payload, int64_t limit) {
+  return int32_t(std::max<int64_t>(1, (payload + limit - 1) / limit));
+}
+
 int32_t wg_per_block(int64_t B, int64_t capacity, int64_t payload_bound, int32_t requested,
                      int64_t target_wgs, int64_t min_bytes_per_wg) {
   if (B < 1) return 1;

@@ -62,6 +62,17 @@ int64_t max_payload(const a2av_config* cfg, bool gather = false);
 // the device skips the part of a chunk past the run's real payload.
 int32_t chunk_launches(const a2av_config* cfg, int64_t limit, bool gather = false);
 
+// The count checks of a2av_run on a host copy of the counts (elements of
+// `elem` bytes), in the device's order: a negative count (INVALID_ARGS),
+// then a source row over in_slab or a destination column over tgt_slab
+// (OVER_CAPACITY).  On success *payload is the run's payload in bytes.
+int check_host_counts(const a2av_config* cfg, const int32_t* counts, int64_t elem,
+                      int64_t* payload);
+
+// Launches of at most `limit` bytes that cover `payload` (at least one: the
+// final launch also writes recv_counts and raises the flags).
+int32_t launches_for(int64_t payload, int64_t limit);
+
 // Workgroups that execute one admitted block.  `requested` > 0 is taken as
 // is (clamped to the capacity); 0 picks enough to cover `target_wgs`
 // workgroups without giving any workgroup less than `min_bytes_per_wg` of the

@@ -238,7 +238,7 @@ int a2av_launch_info_get(a2av_handle* h, int64_t core_num, a2av_launch_info* out
   out->chunk_launches = h->launches;
   out->chunk_limit_bytes = h->chunk_limit;
   out->capacity = h->capacity;
-  out->cooperative = B > 1 ? 1 : 0;
+  out->cooperative = (B > 1 && (h->cfg.flags & A2AV_FLAG_NO_BLOCK_WAIT) == 0) ? 1 : 0;
   return A2AV_OK;
 }
 
@@ -255,6 +255,7 @@ struct RunExtras {
   int64_t index_stride = 0;
   int32_t row_elems = 0;
   int32_t mode = 0;
+  int32_t launches = 0;            // > 0: the run's chunk plan, from a host copy of the counts
 };
 
 // Enqueue one run whose arguments passed the host checks: K1, then the K2
@@ -272,7 +273,9 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   // be named many times), so it may need more launches than the handle's
   // plan for the other exchanges.
   const int32_t launches =
-      mode == 3 ? a2av::chunk_launches(&h->cfg, h->chunk_limit, true) : h->launches;
+      x.launches > 0 ? x.launches
+      : mode == 3    ? a2av::chunk_launches(&h->cfg, h->chunk_limit, true)
+                     : h->launches;
 
   DeviceGuard guard(h->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -368,7 +371,7 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
     kp.chunk_hi = int64_t(c + 1) * h->chunk_limit;
     kp.chunk = c;
     kp.last = last ? 1 : 0;
-    kp.wait = (last && li.blocks > 1) ? 1 : 0;
+    kp.wait = (last && li.cooperative) ? 1 : 0;
     e = a2av::launch_copy(kp, li.workgroups, kp.wait != 0, s);
     if (e != hipSuccess) return hip_fail(h, e, "copy_kernel launch");
   }
@@ -438,6 +441,39 @@ int a2av_run(a2av_handle* h, const void* input, void* target, int32_t* signal,
              int32_t dtype, void* stream) {
   return a2av_run_blocked(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype,
                           1, stream);
+}
+
+int a2av_run_host_counts(a2av_handle* h, const void* input, void* target, int32_t* signal,
+                         const int32_t* send_counts, int32_t* recv_counts,
+                         const int32_t* host_send_counts, int32_t P, int64_t core_num,
+                         int32_t dtype, void* stream) {
+  if (!h) return A2AV_ERR_NULLPTR;
+  if (!host_send_counts) return A2AV_ERR_NULLPTR;
+  int st = a2av::check_run_args(&h->cfg, h->capacity, input, target, signal, send_counts,
+                                recv_counts, P, core_num, dtype);
+  if (st != A2AV_OK) return st;
+  int64_t payload = 0;
+  st = a2av::check_host_counts(&h->cfg, host_send_counts, a2av::elem_bytes(dtype), &payload);
+  if (st != A2AV_OK) return st;
+  RunExtras x;
+  x.launches = a2av::launches_for(payload, h->chunk_limit);
+  return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, x,
+                     stream);
+}
+
+int a2av_check_host_counts(const a2av_config* cfg, const int32_t* host_send_counts,
+                           int32_t dtype, int64_t* payload_bytes, int32_t* launches) {
+  if (!cfg || !host_send_counts || !payload_bytes || !launches) return A2AV_ERR_NULLPTR;
+  if (dtype != A2AV_FP32 && dtype != A2AV_INT8) return A2AV_ERR_UNSUPPORTED_DTYPE;
+  if (a2av::check_config(cfg) != A2AV_OK) return A2AV_ERR_INVALID_ARGS;
+  int64_t payload = 0;
+  const int st = a2av::check_host_counts(cfg, host_send_counts, a2av::elem_bytes(dtype), &payload);
+  if (st != A2AV_OK) return st;
+  const int64_t limit = cfg->chunk_limit_bytes > 0 ? cfg->chunk_limit_bytes
+                                                   : a2av::kDefaultChunkLimit;
+  *payload_bytes = payload;
+  *launches = a2av::launches_for(payload, limit);
+  return A2AV_OK;
 }
 
 int a2av_query_error(a2av_handle* h) {

@@ -46,6 +46,9 @@ class Spec:
     cold_runs: int = 50  # runs of the cache-cold protocol (each after a 1 GiB flush)
     graph: bool = False  # also time replays of one run captured into a HIP graph
     half: bool = False   # bias workloads: FP16 payload and bias instead of BF16 + FP32
+    host_counts: bool = False  # plain: run a2av_run_host_counts (chunk plan from the payload)
+    core_num: int = 0    # > 0: this core_num instead of the workload's (a diagnostic line)
+    block_wait: bool = True  # False: the handle takes A2AV_FLAG_NO_BLOCK_WAIT
 
 
 WORKLOADS = {"c1": Spec("plain", 1, graph=True), "c2": Spec("plain", 2, graph=True), "c3": Spec("plain", 3, cpu_scale=4),
@@ -54,7 +57,21 @@ WORKLOADS = {"c1": Spec("plain", 1, graph=True), "c2": Spec("plain", 2, graph=Tr
              "c5u": Spec("blocked", 5, nblk=8, cpu_scale=8, cold_runs=5),
              "c5b": Spec("bias", nblk=8, cpu_scale=16, cold_runs=5),
              "c5h": Spec("bias", nblk=8, cpu_scale=16, cold_runs=5, half=True),
-             "c3i": Spec("indexed", cpu_scale=4)}
+             "c3i": Spec("indexed", cpu_scale=4),
+             # c4 through a2av_run_host_counts: one launch for its ~0.8 GiB
+             # instead of the two that cover its 2 GiB slab bound.
+             "c4h": Spec("plain", 4, cpu_scale=4, cold_runs=20, host_counts=True),
+             # Diagnostics, not the workloads' configurations: c3 and c4 with
+             # core_num 1 (B = 1, one regular launch of the same workgroups),
+             # beside their cooperative B = 64 / 256 runs, to show what the
+             # cooperative launch itself costs a run.
+             "c3b1": Spec("plain", 3, cpu_scale=4, core_num=1),
+             "c4b1": Spec("plain", 4, cpu_scale=4, cold_runs=20, core_num=1),
+             # c3 and c4 (with its host counts) on handles that skip the
+             # blocks' wait: a regular final launch, the same flags.
+             "c3nw": Spec("plain", 3, cpu_scale=4, block_wait=False),
+             "c4hnw": Spec("plain", 4, cpu_scale=4, cold_runs=20, host_counts=True,
+                           block_wait=False)}
 FLUSH_BYTES = 1 << 30       # written before each cache-cold run: above the 256 MB MALL
 # The library's profiling events cost a few microseconds each on the stream;
 # the timed steps record them on one step in EVENTS_EVERY.
@@ -103,6 +120,13 @@ def make_workload(spec: Spec, scale: int = 1):
     w = wl.workload(spec.k, scale=scale)
     if spec.kind == "blocked":
         w.name += f"_temp3_layout_nblk{spec.nblk}"
+    if spec.host_counts:
+        w.name += "_host_counts"
+    if spec.core_num:
+        w.core_num = spec.core_num
+        w.name += f"_core_num{spec.core_num}"
+    if not spec.block_wait:
+        w.name += "_no_block_wait"
     return w
 
 
@@ -117,6 +141,8 @@ def run_gpu(spec: Spec, steps: int, warmup: int, cold: bool = True):
     # Arguments of Exchange.run beyond the five operands, and the extra bytes
     # a run reads once (the bias, or the gather-list entries in use).
     extra = {"nblk": spec.nblk}
+    if spec.host_counts:
+        extra["host_counts"] = np.ascontiguousarray(w.counts, np.int32)
     extra_bytes = 0
     if spec.kind == "indexed":
         extra["row_elems"] = w.extra["row_elems"]
@@ -132,7 +158,8 @@ def run_gpu(spec: Spec, steps: int, warmup: int, cold: bool = True):
     sig = torch.zeros((w.P, w.S), dtype=torch.int32, device=dev)
     sc = torch.from_numpy(w.counts).to(dev)
     rc = torch.zeros((w.P, w.P), dtype=torch.int32, device=dev)
-    ex = a2av.Exchange(w.P, w.in_slab, w.tgt_slab, w.S, device=0, profile=True)
+    ex = a2av.Exchange(w.P, w.in_slab, w.tgt_slab, w.S, device=0, profile=True,
+                       block_wait=spec.block_wait)
     info = ex.launch_info(w.core_num)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
@@ -353,7 +380,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="c1,c2,c3,c4,c5u,c5b,c5h,c3i",
+    ap.add_argument("--also", default="c1,c2,c3,c4,c5u,c5b,c5h,c3i,c4h,c3b1,c4b1,c3nw,c4hnw",
                     help="other workloads reported beside it")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-cold", action="store_true",

@@ -78,6 +78,16 @@ enum a2av_status {
 /* a2av_config.flags */
 #define A2AV_FLAG_PROFILE 1u /* time each run: HIP events before and after K1 and
                                  after the last K2 launch */
+/* With B > 1, make the final launch a regular one and skip the wait for the
+ * other blocks.  Every admitted block still raises its own flags once its
+ * copies are done, the co-resident capacity is still checked (B above it is
+ * LAUNCH_CAPACITY), and the results, flags included, are those of the
+ * cooperative run: on one GPU the wait is not observable, since the flags are
+ * raised before it and the kernel's end already orders every copy before
+ * later work on the stream.  What it saves is the cooperative launch's own
+ * cost (about 20 us of idle GPU per run on an MI355X).  The default keeps the
+ * all-resident launch of the "Launch width" section of the PyPTO page. */
+#define A2AV_FLAG_NO_BLOCK_WAIT 2u
 
 typedef struct a2av_config {
     int32_t device;            /* HIP device ordinal the handle binds to                 */
@@ -232,6 +242,41 @@ int a2av_run_indexed(a2av_handle *h, const void *input, void *target, int32_t *s
                      const int32_t *send_counts, int32_t *recv_counts, const int32_t *index,
                      int32_t P, int64_t core_num, int32_t dtype, int32_t row_elems,
                      int64_t index_stride, void *stream);
+
+/*
+ * a2av_run with a host copy of the counts, for callers that hold them on the
+ * host (the counts computed on the host side and passed down, as in log C of
+ * section 7 of the vccl alltoallv dev log).  Two things change:
+ *   - the count checks run on the host, before anything is enqueued, and
+ *     their status is the call's return value: a negative count
+ *     (INVALID_ARGS), then a source row or destination column over its slab
+ *     (OVER_CAPACITY), after the host checks of a2av_run and in the
+ *     device's order;
+ *   - the chunk plan follows the payload T: ceil(T / limit) launches (at
+ *     least one) instead of enough to cover the geometry bound
+ *     P * min(in_slab, tgt_slab) (section 2 of the same page re-enqueues by
+ *     the op's bytes).
+ *   host_send_counts  host int32 [P, P], row-major [s][d], read only; it
+ *                     must hold the same counts as send_counts (device)
+ * Everything else is a2av_run: the device still checks send_counts and the
+ * signal (latched, a2av_query_error).  If the device counts differ from the
+ * host copy and their payload exceeds what the planned launches cover, the
+ * run is refused on the device with OVER_CAPACITY and writes nothing.
+ */
+int a2av_run_host_counts(a2av_handle *h, const void *input, void *target, int32_t *signal,
+                         const int32_t *send_counts, int32_t *recv_counts,
+                         const int32_t *host_send_counts, int32_t P, int64_t core_num,
+                         int32_t dtype, void *stream);
+
+/* The host part of a2av_run_host_counts alone (no GPU needed): the count
+ * checks on `host_send_counts` for a handle created with `cfg` (cfg->P
+ * ranks, its slabs, its chunk limit, 0 = 1 GiB) and elements of `dtype`
+ * (FP32 or INT8).  Returns the status the call would return for the counts
+ * and, on A2AV_OK, the payload in bytes and the number of chunk launches.
+ * Errors: NULLPTR, UNSUPPORTED_DTYPE, INVALID_ARGS (cfg geometry; a negative
+ * count), OVER_CAPACITY. */
+int a2av_check_host_counts(const a2av_config *cfg, const int32_t *host_send_counts,
+                           int32_t dtype, int64_t *payload_bytes, int32_t *launches);
 
 /*
  * a2av_run without a handle, for callers that cannot allocate device memory:

@@ -2,7 +2,8 @@
  * a2av_c_driver.c -- test program: the library's C ABI driven from C alone.
  *
  * For a few seeded exchanges (plain FP32 and INT8, chunked, blocked, BF16 and
- * FP16 with the bias Add, indexed)
+ * FP16 with the bias Add, indexed, the plain exchange with a host copy of the
+ * counts, and the entry point that allocates nothing)
  * it allocates the five operands with hipMalloc, calls a2av_create, two runs
  * of the entry point on a stream of its own, a2av_query_error and
  * a2av_destroy, then runs the CPU oracle twice on host copies of the same
@@ -57,7 +58,7 @@ static uint64_t next_u64(void)
     return z ^ (z >> 31);
 }
 
-enum { PLAIN = 0, BLOCKED = 1, INDEXED = 2, BIAS = 3 };
+enum { PLAIN = 0, BLOCKED = 1, INDEXED = 2, BIAS = 3, HOSTC = 4, NOALLOC = 5 };
 
 typedef struct {
     const char *name;
@@ -82,6 +83,8 @@ static const Case kCases[] = {
     {"indexed_int8_rows448", INDEXED, 8, A2AV_INT8, 64, 12, 448, 0, 0, 0},
     {"bias_bf16_nblk2_h64", BIAS, 8, A2AV_BF16, 16, 10, 2 * 64, 0, 2, 64},
     {"bias_fp16_nblk3_h24_chunked", BIAS, 5, A2AV_FP16, 5, 12, 3 * 24, 1024, 3, 24},
+    {"host_counts_fp32_chunked", HOSTC, 6, A2AV_FP32, 12, 5000, 1, 16384, 0, 0},
+    {"noalloc_int8_cooperative", NOALLOC, 8, A2AV_INT8, 64, 9000, 1, 0, 0, 0},
 };
 
 /* A finite 16-bit value: random sign and mantissa, exponent kept well inside
@@ -164,7 +167,7 @@ static int run_case(const Case *c, uint64_t seed)
     for (int64_t i = 0; i < P * (stride > 0 ? stride : 1); ++i)
         h_idx[i] = table_rows > 0 ? (int32_t)(next_u64() % (uint64_t)table_rows) : 0;
 
-    void *d_in, *d_tgt, *d_sig, *d_send, *d_recv, *d_idx, *d_bias;
+    void *d_in, *d_tgt, *d_sig, *d_send, *d_recv, *d_idx, *d_bias, *d_status;
     HIP_OK(hipMalloc(&d_in, in_bytes));
     HIP_OK(hipMalloc(&d_tgt, tgt_bytes));
     HIP_OK(hipMalloc(&d_sig, sig_bytes));
@@ -172,6 +175,7 @@ static int run_case(const Case *c, uint64_t seed)
     HIP_OK(hipMalloc(&d_recv, cnt_bytes));
     HIP_OK(hipMalloc(&d_idx, idx_bytes));
     HIP_OK(hipMalloc(&d_bias, bias_bytes));
+    HIP_OK(hipMalloc(&d_status, sizeof(int32_t)));
     HIP_OK(hipMemcpy(d_in, h_in, in_bytes, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(d_tgt, o_tgt, tgt_bytes, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(d_sig, o_sig, sig_bytes, hipMemcpyHostToDevice));
@@ -201,6 +205,12 @@ static int run_case(const Case *c, uint64_t seed)
         if (c->kind == PLAIN)
             gpu_st = a2av_run(h, d_in, d_tgt, d_sig, d_send, d_recv, P, c->core_num, c->dtype,
                               stream);
+        else if (c->kind == HOSTC)
+            gpu_st = a2av_run_host_counts(h, d_in, d_tgt, d_sig, d_send, d_recv, counts, P,
+                                          c->core_num, c->dtype, stream);
+        else if (c->kind == NOALLOC)
+            gpu_st = a2av_run_noalloc(d_in, d_tgt, d_sig, d_send, d_recv, (int32_t *)d_status, P,
+                                      in_slab, tgt_slab, S, c->core_num, c->dtype, stream);
         else if (c->kind == BLOCKED)
             gpu_st = a2av_run_blocked(h, d_in, d_tgt, d_sig, d_send, d_recv, P, c->core_num,
                                       c->dtype, c->unit, stream);
@@ -214,7 +224,13 @@ static int run_case(const Case *c, uint64_t seed)
             fprintf(stderr, "%s: run %d: %s (%s)\n", c->name, run, a2av_status_string(gpu_st),
                     a2av_last_hip_error(h));
         HIP_OK(hipStreamSynchronize(stream));
-        if (gpu_st == A2AV_OK) gpu_st = a2av_query_error(h);
+        if (gpu_st == A2AV_OK && c->kind == NOALLOC) {
+            int32_t dev_st = -1;
+            HIP_OK(hipMemcpy(&dev_st, d_status, sizeof(dev_st), hipMemcpyDeviceToHost));
+            gpu_st = dev_st;
+        } else if (gpu_st == A2AV_OK) {
+            gpu_st = a2av_query_error(h);
+        }
     }
     HIP_OK(hipMemcpy(h_tgt, d_tgt, tgt_bytes, hipMemcpyDeviceToHost));
     HIP_OK(hipMemcpy(h_sig, d_sig, sig_bytes, hipMemcpyDeviceToHost));
@@ -224,7 +240,7 @@ static int run_case(const Case *c, uint64_t seed)
 
     int o_st = 0;
     for (int run = 0; run < 2 && o_st == 0; ++run) {
-        if (c->kind == PLAIN)
+        if (c->kind == PLAIN || c->kind == HOSTC || c->kind == NOALLOC)
             o_st = a2av_oracle_run(h_in, o_tgt, o_sig, counts, o_recv, P, S, in_slab, tgt_slab,
                                    c->core_num, c->dtype, 0);
         else if (c->kind == BLOCKED)
@@ -275,6 +291,7 @@ static int run_case(const Case *c, uint64_t seed)
     HIP_OK(hipFree(d_recv));
     HIP_OK(hipFree(d_idx));
     HIP_OK(hipFree(d_bias));
+    HIP_OK(hipFree(d_status));
     free(counts);
     free(h_in);
     free(h_tgt);

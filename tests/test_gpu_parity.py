@@ -308,6 +308,27 @@ def test_refused_launch_writes_nothing():
         ex.close()
 
 
+@pytest.mark.parametrize("P,L", [(8, 64), (32, 256), (5, 7), (64, 256)])
+def test_no_block_wait_matches_the_oracle(P, L):
+    # A2AV_FLAG_NO_BLOCK_WAIT: B > 1 runs end in a regular launch with no wait
+    # for the other blocks; target, flags and recv_counts are those of the
+    # cooperative run (the oracle's), over two runs and with chunked launches.
+    rng = np.random.default_rng(P * 1000 + L)
+    C = rng.integers(0, 20000 if P <= 8 else 2000, size=(P, P)).astype(np.int32)
+    C[rng.random((P, P)) < 0.15] = 0
+    for dtype in (wl.FP32, wl.INT8):
+        w = wl.custom(P, dtype, C, core_num=L, seed=L + dtype)
+        for limit in (0, 1 << 16):
+            ex = exchange_for(w, block_wait=False, chunk_limit_bytes=limit)
+            try:
+                info = ex.launch_info(L)
+                assert info.blocks > 1 and info.cooperative == 0
+            finally:
+                ex.close()
+            say("no block wait: P", P, "L", L, "dtype", dtype, "limit", limit)
+            check_case(w, runs=2, block_wait=False, chunk_limit_bytes=limit)
+
+
 def test_host_errors_raise_before_enqueue():
     P = 4
     w = wl.custom(P, wl.FP32, np.ones((P, P), np.int32), core_num=4)

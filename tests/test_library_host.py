@@ -306,3 +306,58 @@ def test_indexed_host_checks_aliasing_matches_oracle():
     b = _idx_bufs()
     b[5][3] = -1
     assert _idx_both(b) == (a2av.OK, a2av.ERR_INVALID_ARGS)
+
+
+# ------------------------------------------------------------------ host counts
+
+def _hc_cfg(P, in_slab, tgt_slab, limit=0):
+    return a2av.a2av_config(0, P, in_slab, tgt_slab, 4, 0, limit, 0, 0, 0)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_host_count_checks_match_oracle(seed):
+    # a2av_check_host_counts against the oracle's count checks (negative,
+    # then a row or column over its slab; the signal is equal here), and its
+    # chunk plan against ceil(T / limit).
+    rng = np.random.default_rng(seed)
+    P = int(rng.integers(1, 9))
+    dtype = [wl.FP32, wl.INT8][seed % 2]
+    e = wl.ELEM_SIZE[dtype]
+    C = rng.integers(0, 50, size=(P, P)).astype(np.int32)
+    in_slab = int(C.sum(axis=1).max()) * e + int(rng.integers(0, 3)) * e
+    tgt_slab = int(C.sum(axis=0).max()) * e + int(rng.integers(0, 3)) * e
+    kind = seed % 4
+    if kind == 1:
+        C[rng.integers(P), rng.integers(P)] = -int(rng.integers(1, 5))
+    elif kind == 2:
+        C[rng.integers(P), rng.integers(P)] += 60            # some row or column over
+    in_slab, tgt_slab = max(in_slab, e), max(tgt_slab, e)
+    limit = int(rng.choice([0, 64, 100 * e]))
+    st, payload, launches = a2av.a2av_check_host_counts(_hc_cfg(P, in_slab, tgt_slab, limit), C,
+                                                        dtype)
+    inp = np.zeros(P * in_slab, np.uint8)
+    tgt = np.zeros(P * tgt_slab, np.uint8)
+    sig = np.zeros((P, 1), np.int32)
+    rc = np.zeros((P, P), np.int32)
+    st_o = oracle.run(inp, tgt, sig, C, rc, P=P, S=1, in_slab=in_slab, tgt_slab=tgt_slab,
+                      core_num=1, dtype=dtype)
+    assert st == st_o, (st, st_o)
+    if st == a2av.OK:
+        T = int(C.astype(np.int64).sum()) * e
+        lim = limit or (1 << 30)
+        assert payload == T and launches == max(1, -(-T // lim))
+
+
+def test_host_count_checks_arguments():
+    C = np.ones((4, 4), np.int32)
+    assert a2av.a2av_check_host_counts(_hc_cfg(4, 64, 64), C, wl.BF16)[0] == \
+        a2av.ERR_UNSUPPORTED_DTYPE
+    assert a2av.a2av_check_host_counts(_hc_cfg(4, 64, 64), None, wl.FP32)[0] == a2av.ERR_NULLPTR
+    assert a2av.a2av_check_host_counts(_hc_cfg(65, 64, 64), C, wl.FP32)[0] == \
+        a2av.ERR_INVALID_ARGS
+    # P = 64 with 1 GiB slabs: the geometry bound needs 64 launches; a small
+    # payload needs one.
+    C64 = np.ones((64, 64), np.int32)
+    st, payload, launches = a2av.a2av_check_host_counts(_hc_cfg(64, 1 << 30, 1 << 30), C64,
+                                                        wl.INT8)
+    assert (st, payload, launches) == (a2av.OK, 4096, 1)
