@@ -548,7 +548,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBiasUnroll = 4;  // 16-byte payload words in flight per lane
+// 16-byte payload words in flight per lane: 8 when each thread keeps one
+// column (rows of at most 8192 elements; measured on c5h 1,466 -> 1,381 us of
+// K2 per run, with the wait below), 4 when each word loads its own bias
+// values (more registers per word).
+constexpr int kBiasUnroll = 4;
+constexpr int kBiasUnrollShort = 8;
 
 // Reinterpret through a scalar argument: applied directly to an element of an
 // ext_vector_type value (b.y), this compiler's __builtin_bit_cast reads
@@ -638,28 +643,34 @@ __device__ void wg_bias_piece(const uint8_t* src, uint8_t* dst, int64_t n, const
     const u32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, int(h * BE), 0, 0);
     u32x4 b1 = u32x4{0u, 0u, 0u, 0u};
     if constexpr (MODE == 1) b1 = __builtin_amdgcn_raw_buffer_load_b128(rb, int(h * BE + 16), 0, 0);
+    // Wait for the bias values here (s_waitcnt vmcnt(0) in gfx9's encoding:
+    // expcnt and lgkmcnt at their maxima).  Left to the compiler, the wait
+    // for them sits in the step loop's header, where in steady state it
+    // makes each step wait for most of the previous step's stores before
+    // issuing its loads (c5b 1,438 -> 1,417 us of K2 per run without it).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     // Whole steps unpredicated, so a step's loads issue back to back; then
     // the remainder predicated.
-    const int64_t step = int64_t(NTe) * kBiasUnroll;
+    const int64_t step = int64_t(NTe) * kBiasUnrollShort;
     int64_t k0 = 0;
     for (; k0 + step <= K; k0 += step) {
-      u32x4 v[kBiasUnroll];
+      u32x4 v[kBiasUnrollShort];
 #pragma unroll
-      for (int j = 0; j < kBiasUnroll; ++j) v[j] = load16(rs, k0 + int64_t(j) * NTe + tid);
+      for (int j = 0; j < kBiasUnrollShort; ++j) v[j] = load16(rs, k0 + int64_t(j) * NTe + tid);
 #pragma unroll
-      for (int j = 0; j < kBiasUnroll; ++j)
+      for (int j = 0; j < kBiasUnrollShort; ++j)
         store16(rd, k0 + int64_t(j) * NTe + tid, add_bias_word<MODE>(v[j], b0, b1));
     }
     if (k0 < K) {
-      u32x4 v[kBiasUnroll];
+      u32x4 v[kBiasUnrollShort];
 #pragma unroll
-      for (int j = 0; j < kBiasUnroll; ++j) {
+      for (int j = 0; j < kBiasUnrollShort; ++j) {
         const int64_t k = k0 + int64_t(j) * NTe + tid;
         v[j] = u32x4{0u, 0u, 0u, 0u};
         if (k < K) v[j] = load16(rs, k);
       }
 #pragma unroll
-      for (int j = 0; j < kBiasUnroll; ++j) {
+      for (int j = 0; j < kBiasUnrollShort; ++j) {
         const int64_t k = k0 + int64_t(j) * NTe + tid;
         if (k < K) store16(rd, k, add_bias_word<MODE>(v[j], b0, b1));
       }
@@ -700,9 +711,14 @@ __device__ void wg_bias_piece(const uint8_t* src, uint8_t* dst, int64_t n, const
 // list[j] of source s.  With rows and operands 16-byte aligned every piece
 // is whole words on both sides; thread t handles words t, t + NT, ... of the
 // piece, keeping its (row, byte-in-row) position and advancing it by NT
-// words per step.  Each word reads its row's list entry (the lanes of a wave
-// share one or two entries, so the list loads are broadcasts from cache) and
-// then the payload word.
+// words per word.  A pass of kGatherUnroll words per thread issues its
+// gather-list loads back to back (the lanes of a wave share one or two
+// entries, so they are broadcasts from cache), then the payload loads, then
+// the stores.  Whole passes run unpredicated; only the last pass of a piece
+// checks each word, and there the row of a word past the piece is clamped
+// to the piece's last row, so every list load stays among the entries in
+// use.  (With each list load and its use inside a per-word branch, the
+// compiler waited for every list load in turn: eight round trips a pass.)
 constexpr int kGatherUnroll = 8;
 
 __device__ void wg_gather_words(const uint8_t* table, uint8_t* dseg, int64_t off0, int64_t n,
@@ -718,15 +734,17 @@ __device__ void wg_gather_words(const uint8_t* table, uint8_t* dseg, int64_t off
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(dseg + off0, n);
   const int64_t step_r = (int64_t(NT) * 16) / RB;
   const int64_t step_w = int64_t(NT) * 16 - step_r * RB;
+  const int64_t last_row = (off0 + n - 1) / RB;
   const int64_t off = off0 + 16 * int64_t(tid);
   int64_t r = off / RB;
   int64_t w = off - r * RB;
-  for (int64_t k0 = 0; k0 < K; k0 += int64_t(NT) * kGatherUnroll) {
-    int64_t src[kGatherUnroll];
+  auto pass = [&](int64_t k0, bool guard) {
+    int64_t rw[kGatherUnroll];
+    int32_t row[kGatherUnroll];
 #pragma unroll
     for (int j = 0; j < kGatherUnroll; ++j) {
-      const int64_t k = k0 + int64_t(j) * NT + tid;
-      src[j] = k < K ? int64_t(list[r]) * RB + w : 0;
+      rw[j] = w;
+      row[j] = list[guard && r > last_row ? last_row : r];
       w += step_w;
       r += step_r;
       if (w >= RB) {
@@ -739,14 +757,18 @@ __device__ void wg_gather_words(const uint8_t* table, uint8_t* dseg, int64_t off
     for (int j = 0; j < kGatherUnroll; ++j) {
       const int64_t k = k0 + int64_t(j) * NT + tid;
       v[j] = u32x4{0u, 0u, 0u, 0u};
-      if (k < K) v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(table + src[j]));
+      const u32x4* p = reinterpret_cast<const u32x4*>(table + int64_t(row[j]) * RB + rw[j]);
+      if (!guard || k < K) v[j] = __builtin_nontemporal_load(p);
     }
 #pragma unroll
     for (int j = 0; j < kGatherUnroll; ++j) {
       const int64_t k = k0 + int64_t(j) * NT + tid;
-      if (k < K) store16(rd, k, v[j]);
+      if (!guard || k < K) store16(rd, k, v[j]);
     }
-  }
+  };
+  int64_t k0 = 0;
+  for (; k0 + int64_t(NT) * kGatherUnroll <= K; k0 += int64_t(NT) * kGatherUnroll) pass(k0, false);
+  if (k0 < K) pass(k0, true);
 }
 
 // Source rank of flattened segment i (the order K1 chose for the body).
