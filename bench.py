@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import dataclasses
 from dataclasses import dataclass
 import json
 import os
@@ -389,6 +390,9 @@ def main():
                     help="only time the streaming probes (read-only, write-only, copy of 1 GiB "
                          "with the copy kernel's instructions) and print them")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming probes")
+    ap.add_argument("--no-block-wait", action="store_true",
+                    help="run the main workload on a handle with A2AV_FLAG_NO_BLOCK_WAIT (a "
+                         "regular final launch; for counter runs under a profiler)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain torch device copy of MIB MiB --steps times (the "
                          "known-size reference for HBM byte counters) and exit")
@@ -406,6 +410,8 @@ def main():
         print(json.dumps({"ceiling": stream_ceiling(reps=args.steps)}), flush=True)
         return
     spec = WORKLOADS[args.workload]
+    if args.no_block_wait:
+        spec = dataclasses.replace(spec, block_wait=False)
     main_res = run_gpu(spec, args.steps, args.warmup, cold=not args.no_cold)
     w, info = main_res["w"], main_res["info"]
     log(f"[bench] {w.name}: {main_res['gbps']:.1f} GB/s whole run, K2 "
