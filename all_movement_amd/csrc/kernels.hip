@@ -60,6 +60,15 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kLoadPolicy = 2;
 constexpr int kStorePolicy = 2 | 16;
 
+// a / b for a >= 0 and b >= 1.  A 64-bit division is a long software
+// sequence on the GPU; when both operands fit 32 bits (the usual case for
+// row and list positions) the 32-bit one gives the same quotient for a
+// fraction of the instructions.
+__device__ inline int64_t div_nonneg(int64_t a, int64_t b) {
+  if (((uint64_t(a) | uint64_t(b)) >> 32) == 0) return int64_t(uint32_t(a) / uint32_t(b));
+  return a / b;
+}
+
 // ------------------------------------------------------------------ K1
 
 // The LDS matrices of K1 are indexed [row][column] with a pitch of
@@ -97,7 +106,7 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   __shared__ int64_t soff[kMaxP * kPitch];  // staged outputs, written back coalesced
   __shared__ int64_t pre[kMaxP * kPitch];
   __shared__ int64_t doff[kMaxP * kPitch];
-  __shared__ int64_t rowsum[kMaxP];        // elements each source sends
+  __shared__ int64_t rowsum[kMaxP];        // units (elements, or rows in the row gather) each source sends
   __shared__ int64_t rowbase[kMaxP + 1];   // bytes before source s (s-major order)
   __shared__ int64_t colbase[kMaxP];       // bytes before destination d (d-major order)
   __shared__ int flags;
@@ -110,6 +119,27 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   const int PP = P * P;
 
   if (tid == 0) flags = 0;
+
+  // Row gather: this workgroup's slice of the P x index_stride gather-list
+  // entries (flat position e = s * index_stride + k), split evenly among the
+  // launch's workgroups.  The thread's first kPre entries of it are loaded
+  // now, so that their round trip overlaps the counts'; which of them are in
+  // use (k below the rows source s sends) is known only once the counts are
+  // summed.  Every entry read lies inside the [P, index_stride] lists.
+  constexpr int kPre = 8;
+  int32_t pre_entry[kPre];
+  int64_t g_lo = 0, g_hi = 0;
+  if (p.index != nullptr) {
+    const int64_t entries = int64_t(P) * p.index_stride;
+    const int64_t per = (entries + gridDim.x - 1) / gridDim.x;
+    g_lo = per * blockIdx.x < entries ? per * blockIdx.x : entries;
+    g_hi = g_lo + per < entries ? g_lo + per : entries;
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      const int64_t e = g_lo + tid + int64_t(j) * kCountThreads;
+      pre_entry[j] = e < g_hi ? p.index[e] : 0;
+    }
+  }
   __syncthreads();
 
   // Load the counts; note negatives (bit 0), counts that are not whole
@@ -159,15 +189,16 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     const int64_t incl = wave_inclusive_scan(bytes);
     if (wave == 0) {
       if (lane < P) {
-        rowsum[lane] = acc;
+        rowsum[lane] = p.index != nullptr ? div_nonneg(acc, unit) : acc;
         rowbase[lane] = incl - bytes;
-        if (p.index != nullptr ? acc / unit > p.index_stride : bytes > p.in_slab)
+        if (p.index != nullptr ? div_nonneg(acc, unit) > p.index_stride : bytes > p.in_slab)
           atomicOr(&flags, 2);
       }
       if (lane == kWave - 1) {
         rowbase[kMaxP] = incl;
         // Never reached when every row and column fits (the launches cover
-        // P times the smaller slab, or P target slabs for the row gather).
+        // P times the smaller slab, or for the row gather the smaller of P
+        // target slabs and P full gather lists).
         if (incl > p.payload_cap) atomicOr(&flags, 2);
       }
     } else if (lane < P) {
@@ -178,32 +209,36 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   __syncthreads();
 
   // Indexed exchange, counts valid (no negative or partial-row count, no
-  // source over its gather list): every gather-list entry in use must name a
-  // whole row of its table (bit 4 of the flags word: 16).  The entries in
-  // use, source by source, are split evenly among the launch's workgroups,
-  // each checking its own slice; reads stay inside each source's list, which
-  // the capacity check bounds.
+  // source over its gather list): every gather-list entry in use in this
+  // workgroup's slice must name a whole row of its table (bit 4 of the flags
+  // word: 16).  The prefetched entries first, then the rest of the slice
+  // source by source, loading entries in use only.
   if (p.index != nullptr && (flags & (1 | 2 | 8)) == 0) {
     // Unsigned compare: a negative entry is a huge value.  Entries are int32,
     // so a table of 2^31 rows or more admits every non-negative entry.
     const uint32_t limit = uint32_t(p.table_rows < (int64_t(1) << 31) ? p.table_rows
                                                                       : (int64_t(1) << 31));
-    int64_t total = 0;
-    for (int s2 = 0; s2 < P; ++s2) total += rowsum[s2] / unit;
-    const int64_t per = (total + gridDim.x - 1) / gridDim.x;
-    const int64_t lo = per * blockIdx.x;
-    const int64_t hi = lo + per < total ? lo + per : total;
+    const int64_t stride = p.index_stride;
+    const int64_t pre_hi = g_lo + int64_t(kPre) * kCountThreads < g_hi
+                               ? g_lo + int64_t(kPre) * kCountThreads
+                               : g_hi;
     int bad_row = 0;
-    int64_t start = 0;  // first entry of source s2 in the concatenation
-    for (int s2 = 0; s2 < P && start < hi; ++s2) {
-      const int64_t rows = rowsum[s2] / unit;
-      const int64_t k0 = lo > start ? lo - start : 0;
-      const int64_t k1 = hi < start + rows ? hi - start : rows;
-      const int32_t* list = p.index + int64_t(s2) * p.index_stride;
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      const int64_t e = g_lo + tid + int64_t(j) * kCountThreads;
+      if (e < pre_hi) {
+        const int64_t s2 = div_nonneg(e, stride);
+        if (e - s2 * stride < rowsum[s2] && uint32_t(pre_entry[j]) >= limit) bad_row = 16;
+      }
+    }
+    for (int64_t s2 = div_nonneg(pre_hi, stride); pre_hi < g_hi && s2 < P && s2 * stride < g_hi; ++s2) {
+      const int64_t k0 = (pre_hi > s2 * stride ? pre_hi : s2 * stride) - s2 * stride;
+      const int64_t in_use = rowsum[s2];
+      const int64_t k1 = g_hi - s2 * stride < in_use ? g_hi - s2 * stride : in_use;
+      const int32_t* list = p.index + s2 * stride;
 #pragma unroll 8
       for (int64_t k = k0 + tid; k < k1; k += kCountThreads)
         bad_row |= uint32_t(list[k]) >= limit ? 16 : 0;
-      start += rows;
     }
     if (bad_row) atomicOr(&flags, bad_row);
     __syncthreads();
@@ -635,7 +670,8 @@ __device__ void wg_bias_piece(const uint8_t* src, uint8_t* dst, int64_t n, const
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(brow, int64_t(hidden) * BE);
   const uint32_t H = uint32_t(hidden);
   const uint32_t Hw = H / 8u;
-  uint32_t h = uint32_t((e0 + 8 * int64_t(tid)) % int64_t(H));
+  const int64_t e_t = e0 + 8 * int64_t(tid);
+  uint32_t h = uint32_t(e_t - div_nonneg(e_t, int64_t(H)) * int64_t(H));
 
   if (Hw <= uint32_t(NT)) {
     const int NTe = int((uint32_t(NT) / Hw) * Hw);
@@ -643,36 +679,49 @@ __device__ void wg_bias_piece(const uint8_t* src, uint8_t* dst, int64_t n, const
     const u32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, int(h * BE), 0, 0);
     u32x4 b1 = u32x4{0u, 0u, 0u, 0u};
     if constexpr (MODE == 1) b1 = __builtin_amdgcn_raw_buffer_load_b128(rb, int(h * BE + 16), 0, 0);
-    // Wait for the bias values here (s_waitcnt vmcnt(0) in gfx9's encoding:
-    // expcnt and lgkmcnt at their maxima).  Left to the compiler, the wait
-    // for them sits in the step loop's header, where in steady state it
-    // makes each step wait for most of the previous step's stores before
-    // issuing its loads (c5b 1,438 -> 1,417 us of K2 per run without it).
-    __builtin_amdgcn_s_waitcnt(0x0F70);
     // Whole steps unpredicated, so a step's loads issue back to back; then
-    // the remainder predicated.
-    const int64_t step = int64_t(NTe) * kBiasUnrollShort;
-    int64_t k0 = 0;
-    for (; k0 + step <= K; k0 += step) {
+    // the remainder predicated.  The first step is written out ahead of the
+    // loop: its payload loads follow the bias loads at once, and its first
+    // wait (for the first payload word) covers the bias too.  Inside a loop
+    // the compiler's wait for the bias values sat in the loop header, where
+    // it made each step wait for the previous step's stores before issuing
+    // its loads.
+    // A piece lies inside one tile (at most 128 KiB and 127 bytes), so its
+    // word counts fit 32 bits; kept there, the step tests stay on the scalar
+    // unit instead of borrowing vector registers that the previous step's
+    // stores still read (which made each step wait for those stores).
+    const int32_t K32 = int32_t(K);
+    const int32_t step = NTe * kBiasUnrollShort;
+    int32_t k0 = 0;
+    if (step <= K32) {
       u32x4 v[kBiasUnrollShort];
 #pragma unroll
-      for (int j = 0; j < kBiasUnrollShort; ++j) v[j] = load16(rs, k0 + int64_t(j) * NTe + tid);
+      for (int j = 0; j < kBiasUnrollShort; ++j) v[j] = load16(rs, j * NTe + tid);
 #pragma unroll
       for (int j = 0; j < kBiasUnrollShort; ++j)
-        store16(rd, k0 + int64_t(j) * NTe + tid, add_bias_word<MODE>(v[j], b0, b1));
+        store16(rd, j * NTe + tid, add_bias_word<MODE>(v[j], b0, b1));
+      k0 = step;
     }
-    if (k0 < K) {
+    for (; k0 + step <= K32; k0 += step) {
+      u32x4 v[kBiasUnrollShort];
+#pragma unroll
+      for (int j = 0; j < kBiasUnrollShort; ++j) v[j] = load16(rs, k0 + j * NTe + tid);
+#pragma unroll
+      for (int j = 0; j < kBiasUnrollShort; ++j)
+        store16(rd, k0 + j * NTe + tid, add_bias_word<MODE>(v[j], b0, b1));
+    }
+    if (k0 < K32) {
       u32x4 v[kBiasUnrollShort];
 #pragma unroll
       for (int j = 0; j < kBiasUnrollShort; ++j) {
-        const int64_t k = k0 + int64_t(j) * NTe + tid;
+        const int32_t k = k0 + j * NTe + tid;
         v[j] = u32x4{0u, 0u, 0u, 0u};
-        if (k < K) v[j] = load16(rs, k);
+        if (k < K32) v[j] = load16(rs, k);
       }
 #pragma unroll
       for (int j = 0; j < kBiasUnrollShort; ++j) {
-        const int64_t k = k0 + int64_t(j) * NTe + tid;
-        if (k < K) store16(rd, k, add_bias_word<MODE>(v[j], b0, b1));
+        const int32_t k = k0 + j * NTe + tid;
+        if (k < K32) store16(rd, k, add_bias_word<MODE>(v[j], b0, b1));
       }
     }
     return;
@@ -732,11 +781,11 @@ __device__ void wg_gather_words(const uint8_t* table, uint8_t* dseg, int64_t off
   RB = wave_uniform(RB);
   const int64_t K = n >> 4;
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(dseg + off0, n);
-  const int64_t step_r = (int64_t(NT) * 16) / RB;
+  const int64_t step_r = div_nonneg(int64_t(NT) * 16, RB);
   const int64_t step_w = int64_t(NT) * 16 - step_r * RB;
-  const int64_t last_row = (off0 + n - 1) / RB;
+  const int64_t last_row = div_nonneg(off0 + n - 1, RB);
   const int64_t off = off0 + 16 * int64_t(tid);
-  int64_t r = off / RB;
+  int64_t r = div_nonneg(off, RB);
   int64_t w = off - r * RB;
   auto pass = [&](int64_t k0, bool guard) {
     int64_t rw[kGatherUnroll];
@@ -845,7 +894,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
         // of source s's gather list.
         const int s = source_of<MODE>(i, p.P);
         const int64_t RB = p.row_bytes;
-        const int64_t row0 = (tab.src[i] - int64_t(s) * p.in_slab) / RB;
+        const int64_t row0 = div_nonneg(tab.src[i] - int64_t(s) * p.in_slab, RB);
         const int32_t* list = p.index + int64_t(s) * p.index_stride + row0;
         const uint8_t* table = p.input + int64_t(s) * p.in_slab;
         uint8_t* dseg = p.target + tab.dst[i];
@@ -855,7 +904,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
           // Any alignment: one piece per row (or part of a row), copied by
           // the byte-exact path.
           for (int64_t off = x - seg_lo; off < pe - seg_lo;) {
-            const int64_t r = off / RB;
+            const int64_t r = div_nonneg(off, RB);
             const int64_t w = off - r * RB;
             const int64_t end = (r + 1) * RB < pe - seg_lo ? (r + 1) * RB : pe - seg_lo;
             const int64_t row = __builtin_amdgcn_readfirstlane(list[r]);
@@ -872,7 +921,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
         const int64_t stride = tab.sstride[s];
         constexpr int be = MODE == 1 ? 4 : 2;
         for (int64_t off = x - seg_lo; off < pe - seg_lo;) {
-          const int64_t a = off / sub;
+          const int64_t a = div_nonneg(off, sub);
           const int64_t w = off - a * sub;
           const int64_t end = (a + 1) * sub < pe - seg_lo ? (a + 1) * sub : pe - seg_lo;
           const uint8_t* brow = static_cast<const uint8_t*>(p.bias) +
@@ -890,7 +939,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
         const int64_t sub = (seg_hi - seg_lo) / p.nblk;
         const int64_t stride = tab.sstride[source_of<MODE>(i, p.P)];
         for (int64_t off = x - seg_lo; off < pe - seg_lo;) {
-          const int64_t a = off / sub;
+          const int64_t a = div_nonneg(off, sub);
           const int64_t w = off - a * sub;
           const int64_t end = (a + 1) * sub < pe - seg_lo ? (a + 1) * sub : pe - seg_lo;
           wg_copy_piece(p.input + tab.src[i] + a * stride + w, p.target + tab.dst[i] + off,

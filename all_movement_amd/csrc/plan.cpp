@@ -126,10 +126,11 @@ int check_indexed_args(const a2av_config* cfg, int64_t capacity, const void* inp
   if (P != cfg->P || row_elems < 1 || index_stride < 1) return A2AV_ERR_INVALID_ARGS;
   // Keep P * index_stride entries far from 64-bit overflow.
   if (index_stride > (int64_t(1) << 40)) return A2AV_ERR_INVALID_ARGS;
-  // A gathered payload is bounded by the target slabs only; a chunk limit
-  // that needs more than kMaxLaunches launches to cover them is refused.
+  // A chunk limit that needs more than kMaxLaunches launches to cover the
+  // largest gathered payload is refused.
   const int64_t limit = cfg->chunk_limit_bytes > 0 ? cfg->chunk_limit_bytes : kDefaultChunkLimit;
-  if ((max_payload(cfg, true) + limit - 1) / limit > kMaxLaunches) return A2AV_ERR_INVALID_ARGS;
+  const int64_t bound = gather_max_payload(cfg, int64_t(row_elems) * elem_bytes(dtype), index_stride);
+  if ((bound + limit - 1) / limit > kMaxLaunches) return A2AV_ERR_INVALID_ARGS;
   if (core_num < 1 || core_num > kInt32Max) return A2AV_ERR_INVALID_ARGS;
   const int64_t B = fold_blocks(P, core_num);
   if (int64_t(cfg->S) < B) return A2AV_ERR_INVALID_ARGS;
@@ -152,14 +153,20 @@ int check_indexed_args(const a2av_config* cfg, int64_t capacity, const void* inp
   return A2AV_OK;
 }
 
-int64_t max_payload(const a2av_config* cfg, bool gather) {
-  const int64_t slab = gather ? cfg->tgt_slab_bytes
-                              : std::min(cfg->in_slab_bytes, cfg->tgt_slab_bytes);
-  return int64_t(cfg->P) * slab;
+int64_t max_payload(const a2av_config* cfg) {
+  return int64_t(cfg->P) * std::min(cfg->in_slab_bytes, cfg->tgt_slab_bytes);
 }
 
-int32_t chunk_launches(const a2av_config* cfg, int64_t limit, bool gather) {
-  const int64_t t = max_payload(cfg, gather);
+int64_t gather_max_payload(const a2av_config* cfg, int64_t row_bytes, int64_t index_stride) {
+  const int64_t by_target = int64_t(cfg->P) * cfg->tgt_slab_bytes;
+  // index_stride <= by_target / row_bytes / P keeps the product below
+  // by_target, so it cannot overflow.
+  if (row_bytes < 1 || index_stride > by_target / row_bytes / cfg->P) return by_target;
+  return int64_t(cfg->P) * index_stride * row_bytes;
+}
+
+int32_t chunk_launches(const a2av_config* cfg, int64_t limit) {
+  const int64_t t = max_payload(cfg);
   const int64_t n = (t + limit - 1) / limit;
   return int32_t(std::max<int64_t>(1, n));
 }

@@ -53,14 +53,18 @@ int check_indexed_args(const a2av_config* cfg, int64_t capacity, const void* inp
 // Upper bound of the payload of any valid run.  Every destination column
 // fits its target slab, so T <= P * tgt_slab always; in the exchanges that
 // read each input byte at most once every source row also fits its input
-// slab, so T <= P * min(in_slab, tgt_slab).  The row gather (`gather`) may
-// name a row any number of times: only the target bound holds there.
-int64_t max_payload(const a2av_config* cfg, bool gather = false);
+// slab, so T <= P * min(in_slab, tgt_slab).
+int64_t max_payload(const a2av_config* cfg);
+
+// The same bound for the row gather, which may name a row any number of
+// times: the target bound, and every source sending at most index_stride
+// rows of row_bytes bytes (its gather list), whichever is smaller.
+int64_t gather_max_payload(const a2av_config* cfg, int64_t row_bytes, int64_t index_stride);
 
 // K2 launches per run: enough chunks of `limit` bytes to cover max_payload.
 // Launch c copies the flattened payload bytes [c * limit, (c + 1) * limit);
 // the device skips the part of a chunk past the run's real payload.
-int32_t chunk_launches(const a2av_config* cfg, int64_t limit, bool gather = false);
+int32_t chunk_launches(const a2av_config* cfg, int64_t limit);
 
 // The count checks of a2av_run on a host copy of the counts (elements of
 // `elem` bytes), in the device's order: a negative count (INVALID_ARGS),

@@ -269,12 +269,15 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   a2av_launch_info li;
   int st = a2av_launch_info_get(h, core_num, &li);
   if (st != A2AV_OK) return st;
-  // The row gather's payload is bounded by the target slabs only (a row may
-  // be named many times), so it may need more launches than the handle's
-  // plan for the other exchanges.
+  // The row gather's payload has its own bound (a row may be named many
+  // times), so it may need more or fewer launches than the handle's plan for
+  // the other exchanges.
   const int32_t launches =
       x.launches > 0 ? x.launches
-      : mode == 3    ? a2av::chunk_launches(&h->cfg, h->chunk_limit, true)
+      : mode == 3    ? a2av::launches_for(a2av::gather_max_payload(
+                                              &h->cfg, int64_t(x.row_elems) * a2av::elem_bytes(dtype),
+                                              x.index_stride),
+                                          h->chunk_limit)
                      : h->launches;
 
   DeviceGuard guard(h->device);

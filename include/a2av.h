@@ -358,8 +358,9 @@ int a2av_query_error(a2av_handle *h);
  * sync-start launch beyond the co-resident capacity instead of launching
  * part of it), the workgroups that run them, and the chunk launches of at
  * most chunk_limit_bytes each (the re-enqueue above 1 GB of section 2 of the
- * vccl alltoallv dev log).  a2av_run_indexed may take more chunk launches:
- * its payload is bounded by P target slabs only.  Errors: NULLPTR,
+ * vccl alltoallv dev log).  a2av_run_indexed plans its own: its payload is
+ * bounded by the smaller of P target slabs and P gather lists of index_stride
+ * rows each (a row may be named many times).  Errors: NULLPTR,
  * INVALID_ARGS (core_num out of range), LAUNCH_CAPACITY. */
 int a2av_launch_info_get(a2av_handle *h, int64_t core_num, a2av_launch_info *out);
 

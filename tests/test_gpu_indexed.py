@@ -80,8 +80,8 @@ def test_indexed_sweep(P, R, dtype):
 def test_indexed_small_chunks_and_two_runs(limit):
     # 1000 is not a multiple of 16: the byte-exact path even for aligned rows.
     # Rows are named up to twice, so the payload exceeds P * in_slab: the
-    # launches must still cover it at no more than `limit` bytes each (the
-    # plan covers P * tgt_slab, and launch c copies [c * limit, (c+1) * limit)).
+    # launches must still cover it at no more than `limit` bytes each (launch
+    # c copies [c * limit, (c+1) * limit)).
     w, index = indexed_case(4, 64, wl.INT8, 40, 30, core_num=8, seed=limit)
     assert w.payload_bytes > w.P * w.in_slab
     c = check_indexed(w, index, 64, runs=2, chunk_limit_bytes=limit, profile=True)
@@ -94,7 +94,9 @@ def test_indexed_small_chunks_and_two_runs(limit):
         assert runs == 1
         say("payload", w.payload_bytes, "limit", limit, "launches", launches)
         assert launches * limit >= w.payload_bytes
-        assert launches == -(-w.P * w.tgt_slab // limit)
+        # The plan covers the smaller of P target slabs and P gather lists.
+        bound = min(w.P * w.tgt_slab, w.P * index.shape[1] * 64)
+        assert launches == -(-bound // limit)
     finally:
         ex.close()
 

@@ -361,3 +361,24 @@ def test_host_count_checks_arguments():
     st, payload, launches = a2av.a2av_check_host_counts(_hc_cfg(64, 1 << 30, 1 << 30), C64,
                                                         wl.INT8)
     assert (st, payload, launches) == (a2av.OK, 4096, 1)
+
+
+def test_gather_chunk_plan_takes_the_smaller_bound():
+    # The row gather's plan covers min(P * tgt_slab, P * index_stride * row
+    # bytes).  P = 8, input slabs of 2^16 bytes, target slabs of 2^20 bytes,
+    # rows of 4 bytes.  At a chunk limit of 8 bytes the target bound needs
+    # exactly 2^20 launches (accepted, whatever the gather lists); at 7 bytes
+    # it needs more (refused) unless the gather lists bound the payload more
+    # tightly.
+    P = 8
+    args = lambda cfg, stride: (ctypes.byref(cfg), 0, 1 << 40, 1 << 41, 1 << 42, 1 << 43,
+                                1 << 44, 1 << 45, P, 1, wl.INT8, 4, stride)
+    ok = a2av.a2av_config(0, P, 1 << 16, 1 << 20, 1, 0, 8, 0, 0, 0)
+    over = a2av.a2av_config(0, P, 1 << 16, 1 << 20, 1, 0, 7, 0, 0, 0)
+    lib = a2av.lib()
+    assert lib.a2av_check_indexed_args(*args(ok, 1 << 18)) == a2av.OK
+    assert lib.a2av_check_indexed_args(*args(ok, 1 << 30)) == a2av.OK
+    assert lib.a2av_check_indexed_args(*args(over, 1 << 30)) == a2av.ERR_INVALID_ARGS
+    assert lib.a2av_check_indexed_args(*args(over, 1 << 18)) == a2av.ERR_INVALID_ARGS
+    # 2^17 rows of 4 bytes per source: 2^22 bytes / 7 < 2^20 launches.
+    assert lib.a2av_check_indexed_args(*args(over, 1 << 17)) == a2av.OK
