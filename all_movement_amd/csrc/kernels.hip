@@ -53,11 +53,14 @@ constexpr int64_t kTileBytes = 131072; // flattened payload bytes per workgroup 
 // past it (loads read 0, stores are discarded), so a piece's descriptor also
 // fences its accesses to the piece.
 constexpr int kRsrcWord3 = 0x00020000;
-// Cache policy bits of buffer instructions on gfx950: nt = 2 (streaming),
-// sc1 = 16 (device scope).  Payload loads stream; payload stores stream and
-// are device-scope, so a store is visible to every XCD once acknowledged and
-// the arrival below needs no L2 writeback.
+// Cache policy bits of buffer instructions on gfx950: sc0 = 1 (workgroup
+// scope), nt = 2 (streaming), sc1 = 16 (device scope).  Payload loads
+// stream (dword-phase sources excepted: kLoadPolicyShared, see the copy
+// body); payload stores stream and are device-scope, so a store is visible
+// to every XCD once acknowledged and the arrival below needs no L2
+// writeback.
 constexpr int kLoadPolicy = 2;
+constexpr int kLoadPolicyShared = 1;
 constexpr int kStorePolicy = 2 | 16;
 
 // a / b for a >= 0 and b >= 1.  A 64-bit division is a long software
@@ -248,14 +251,17 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   // plan (flags in the high half, then a count of workgroups in the low
   // half: both on one address, so the last workgroup's count sees every
   // workgroup's flags), and the last one to count latches the status or
-  // marks the run valid.
+  // marks the run valid.  A launch of one workgroup decides on its own
+  // flags, without the round trip of the atomics.
   const int f = flags;
   if (tid == 0) {
     RunPlan* plan = p.ws.plan;
-    __hip_atomic_fetch_or(&plan->kstate, uint32_t(f) << 16, __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t old =
-        __hip_atomic_fetch_add(&plan->kstate, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t old = uint32_t(f) << 16;
+    if (gridDim.x > 1) {
+      __hip_atomic_fetch_or(&plan->kstate, uint32_t(f) << 16, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+      old = __hip_atomic_fetch_add(&plan->kstate, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if ((old & 0xFFFFu) == gridDim.x - 1u) {
       const int all = int(old >> 16);
       if (all != 0) {
@@ -350,6 +356,12 @@ __device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, int64_t word) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, int(word * 16), 0, kLoadPolicy);
 }
 
+// The same with the cache policy LP.
+template <int LP>
+__device__ inline u32x4 load16p(__amdgpu_buffer_rsrc_t r, int64_t word) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, int(word * 16), 0, LP);
+}
+
 __device__ inline void store16(__amdgpu_buffer_rsrc_t r, int64_t word, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, int(word * 16), 0, kStorePolicy);
 }
@@ -373,9 +385,10 @@ __device__ inline u32x4 funnel(u32x4 a, u32x4 b, uint32_t r) {
 // bodies overflow the 128 registers a 1024-thread workgroup allows).
 
 // Body with the destination 16-byte aligned and the source at least
-// dword-aligned: K words.  Thread t
+// dword-aligned: K words, loaded with cache policy LP.  Thread t
 // moves words t, t + ng, ... : each load instruction of a wave covers 1 KiB,
 // and a thread's kUnroll loads in flight are ng words apart.
+template <int LP>
 __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int tid, int ng) {
   const int NT = ng;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, K * 16);
@@ -393,7 +406,7 @@ __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int
     for (int j = 0; j < kUnroll; ++j) {
       const int64_t k = k0 + j * NT + tid;
       v[j] = u32x4{0u, 0u, 0u, 0u};
-      if (k >= 0 && k < K) v[j] = load16(rs, k);
+      if (k >= 0 && k < K) v[j] = load16p<LP>(rs, k);
     }
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
@@ -409,7 +422,7 @@ __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int
   for (; k0 + int64_t(NT) * kUnroll <= K; k0 += int64_t(NT) * kUnroll) {
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) v[j] = load16(rs, k0 + j * NT + tid);
+    for (int j = 0; j < kUnroll; ++j) v[j] = load16p<LP>(rs, k0 + j * NT + tid);
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) store16(rd, k0 + j * NT + tid, v[j]);
   }
@@ -530,9 +543,16 @@ __device__ void grp_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int 
   // dword-aligned address: the body needs no realignment (measured on c4:
   // 364 -> 352 us per run against a funnel through LDS, and 347.6 -> 340.2
   // against the register funnel below).  Only sources at odd byte phases
-  // take the funnel.
-  if ((phi & 3u) == 0) {
-    grp_copy_aligned(reinterpret_cast<const u32x4*>(sb), D, K, t, ng);
+  // take the funnel.  A dword-phase wave's 1 KiB load starts mid-line and
+  // shares its first and last source lines with the neighbouring waves'
+  // loads: with streaming loads those lines were often fetched from HBM
+  // twice (c4 read 1.0155x its payload), with workgroup-scope loads the
+  // neighbours find them in cache (1.0057x, same time).  Aligned sources
+  // keep the streaming loads (plain loads were slower on c5).
+  if (phi == 0) {
+    grp_copy_aligned<kLoadPolicy>(reinterpret_cast<const u32x4*>(sb), D, K, t, ng);
+  } else if ((phi & 3u) == 0) {
+    grp_copy_aligned<kLoadPolicyShared>(reinterpret_cast<const u32x4*>(sb), D, K, t, ng);
   } else {
     const u32x4* A = reinterpret_cast<const u32x4*>(sb - phi);
     const uint32_t r = phi & 3u;
@@ -820,6 +840,65 @@ __device__ void wg_gather_words(const uint8_t* table, uint8_t* dseg, int64_t off
   if (k0 < K) pass(k0, true);
 }
 
+// wg_gather_words with 32-bit positions, the table read through a buffer
+// descriptor with 32-bit offsets: for tables below 2 GiB and pieces that end
+// below 2 GiB into their segment (c3i's token tables are 28 MiB).  The
+// row/byte bookkeeping per word is then 32-bit arithmetic, and the payload
+// address one multiply-add.  Every table offset is row * RB + w with row a
+// checked gather entry (below the table's rows) and w < RB, so it stays
+// inside the descriptor's range.
+__device__ void wg_gather_words32(const uint8_t* table, int64_t table_bytes, uint8_t* dseg,
+                                  int64_t off0_, int64_t n_, const int32_t* list, int64_t RB_,
+                                  int tid) {
+  constexpr uint32_t NT = kCopyThreads;
+  table = wave_uniform(table);
+  dseg = wave_uniform(dseg);
+  list = wave_uniform(list);
+  const uint32_t off0 = uint32_t(wave_uniform(off0_));
+  const uint32_t n = uint32_t(wave_uniform(n_));
+  const uint32_t RB = uint32_t(wave_uniform(RB_));
+  const uint32_t K = n >> 4;
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(dseg + off0, n);
+  const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, wave_uniform(table_bytes));
+  const uint32_t step_r = (NT * 16u) / RB;
+  const uint32_t step_w = NT * 16u - step_r * RB;
+  const uint32_t last_row = (off0 + n - 1u) / RB;
+  const uint32_t off = off0 + 16u * uint32_t(tid);
+  uint32_t r = off / RB;
+  uint32_t w = off - r * RB;
+  auto pass = [&](uint32_t k0, bool guard) {
+    uint32_t rw[kGatherUnroll];
+    uint32_t row[kGatherUnroll];
+#pragma unroll
+    for (int j = 0; j < kGatherUnroll; ++j) {
+      rw[j] = w;
+      row[j] = uint32_t(list[guard && r > last_row ? last_row : r]);
+      w += step_w;
+      r += step_r;
+      if (w >= RB) {
+        w -= RB;
+        ++r;
+      }
+    }
+    u32x4 v[kGatherUnroll];
+#pragma unroll
+    for (int j = 0; j < kGatherUnroll; ++j) {
+      const uint32_t k = k0 + uint32_t(j) * NT + uint32_t(tid);
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (!guard || k < K)
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(rt, int(row[j] * RB + rw[j]), 0, kLoadPolicy);
+    }
+#pragma unroll
+    for (int j = 0; j < kGatherUnroll; ++j) {
+      const uint32_t k = k0 + uint32_t(j) * NT + uint32_t(tid);
+      if (!guard || k < K) store16(rd, k, v[j]);
+    }
+  };
+  uint32_t k0 = 0;
+  for (; k0 + NT * kGatherUnroll <= K; k0 += NT * kGatherUnroll) pass(k0, false);
+  if (k0 < K) pass(k0, true);
+}
+
 // Source rank of flattened segment i (the order K1 chose for the body).
 template <int MODE>
 __device__ inline int source_of(int i, int P) {
@@ -899,7 +978,10 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
         const uint8_t* table = p.input + int64_t(s) * p.in_slab;
         uint8_t* dseg = p.target + tab.dst[i];
         if (p.gather_words) {
-          wg_gather_words(table, dseg, x - seg_lo, pe - x, list, RB, tid);
+          if (p.in_slab < (int64_t(1) << 31) && pe - seg_lo < (int64_t(1) << 31))
+            wg_gather_words32(table, p.in_slab, dseg, x - seg_lo, pe - x, list, RB, tid);
+          else
+            wg_gather_words(table, dseg, x - seg_lo, pe - x, list, RB, tid);
         } else {
           // Any alignment: one piece per row (or part of a row), copied by
           // the byte-exact path.

@@ -190,3 +190,39 @@ def test_indexed_moe_full_size():
     finally:
         ex.close()
     assert torch.equal(c3.target, c.target)
+
+
+def test_indexed_table_past_2_gib():
+    # Token tables of more than 2^31 bytes: rows past the 2 GiB mark take the
+    # 64-bit position path of the gather body, rows below it mix in.  The
+    # input is generated on the GPU; the oracle gets a host copy holding the
+    # named rows only (no other input byte reaches the target).
+    P, R = 2, 4096
+    table_rows = (1 << 31) // R + 16
+    in_slab = table_rows * R
+    rows_per_seg = 6
+    C = np.full((P, P), rows_per_seg * R, np.int32)
+    w = wl.custom(P, wl.INT8, C, core_num=8, seed=91, in_slab=in_slab,
+                  tgt_slab=P * rows_per_seg * R)
+    rng = np.random.default_rng(91)
+    stride = P * rows_per_seg + 3
+    index = np.concatenate([rng.integers(table_rows - 16, table_rows, size=(P, 8)),
+                            rng.integers(0, 64, size=(P, 4)),
+                            np.full((P, 3), -1)], axis=1).astype(np.int32)
+    assert index.shape == (P, stride) and (index[:, :8] >= (1 << 31) // R).all()
+    say("table bytes", in_slab, "index", index.tolist())
+    c = Case(w, host_input=False)
+    host = np.zeros(P * in_slab, np.uint8)
+    for s in range(P):
+        for row in set(index[s, :P * rows_per_seg].tolist()):
+            a = s * in_slab + row * R
+            host[a:a + R] = wl.random_bytes_np(w.payload_seed, a, R)
+    c.input_np = host
+    ex = exchange_for(w)
+    try:
+        st = c.run_gpu(ex, index=upload(index), row_elems=R)
+        c.assert_matches(st, c.run_oracle(index=index, row_elems=R))
+    finally:
+        ex.close()
+        del c
+        torch.cuda.empty_cache()
