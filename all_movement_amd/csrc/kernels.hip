@@ -53,14 +53,11 @@ constexpr int64_t kTileBytes = 131072; // flattened payload bytes per workgroup 
 // past it (loads read 0, stores are discarded), so a piece's descriptor also
 // fences its accesses to the piece.
 constexpr int kRsrcWord3 = 0x00020000;
-// Cache policy bits of buffer instructions on gfx950: sc0 = 1 (workgroup
-// scope), nt = 2 (streaming), sc1 = 16 (device scope).  Payload loads
-// stream (dword-phase sources excepted: kLoadPolicyShared, see the copy
-// body); payload stores stream and are device-scope, so a store is visible
-// to every XCD once acknowledged and the arrival below needs no L2
-// writeback.
+// Cache policy bits of buffer instructions on gfx950: nt = 2 (streaming),
+// sc1 = 16 (device scope).  Payload loads stream; payload stores stream and
+// are device-scope, so a store is visible to every XCD once acknowledged and
+// the arrival below needs no L2 writeback.
 constexpr int kLoadPolicy = 2;
-constexpr int kLoadPolicyShared = 1;
 constexpr int kStorePolicy = 2 | 16;
 
 // a / b for a >= 0 and b >= 1.  A 64-bit division is a long software
@@ -356,11 +353,6 @@ __device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, int64_t word) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, int(word * 16), 0, kLoadPolicy);
 }
 
-// The same with the cache policy LP.
-template <int LP>
-__device__ inline u32x4 load16p(__amdgpu_buffer_rsrc_t r, int64_t word) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, int(word * 16), 0, LP);
-}
 
 __device__ inline void store16(__amdgpu_buffer_rsrc_t r, int64_t word, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, int(word * 16), 0, kStorePolicy);
@@ -385,10 +377,9 @@ __device__ inline u32x4 funnel(u32x4 a, u32x4 b, uint32_t r) {
 // bodies overflow the 128 registers a 1024-thread workgroup allows).
 
 // Body with the destination 16-byte aligned and the source at least
-// dword-aligned: K words, loaded with cache policy LP.  Thread t
+// dword-aligned: K words.  Thread t
 // moves words t, t + ng, ... : each load instruction of a wave covers 1 KiB,
 // and a thread's kUnroll loads in flight are ng words apart.
-template <int LP>
 __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int tid, int ng) {
   const int NT = ng;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, K * 16);
@@ -406,7 +397,7 @@ __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int
     for (int j = 0; j < kUnroll; ++j) {
       const int64_t k = k0 + j * NT + tid;
       v[j] = u32x4{0u, 0u, 0u, 0u};
-      if (k >= 0 && k < K) v[j] = load16p<LP>(rs, k);
+      if (k >= 0 && k < K) v[j] = load16(rs, k);
     }
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
@@ -422,7 +413,7 @@ __device__ inline void grp_copy_aligned(const u32x4* s, u32x4* d, int64_t K, int
   for (; k0 + int64_t(NT) * kUnroll <= K; k0 += int64_t(NT) * kUnroll) {
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) v[j] = load16p<LP>(rs, k0 + j * NT + tid);
+    for (int j = 0; j < kUnroll; ++j) v[j] = load16(rs, k0 + j * NT + tid);
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) store16(rd, k0 + j * NT + tid, v[j]);
   }
@@ -545,14 +536,14 @@ __device__ void grp_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int 
   // against the register funnel below).  Only sources at odd byte phases
   // take the funnel.  A dword-phase wave's 1 KiB load starts mid-line and
   // shares its first and last source lines with the neighbouring waves'
-  // loads: with streaming loads those lines were often fetched from HBM
-  // twice (c4 read 1.0155x its payload), with workgroup-scope loads the
-  // neighbours find them in cache (1.0057x, same time).  Aligned sources
-  // keep the streaming loads (plain loads were slower on c5).
-  if (phi == 0) {
-    grp_copy_aligned<kLoadPolicy>(reinterpret_cast<const u32x4*>(sb), D, K, t, ng);
-  } else if ((phi & 3u) == 0) {
-    grp_copy_aligned<kLoadPolicyShared>(reinterpret_cast<const u32x4*>(sb), D, K, t, ng);
+  // loads, which streaming loads sometimes fetch from HBM twice (c4 reads
+  // 1.0155x its payload).  Workgroup-scope loads let the neighbours find
+  // them in cache (1.0057x) at the same speed back to back, but they keep
+  // the source lines in the caches: right after other work has filled the
+  // caches with dirty lines, c4 then ran 343 -> 396 us, so the streaming
+  // loads stay.
+  if ((phi & 3u) == 0) {
+    grp_copy_aligned(reinterpret_cast<const u32x4*>(sb), D, K, t, ng);
   } else {
     const u32x4* A = reinterpret_cast<const u32x4*>(sb - phi);
     const uint32_t r = phi & 3u;
