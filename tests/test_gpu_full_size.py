@@ -162,3 +162,28 @@ def test_largest_count_int8():
             assert got[j] == want, (int(d_idx[j]), int(offs[j]))
     finally:
         ex.close()
+
+
+@pytest.mark.parametrize("k,variant", [(3, "no_block_wait"), (4, "host_counts_no_block_wait"),
+                                       (3, "core_num_1"), (4, "core_num_1"), (4, "host_counts")])
+def test_full_size_bench_variants_against_oracle(k, variant):
+    # The other configurations the benchmark times on c3 and c4: a handle
+    # with A2AV_FLAG_NO_BLOCK_WAIT, the run with a host copy of the counts,
+    # and core_num 1 (B = 1, a regular launch); whole oracle on the host.
+    w = wl.workload(k)
+    if variant == "core_num_1":
+        w.core_num = 1
+    say("full size", w.name, variant, "payload bytes", w.payload_bytes)
+    c = Case(w, host_input=False)
+    ex = exchange_for(w, block_wait="no_block_wait" not in variant)
+    try:
+        if "host_counts" in variant:
+            ex.run(c.input, c.target, c.signal, c.send, c.recv, w.core_num, w.dtype,
+                   host_counts=w.counts)
+            torch.cuda.synchronize()
+            st = ex.query_error()
+        else:
+            st = c.run_gpu(ex)
+        c.assert_matches(st, c.run_oracle())
+    finally:
+        ex.close()
