@@ -1093,10 +1093,10 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   // workgroups that stream slower take fewer tiles and the launch ends when
   // the last tile does, not when the slowest workgroup's share does
   // (measured on gfx950: c5 5.79 -> 6.11 TB/s in-kernel, c3 5.25 -> 5.75;
-  // an eighth static rather than a quarter, c5 -0.7 %, c5b -0.6 %).  The row
-  // gather claims every tile: its tiles start with a dependent gather-list
-  // load, and it ran fastest with no static deal (c3i 180.4 -> 177.8 us).
-  const int64_t rounds_static = MODE == 3 ? 0 : (rounds + 7) / 8;
+  // an eighth static rather than a quarter, c5 -0.7 %, c5b -0.6 %; the row
+  // gather with its current body, 193.6 -> 191.0 us per run against claiming
+  // every tile).
+  const int64_t rounds_static = (rounds + 7) / 8;
   const int64_t nstatic = W * rounds_static < ntiles ? W * rounds_static : ntiles;
 
   int small = 0;  // small pieces met so far (see wg_copy_piece)
