@@ -60,10 +60,11 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kLoadPolicy = 2;
 constexpr int kStorePolicy = 2 | 16;
 
-// a / b for a >= 0 and b >= 1.  A 64-bit division is a long software
-// sequence on the GPU; when both operands fit 32 bits (the usual case for
-// row and list positions) the 32-bit one gives the same quotient for a
-// fraction of the instructions.
+// a / b for b >= 1.  A 64-bit division is a long software sequence on the
+// GPU; when both operands are non-negative and fit 32 bits (the usual case
+// for row and list positions) the 32-bit one gives the same quotient for a
+// fraction of the instructions.  Any other a (a negative count sum among
+// them) takes the 64-bit division.
 __device__ inline int64_t div_nonneg(int64_t a, int64_t b) {
   if (((uint64_t(a) | uint64_t(b)) >> 32) == 0) return int64_t(uint32_t(a) / uint32_t(b));
   return a / b;
