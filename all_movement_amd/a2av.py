@@ -338,6 +338,10 @@ class Exchange:
         failure (ValueError for INVALID_ARGS / OVER_CAPACITY, A2avError for
         TIMEOUT), as if the checks had run before the call returned."""
         import torch
+        if sum(x is not None for x in (index, bias, host_counts)) > 1:
+            raise ValueError("index, bias and host_counts select different exchanges; give at most one")
+        if index is not None and nblk != 1:
+            raise ValueError("the indexed exchange takes no nblk")
         c = self.cfg
         P = c.P
         ip = self._check(input, P * c.in_slab_bytes, "input")

@@ -349,6 +349,13 @@ def test_host_errors_raise_before_enqueue():
         assert st == a2av.ERR_NULLPTR
         with pytest.raises(ValueError, match="contiguous"):
             ex.run(c.input, c.target, c.signal, c.send.t(), c.recv, 4, wl.FP32)
+        with pytest.raises(ValueError, match="at most one"):       # two exchanges named
+            ex.run(c.input, c.target, c.signal, c.send, c.recv, 4, wl.FP32,
+                   index=torch.zeros((P, 4), dtype=torch.int32, device=DEV), row_elems=1,
+                   host_counts=w.counts)
+        with pytest.raises(ValueError, match="no nblk"):
+            ex.run(c.input, c.target, c.signal, c.send, c.recv, 4, wl.FP32, nblk=2,
+                   index=torch.zeros((P, 4), dtype=torch.int32, device=DEV), row_elems=1)
         torch.cuda.synchronize()
         assert (c.target.cpu().numpy() == wl.SENTINEL).all()
         assert (c.signal.cpu().numpy() == 0).all()
