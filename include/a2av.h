@@ -223,7 +223,9 @@ int a2av_run_bias(a2av_handle *h, const void *input, void *target, int32_t *sign
  *   index   device, int32 [P, index_stride], read only: the rows source s
  *           sends, for d = 0..P-1 in turn, are table rows index[s][0],
  *           index[s][1], ...; a row may be named any number of times;
- *           entries past the rows a source sends are never read
+ *           entries past the rows a source sends are ignored (all
+ *           P * index_stride entries must be allocated: the device may load
+ *           them, but their values never affect the result)
  *   send_counts / recv_counts / target / signal as in a2av_run (counts in
  *           elements, whole rows)
  * Segment s -> d lands where a2av_run puts it: the exchange of the packed
