@@ -420,3 +420,30 @@ def test_block_count_changes_between_runs_on_one_handle():
             c.assert_matches(c.run_gpu(ex, core_num=L), c.run_oracle(core_num=L))
     finally:
         ex.close()
+
+
+@pytest.mark.parametrize("core_num", [1, 16])
+def test_signal_wraps_at_int32_max(core_num):
+    # Every admitted entry at INT32_MAX: one run takes it to INT32_MIN (32-bit
+    # wraparound), the next to INT32_MIN + 1; columns past the admitted
+    # blocks hold other values and stay untouched.  B = 1 (regular launch)
+    # and B = 16 (cooperative).
+    P = 4
+    rng = np.random.default_rng(31)
+    C = rng.integers(0, 300, size=(P, P)).astype(np.int32)
+    w = wl.custom(P, wl.FP32, C, core_num=core_num, S=24, seed=31)
+    B = a2av.a2av_blocks(P, core_num)
+    sig = np.full((P, w.S), -5, np.int32)
+    sig[:, :B] = np.iinfo(np.int32).max
+    c = Case(w, signal_np=sig)
+    ex = exchange_for(w)
+    try:
+        for expect in (np.iinfo(np.int32).min, np.iinfo(np.int32).min + 1):
+            st = c.run_gpu(ex)
+            exp = c.run_oracle()
+            c.assert_matches(st, exp)
+            got = c.signal.cpu().numpy()
+            assert (got[:, :B] == expect).all() and (got[:, B:] == -5).all()
+            c.signal_np0 = exp[2].copy()
+    finally:
+        ex.close()
