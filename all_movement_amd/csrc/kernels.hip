@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   __shared__ int64_t soff[kMaxP * kPitch];  // staged outputs, written back coalesced
   __shared__ int64_t pre[kMaxP * kPitch];
   __shared__ int64_t doff[kMaxP * kPitch];
-  __shared__ int64_t rowsum[kMaxP];        // units (elements, or rows in the row gather) each source sends
+  __shared__ int64_t rowsum[kMaxP];        // elements (row gather: rows) each source sends
   __shared__ int64_t rowbase[kMaxP + 1];   // bytes before source s (s-major order)
   __shared__ int64_t colbase[kMaxP];       // bytes before destination d (d-major order)
   __shared__ int flags;

@@ -129,7 +129,8 @@ int check_indexed_args(const a2av_config* cfg, int64_t capacity, const void* inp
   // A chunk limit that needs more than kMaxLaunches launches to cover the
   // largest gathered payload is refused.
   const int64_t limit = cfg->chunk_limit_bytes > 0 ? cfg->chunk_limit_bytes : kDefaultChunkLimit;
-  const int64_t bound = gather_max_payload(cfg, int64_t(row_elems) * elem_bytes(dtype), index_stride);
+  const int64_t row_bytes = int64_t(row_elems) * elem_bytes(dtype);
+  const int64_t bound = gather_max_payload(cfg, row_bytes, index_stride);
   if ((bound + limit - 1) / limit > kMaxLaunches) return A2AV_ERR_INVALID_ARGS;
   if (core_num < 1 || core_num > kInt32Max) return A2AV_ERR_INVALID_ARGS;
   const int64_t B = fold_blocks(P, core_num);

@@ -272,12 +272,11 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
   // The row gather's payload has its own bound (a row may be named many
   // times), so it may need more or fewer launches than the handle's plan for
   // the other exchanges.
+  const int64_t row_bytes = int64_t(x.row_elems) * a2av::elem_bytes(dtype);
   const int32_t launches =
       x.launches > 0 ? x.launches
-      : mode == 3    ? a2av::launches_for(a2av::gather_max_payload(
-                                              &h->cfg, int64_t(x.row_elems) * a2av::elem_bytes(dtype),
-                                              x.index_stride),
-                                          h->chunk_limit)
+      : mode == 3    ? a2av::launches_for(
+                        a2av::gather_max_payload(&h->cfg, row_bytes, x.index_stride), h->chunk_limit)
                      : h->launches;
 
   DeviceGuard guard(h->device);
