@@ -9,8 +9,9 @@
 // partitions.
 //
 // K2 (copy_kernel, W = B * G workgroups): the flattened payload is cut into
-// tiles of at most 128 KiB; the first eighth is dealt round-robin to the
-// workgroups, the rest are claimed from a counter.  Inside a segment the
+// tiles of at most 64 KiB (128 KiB for the bias and gather bodies); the first
+// eighth is dealt round-robin to the workgroups, the rest are claimed from a
+// counter.  Inside a segment the
 // copy is destination-aligned: 128-bit streaming buffer loads and
 // device-scope streaming buffer stores in the body, numbered from the
 // destination's 128-byte line so every wave store writes whole lines, and
@@ -44,9 +45,19 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kUnroll = 8;          // 16-byte words in flight per lane, aligned body
+constexpr int kUnroll = 4;          // 16-byte words in flight per lane, aligned body
 constexpr int kRealignUnroll = 4;   // 64-word rows in flight per wave, realigned body
-constexpr int64_t kTileBytes = 131072; // flattened payload bytes per workgroup tile
+
+// Flattened payload bytes per workgroup tile: one pass of the body, 64 KiB
+// for the byte copy (4 words per lane), 128 KiB for the bias and gather
+// bodies (8 words per lane).  With the copy body at 64 KiB tiles c5 ran
+// 2,715 -> 2,624 us per run, c3 181.5 -> 176.4, c4 338.5 -> 328.1 (the
+// narrower window of tiles in flight streams better, as the probes show);
+// the bias and gather bodies lose 9 % at 64 KiB.
+template <int MODE>
+constexpr int64_t tile_bytes() {
+  return MODE == 0 ? 65536 : 131072;
+}
 
 // Buffer resources: word 3 of a raw (untyped, stride 0) buffer descriptor on
 // the gfx9 family; num_records is in bytes and the hardware drops any access
@@ -558,13 +569,13 @@ __device__ void grp_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int 
   if (edge) __builtin_amdgcn_raw_buffer_store_b8(ev, rb, int(ek), 0, kStorePolicy);
 }
 
-// Pieces of at most kSmallPiece bytes (one pass of a wave's aligned body)
+// Pieces of at most kSmallPiece bytes (two passes of a wave's aligned body)
 // take one wave each, dealt to the waves in turn; `small` counts the small
 // pieces met so far and is the same in every wave.  A workgroup copying such
 // pieces one after another would pay a memory round trip per piece (measured
 // on gfx950: 16 pieces of ~130 bytes took 24 us in one workgroup).  Larger
 // pieces take the whole workgroup.
-constexpr int64_t kSmallPiece = int64_t(kWave) * kUnroll * 16;
+constexpr int64_t kSmallPiece = 8192;
 
 __device__ inline void wg_copy_piece(const uint8_t* src, uint8_t* dst, int64_t n, int tid,
                                      int lane, int wave, int& small) {
@@ -917,12 +928,44 @@ __device__ inline int seg_of(const int64_t* prefix, int nseg, int64_t x) {
   return lo;
 }
 
+// The same for a wave-uniform x, found by the wave's 64 lanes together: each
+// level reads one prefix entry per lane (64 candidates), and the ballot of
+// "prefix <= x", true on a leading run of lanes since the prefix never
+// falls, gives the next base.  One LDS round trip per level of 64 (nseg <=
+// 4096: at most two) where the binary search takes up to 12 in turn.  All
+// lanes of the wave must be active.
+__device__ inline int wave_seg_of(const int64_t* prefix, int nseg, int64_t x, int lane) {
+  int base = 0;
+  int span = nseg > kWave ? kWave : 1;
+  for (;;) {
+    const int i = base + lane * span;
+    const bool le = i < nseg && prefix[i] <= x;
+    const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(le));
+    base += (cnt - 1) * span;
+    if (span == 1) break;
+    span = 1;
+  }
+  return base;
+}
+
 // A tile boundary x moved forward (never past its segment's end or c_hi) so
 // that the destination byte it maps to starts a 128-byte line: neighbouring
 // tiles then never share a destination line inside a segment.  Monotone in x.
 __device__ inline int64_t align_boundary(const SegTables& t, int nseg, const uint8_t* target,
                                          int64_t x, int64_t c_hi) {
   const int i = seg_of(t.prefix, nseg, x);
+  const uintptr_t a = uintptr_t(target) + uintptr_t(t.dst[i] + (x - t.prefix[i]));
+  int64_t y = x + int64_t((0u - a) & 127u);
+  if (y > t.prefix[i + 1]) y = t.prefix[i + 1];
+  if (y > c_hi) y = c_hi;
+  return y;
+}
+
+// align_boundary for a wave-uniform x (the claimed tiles' bounds), searched
+// by the whole wave.
+__device__ inline int64_t align_boundary_w(const SegTables& t, int nseg, const uint8_t* target,
+                                           int64_t x, int64_t c_hi, int lane) {
+  const int i = wave_seg_of(t.prefix, nseg, x, lane);
   const uintptr_t a = uintptr_t(target) + uintptr_t(t.dst[i] + (x - t.prefix[i]));
   int64_t y = x + int64_t((0u - a) & 127u);
   if (y > t.prefix[i + 1]) y = t.prefix[i + 1];
@@ -1028,7 +1071,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
 }
 
 // One K2 launch copies the flattened payload bytes [c_lo, c_hi) of the run.
-// The range is cut into tiles of at most 128 KiB, handed out in tile order
+// The range is cut into tiles of at most tile_bytes<MODE>(), handed out in tile order
 // (round-robin first, then by claim), so at any moment the grid streams
 // through one narrow window of the source and of the destination (measured
 // on gfx950: contiguous per-workgroup ranges that fan out to destination
@@ -1082,11 +1125,13 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
     for (int i = tid; i < nseg; i += NT)
       p.recv_counts[i] = p.send_counts[(i % p.P) * p.P + i / p.P];
 
-  // Tile size: at most kTileBytes, chosen so W workgroups take the same number
-  // of rounds (with the static deal, no workgroup is left with one extra tile).
+  // Tile size: at most tile_bytes<MODE>(), chosen so W workgroups take the
+  // same number of rounds (with the static deal, no workgroup is left with
+  // one extra tile).
+  constexpr int64_t kTile = tile_bytes<MODE>();
   const int64_t len = c_hi - c_lo;
   const int64_t W = gridDim.x;
-  const int64_t rounds = (len + W * kTileBytes - 1) / (W * kTileBytes);
+  const int64_t rounds = (len + W * kTile - 1) / (W * kTile);
   const int64_t tile = rounds > 0 ? ((len + W * rounds - 1) / (W * rounds) + 15) & ~int64_t(15) : 1;
   const int64_t ntiles = (len + tile - 1) / tile;
   // The first eighth of the rounds (rounded up) is dealt statically: tile t
@@ -1122,28 +1167,36 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   // the current one.  Claims only grow, so every workgroup leaves the loop
   // once they pass ntiles, and each tile is copied exactly once.
   if (nstatic < ntiles) {
-    __shared__ int64_t s_claim;
+    // The claimed tiles' bounds are wave-uniform, so each wave finds their
+    // segments with the whole-wave search, and the claims alternate between
+    // two LDS slots, so one barrier per tile suffices (with the binary
+    // search and two barriers per tile the 64 KiB tiles ran slower than
+    // 128 KiB ones).
+    __shared__ int64_t s_claim[2];
     uint32_t* ctr = &plan->claim[p.chunk & 1];
     if (tid == 0)
-      s_claim = nstatic + int64_t(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT));
+      s_claim[0] = nstatic + int64_t(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT));
     __syncthreads();
-    int64_t t = s_claim;
+    int64_t t = s_claim[0];
+    int slot = 0;
     while (t < ntiles) {
       uint32_t next = 0;
       if (tid == 0) next = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int64_t x0 = c_lo + t * tile;
       const int64_t x1 = x0 + tile < c_hi ? x0 + tile : c_hi;
-      const int64_t a = t == 0 ? c_lo : align_boundary(tab, nseg, p.target, x0, c_hi);
-      const int64_t b = x1 >= c_hi ? c_hi : align_boundary(tab, nseg, p.target, x1, c_hi);
+      const int64_t a = t == 0 ? c_lo : align_boundary_w(tab, nseg, p.target, x0, c_hi, lane);
+      const int64_t b = x1 >= c_hi ? c_hi : align_boundary_w(tab, nseg, p.target, x1, c_hi, lane);
       if (a < b)
         copy_range<MODE>(p, tab, wave_uniform(a), wave_uniform(b),
-                         __builtin_amdgcn_readfirstlane(seg_of(tab.prefix, nseg, a)), tid, lane,
-                         wave, small);
-      __syncthreads();  // every wave is done with s_claim's tile
-      if (tid == 0) s_claim = nstatic + int64_t(next);
+                         __builtin_amdgcn_readfirstlane(wave_seg_of(tab.prefix, nseg, a, lane)),
+                         tid, lane, wave, small);
+      // The next claim goes to the other slot: every thread read it at the
+      // start of the previous tile, before the barrier that ended that tile.
+      if (tid == 0) s_claim[slot ^ 1] = nstatic + int64_t(next);
       __syncthreads();
-      t = s_claim;
+      slot ^= 1;
+      t = s_claim[slot];
     }
   }
 

@@ -14,8 +14,8 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 1024;       // as the copy kernel's workgroups
-constexpr int kUnroll = 8;           // 16-byte words in flight per lane
-constexpr int64_t kTile = 131072;    // bytes per claimed tile
+constexpr int kUnroll = 4;           // 16-byte words in flight per lane
+constexpr int64_t kTile = 65536;     // bytes per claimed tile (one pass)
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kLoadPolicy = 2;       // nt
 constexpr int kStorePolicy = 2 | 16; // nt sc1

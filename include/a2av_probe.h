@@ -6,11 +6,11 @@
  * is read, beside the published HBM peak.
  *
  * Each probe streams `bytes` through the same instructions and launch shape
- * as the segment-copy kernel: 1024-thread workgroups (one per compute unit
- * unless `workgroups` says otherwise), 128 KiB tiles claimed from a counter
- * in tile order, 16-byte streaming loads (buffer_load nt) with 8 words in
- * flight per lane, 16-byte streaming device-scope stores (buffer_store nt
- * sc1).
+ * as the segment-copy kernel's byte copy: 1024-thread workgroups (one per
+ * compute unit unless `workgroups` says otherwise), 64 KiB tiles claimed from
+ * a counter in tile order, 16-byte streaming loads (buffer_load nt) with 4
+ * words in flight per lane, 16-byte streaming device-scope stores
+ * (buffer_store nt sc1).
  *   A2AV_PROBE_READ   reads src; writes nothing (dst may be NULL)
  *   A2AV_PROBE_WRITE  writes the 32-bit pattern 0xA5A5A5A5 into dst; reads nothing
  *   A2AV_PROBE_COPY   copies src to dst
