@@ -11,9 +11,11 @@ namespace a2av {
 // Words written by K1 for one run and read by every K2 launch of that run.
 struct alignas(64) RunPlan {
   int32_t valid;        // 1 when the run's counts and signal passed the device checks
-  uint32_t kstate;      // K1's verdict word: flags << 16 | workgroups done (0 between runs)
-  int64_t total_bytes;  // payload bytes T of the run
   int32_t error;        // latched status (first failure since the last query)
+  int64_t total_bytes;  // payload bytes T of the run
+  uint64_t kstate;      // K1's verdict word (0 between runs): 8-bit fields, the
+                        // workgroups done in the lowest, then per failure kind
+                        // the workgroups that found it
   uint32_t claim[2];    // dynamic tile counters; K2 launch c uses claim[c & 1]
 };
 

@@ -1,8 +1,8 @@
 // kernels.hip -- the two gfx950 kernels of the all_to_all_v exchange.
 //
-// K1 (count_kernel, one 1024-thread workgroup): checks the count matrix and
-// the signal on the device and derives every segment's source and target
-// byte offsets
+// K1 (count_kernel, one 1024-thread workgroup; the row gather adds up to 63
+// more to check its gather lists): checks the count matrix and the signal
+// on the device and derives every segment's source and target byte offsets
 // (exclusive prefixes along d on the send side and along s on the receive
 // side, one wave scanning each row or column of the LDS copy of the matrix
 // with DPP lane moves), and the prefix of the flattened payload that K2
@@ -113,6 +113,119 @@ __device__ inline int64_t wave_inclusive_scan(int64_t v) {
   return v;
 }
 
+// K1's outputs for a valid run, by workgroup 0: the segment tables and the
+// cleared counters of the run.
+__device__ void write_tables(const CountParams& p, const int32_t* C, int64_t* soff, int64_t* pre,
+                             int64_t* doff, const int64_t* rowbase, const int64_t* colbase) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  constexpr int kWaves = kCountThreads / kWave;
+  const int P = p.P;
+  const int PP = P * P;
+
+  // The flattened order K2 partitions.  The copy and bias bodies take it
+  // destination-major (segment j = d*P + s): the tiles in flight then write
+  // one contiguous stretch of a target slab and read pieces of several
+  // source slabs, which DRAM serves better than the transpose the other way
+  // round.  The row gather takes it source-major (j = s*P + d), measured
+  // faster for it.
+  const bool dmajor = p.index == nullptr;
+
+  // Send side, one wave per source row s (lane d): the exclusive prefix
+  // along d of the row's bytes (input packed by destination) gives the
+  // source offsets; with nblk > 1 the source offset is instead the prefix of
+  // the sub-block sizes (the segment's sub-block in block-row 0; block-rows
+  // are sstride[s] bytes apart).  Receive side, one wave per destination
+  // column d (lane s): the exclusive prefix along s (target packed by
+  // source).  Each side writes the flattened prefix in its own order.
+  for (int s2 = wave; s2 < P; s2 += kWaves) {
+    const int32_t c = lane < P ? C[lds_at(s2, lane)] : 0;
+    const int64_t v = int64_t(c) * p.elem;
+    const int64_t ex = wave_inclusive_scan(v) - v;
+    int64_t sv = v;
+    int64_t sex = ex;
+    if (p.nblk != 1) {
+      sv = int64_t(c / p.nblk) * p.elem;
+      sex = wave_inclusive_scan(sv) - sv;
+    }
+    if (lane < P) {
+      soff[lds_at(s2, lane)] = int64_t(s2) * p.in_slab + sex;
+      if (!dmajor) pre[lds_at(s2, lane)] = rowbase[s2] + ex;
+    }
+    if (lane == P - 1) p.ws.sstride[s2] = sex + sv;
+  }
+  for (int d = wave; d < P; d += kWaves) {
+    const int64_t v = lane < P ? int64_t(C[lds_at(lane, d)]) * p.elem : 0;
+    const int64_t ex = wave_inclusive_scan(v) - v;
+    if (lane < P) {
+      doff[lds_at(lane, d)] = int64_t(d) * p.tgt_slab + ex;
+      if (dmajor) pre[lds_at(d, lane)] = colbase[d] + ex;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < PP; i += kCountThreads) {
+    // Flattened segment i is s -> d: i = d*P + s (destination-major) or
+    // s*P + d (source-major); pre holds it at lds_at(d, s) or lds_at(s, d).
+    const int hi = i / P;
+    const int lo = i - hi * P;
+    const int s2 = dmajor ? lo : hi;
+    const int d = dmajor ? hi : lo;
+    p.ws.src_off[i] = soff[lds_at(s2, d)];
+    p.ws.prefix[i] = pre[lds_at(hi, lo)];
+    p.ws.dst_off[i] = doff[lds_at(s2, d)];
+  }
+  for (int b = tid; b < p.B; b += kCountThreads) p.ws.blk_cnt[b] = 0u;
+  if (tid < kArriveReplicas) p.ws.arrived[int64_t(tid) * kArriveStride] = 0u;
+  if (tid == 0) {
+    p.ws.prefix[PP] = rowbase[kMaxP];
+    p.ws.plan->claim[0] = 0u;
+    p.ws.plan->claim[1] = 0u;
+  }
+}
+
+// The run's verdict.  With one workgroup its flags decide.  Otherwise every
+// workgroup adds to one 64-bit word of the plan, in one atomic: 1 to the
+// count of workgroups done (bits 0-7) and 1 to the field of each failure
+// kind it found (8 bits each: at most 64 workgroups, so no field carries
+// into the next).  The add that brings the count to the grid size sees every
+// workgroup's findings; that workgroup latches the status or marks the run
+// valid, and clears the word for the next run.
+__device__ void verdict(const CountParams& p, int f, int64_t total) {
+  if (threadIdx.x != 0) return;
+  RunPlan* plan = p.ws.plan;
+  // Failure kinds (flag bits) and their fields.
+  constexpr int kKinds[5] = {1, 2, 4, 8, 16};
+  uint64_t mine = 1u;
+  for (int k = 0; k < 5; ++k)
+    if (f & kKinds[k]) mine += uint64_t(1) << (8 * (k + 1));
+  uint64_t all = mine;
+  if (gridDim.x > 1) {
+    all += __hip_atomic_fetch_add(&plan->kstate, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((all & 0xFFu) != gridDim.x) return;
+  }
+  int any = 0;
+  for (int k = 0; k < 5; ++k)
+    if ((all >> (8 * (k + 1))) & 0xFFu) any |= kKinds[k];
+  if (any != 0) {
+    // Order: negative count, count not whole sub-blocks or rows,
+    // over-capacity, gather index outside its table, unequal signal.
+    const int code = (any & 1) ? A2AV_ERR_INVALID_ARGS
+                   : (any & 8) ? A2AV_ERR_INVALID_ARGS
+                   : (any & 2) ? A2AV_ERR_OVER_CAPACITY
+                               : A2AV_ERR_INVALID_ARGS;
+    atomicCAS(&plan->error, 0, code);
+    plan->valid = 0;
+    if (p.status_out) *p.status_out = code;
+  } else {
+    plan->total_bytes = total;
+    plan->valid = 1;
+    if (p.status_out) *p.status_out = A2AV_OK;
+  }
+  if (gridDim.x > 1)
+    __hip_atomic_store(&plan->kstate, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
   __shared__ int32_t C[kMaxP * kPitch];     // C[lds_at(s, d)] = send_counts[s][d]
   __shared__ int64_t soff[kMaxP * kPitch];  // staged outputs, written back coalesced
@@ -134,17 +247,21 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
 
   // Row gather: this workgroup's slice of the P x index_stride gather-list
   // entries (flat position e = s * index_stride + k), split evenly among the
-  // launch's workgroups.  The thread's first kPre entries of it are loaded
-  // now, so that their round trip overlaps the counts'; which of them are in
-  // use (k below the rows source s sends) is known only once the counts are
-  // summed.  Every entry read lies inside the [P, index_stride] lists.
+  // launch's checking workgroups: all of them when the launch has one,
+  // otherwise every workgroup but 0, which writes the tables.  The thread's
+  // first kPre entries of it are loaded now, so that their round trip
+  // overlaps the counts'; which of them are in use (k below the rows source
+  // s sends) is known only once the counts are summed.  Every entry read
+  // lies inside the [P, index_stride] lists.
   constexpr int kPre = 8;
   int32_t pre_entry[kPre];
   int64_t g_lo = 0, g_hi = 0;
-  if (p.index != nullptr) {
+  if (p.index != nullptr && (gridDim.x == 1 || blockIdx.x != 0)) {
     const int64_t entries = int64_t(P) * p.index_stride;
-    const int64_t per = (entries + gridDim.x - 1) / gridDim.x;
-    g_lo = per * blockIdx.x < entries ? per * blockIdx.x : entries;
+    const int64_t checkers = gridDim.x == 1 ? 1 : gridDim.x - 1;
+    const int64_t slot = gridDim.x == 1 ? 0 : blockIdx.x - 1;
+    const int64_t per = (entries + checkers - 1) / checkers;
+    g_lo = per * slot < entries ? per * slot : entries;
     g_hi = g_lo + per < entries ? g_lo + per : entries;
 #pragma unroll
     for (int j = 0; j < kPre; ++j) {
@@ -256,105 +373,13 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountParams p) {
     __syncthreads();
   }
 
-  // The run's verdict: every workgroup adds its flags to one word of the
-  // plan (flags in the high half, then a count of workgroups in the low
-  // half: both on one address, so the last workgroup's count sees every
-  // workgroup's flags), and the last one to count latches the status or
-  // marks the run valid.  A launch of one workgroup decides on its own
-  // flags, without the round trip of the atomics.
   const int f = flags;
-  if (tid == 0) {
-    RunPlan* plan = p.ws.plan;
-    uint32_t old = uint32_t(f) << 16;
-    if (gridDim.x > 1) {
-      __hip_atomic_fetch_or(&plan->kstate, uint32_t(f) << 16, __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT);
-      old = __hip_atomic_fetch_add(&plan->kstate, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if ((old & 0xFFFFu) == gridDim.x - 1u) {
-      const int all = int(old >> 16);
-      if (all != 0) {
-        // Order: negative count, count not whole sub-blocks or rows,
-        // over-capacity, gather index outside its table, unequal signal.
-        const int code = (all & 1) ? A2AV_ERR_INVALID_ARGS
-                       : (all & 8) ? A2AV_ERR_INVALID_ARGS
-                       : (all & 2) ? A2AV_ERR_OVER_CAPACITY
-                                   : A2AV_ERR_INVALID_ARGS;
-        atomicCAS(&plan->error, 0, code);
-        plan->valid = 0;
-        if (p.status_out) *p.status_out = code;
-      } else {
-        plan->total_bytes = rowbase[kMaxP];
-        plan->valid = 1;
-        if (p.status_out) *p.status_out = A2AV_OK;
-      }
-      __hip_atomic_store(&plan->kstate, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  // Workgroup 0 writes the tables and clears the run's counters; the other
-  // workgroups are done.  The tables of a run that fails are never read.
-  if (f != 0 || blockIdx.x != 0) return;
-
-  // The flattened order K2 partitions.  The copy and bias bodies take it
-  // destination-major (segment j = d*P + s): the tiles in flight then write
-  // one contiguous stretch of a target slab and read pieces of several
-  // source slabs, which DRAM serves better than the transpose the other way
-  // round.  The row gather takes it source-major (j = s*P + d), measured
-  // faster for it.
-  const bool dmajor = p.index == nullptr;
-
-  // Send side, one wave per source row s (lane d): the exclusive prefix
-  // along d of the row's bytes (input packed by destination) gives the
-  // source offsets; with nblk > 1 the source offset is instead the prefix of
-  // the sub-block sizes (the segment's sub-block in block-row 0; block-rows
-  // are sstride[s] bytes apart).  Receive side, one wave per destination
-  // column d (lane s): the exclusive prefix along s (target packed by
-  // source).  Each side writes the flattened prefix in its own order.
-  for (int s2 = wave; s2 < P; s2 += kWaves) {
-    const int32_t c = lane < P ? C[lds_at(s2, lane)] : 0;
-    const int64_t v = int64_t(c) * p.elem;
-    const int64_t ex = wave_inclusive_scan(v) - v;
-    int64_t sv = v;
-    int64_t sex = ex;
-    if (p.nblk != 1) {
-      sv = int64_t(c / p.nblk) * p.elem;
-      sex = wave_inclusive_scan(sv) - sv;
-    }
-    if (lane < P) {
-      soff[lds_at(s2, lane)] = int64_t(s2) * p.in_slab + sex;
-      if (!dmajor) pre[lds_at(s2, lane)] = rowbase[s2] + ex;
-    }
-    if (lane == P - 1) p.ws.sstride[s2] = sex + sv;
-  }
-  for (int d = wave; d < P; d += kWaves) {
-    const int64_t v = lane < P ? int64_t(C[lds_at(lane, d)]) * p.elem : 0;
-    const int64_t ex = wave_inclusive_scan(v) - v;
-    if (lane < P) {
-      doff[lds_at(lane, d)] = int64_t(d) * p.tgt_slab + ex;
-      if (dmajor) pre[lds_at(d, lane)] = colbase[d] + ex;
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < PP; i += kCountThreads) {
-    // Flattened segment i is s -> d: i = d*P + s (destination-major) or
-    // s*P + d (source-major); pre holds it at lds_at(d, s) or lds_at(s, d).
-    const int hi = i / P;
-    const int lo = i - hi * P;
-    const int s2 = dmajor ? lo : hi;
-    const int d = dmajor ? hi : lo;
-    p.ws.src_off[i] = soff[lds_at(s2, d)];
-    p.ws.prefix[i] = pre[lds_at(hi, lo)];
-    p.ws.dst_off[i] = doff[lds_at(s2, d)];
-  }
-  for (int b = tid; b < p.B; b += kCountThreads) p.ws.blk_cnt[b] = 0u;
-  if (tid < kArriveReplicas) p.ws.arrived[int64_t(tid) * kArriveStride] = 0u;
-  if (tid == 0) {
-    p.ws.prefix[PP] = rowbase[kMaxP];
-    p.ws.plan->claim[0] = 0u;
-    p.ws.plan->claim[1] = 0u;
-  }
+  // Workgroup 0 writes the tables and clears the run's counters, then takes
+  // part in the verdict; the other workgroups go straight to it.  The tables
+  // of a run that fails are never read.
+  if (f == 0 && blockIdx.x == 0) write_tables(p, C, soff, pre, doff, rowbase, colbase);
+  verdict(p, f, rowbase[kMaxP]);
 }
-
 // ------------------------------------------------------------------ K2
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {

@@ -323,12 +323,14 @@ int enqueue_run(a2av_handle* h, const void* input, void* target, int32_t* signal
       ev = &h->events[size_t(h->run_counter % kProfileRuns) * size_t(h->events_per_run)];
   }
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
-  // The row gather's K1 checks every gather-list entry in use: its launch
-  // spreads them over up to 64 workgroups, about 8,192 entries each.
+  // The row gather's K1 checks every gather-list entry in use: beyond 8,192
+  // entries its launch spreads them over up to 63 workgroups besides
+  // workgroup 0, which writes the tables, about 8,192 entries each.
   int k1_wgs = 1;
   if (mode == 3) {
     const int64_t entries = int64_t(P) * x.index_stride;
-    k1_wgs = int(std::min<int64_t>(64, std::max<int64_t>(1, (entries + 8191) / 8192)));
+    const int64_t checkers = std::min<int64_t>(63, (entries + 8191) / 8192);
+    k1_wgs = checkers > 1 ? int(checkers) + 1 : 1;
   }
   if ((e = a2av::launch_count(cp, k1_wgs, s)) != hipSuccess)
     return hip_fail(h, e, "count_kernel launch");

@@ -173,6 +173,60 @@ def test_indexed_device_rejections_match_oracle(what):
     assert (c.target.cpu().numpy() == wl.SENTINEL).all()
 
 
+@pytest.mark.parametrize("what", ["clean", "index_first", "index_mid", "index_last_used",
+                                  "negative", "partial_row", "signal", "over_before_index"])
+def test_indexed_wide_check_verdict_then_clean_run(what):
+    # Gather lists of more than 2 x 8,192 entries, so K1 spreads their check
+    # over several workgroups that vote on the run's verdict: each failure
+    # kind, found by one checking workgroup (a bad entry at the start, in
+    # the middle or at the last entry in use of the lists) or by all of them
+    # (a count failure), against the oracle with nothing written; then a
+    # clean run on the same handle, which must find the verdict word cleared.
+    import copy
+    P, R = 4, 16
+    w, index = indexed_case(P, R, wl.INT8, 2048, 300, core_num=4, seed=33, zero_frac=0.0)
+    stride = index.shape[1]
+    assert P * stride > 2 * 8192
+    C = w.counts.copy()
+    rows = C.astype(np.int64).sum(axis=1) // R
+    bad_index = index.copy()
+    sig = wl.signal_np(w)
+    if what == "index_first":
+        bad_index[0, 0] = -1
+    elif what == "index_mid":
+        bad_index[2, min(int(rows[2]) - 1, stride // 2)] = 300
+    elif what == "index_last_used":
+        bad_index[3, rows[3] - 1] = 1 << 30
+    elif what == "negative":
+        C[1, 1] = -R
+    elif what == "partial_row":
+        C[2, 3] += 3
+    elif what == "signal":
+        sig[3, 2] += 1
+    elif what == "over_before_index":
+        C[0, 1] += R * (stride - int(rows[0]) + 1)
+        bad_index[1, 0] = -5
+    wb = copy.copy(w)
+    wb.counts = C.astype(np.int32)
+    say(what, P * stride)
+    ex = exchange_for(w)
+    try:
+        c = Case(wb, signal_np=sig)
+        st = c.run_gpu(ex, index=upload(bad_index), row_elems=R)
+        c.assert_matches(st, c.run_oracle(index=bad_index, row_elems=R))
+        if what == "clean":
+            assert st == a2av.OK
+        else:
+            assert st != a2av.OK
+            assert (c.target.cpu().numpy() == wl.SENTINEL).all()
+        c2 = Case(w)
+        st2 = c2.run_gpu(ex, index=upload(index), row_elems=R)
+        assert st2 == a2av.OK
+        c2.assert_matches(st2, c2.run_oracle(index=index, row_elems=R))
+    finally:
+        ex.close()
+
+
 def test_indexed_moe_full_size():
     # The MoE dispatch at full size: token tables of 4096 x 7168 int8 per
     # source, c3's routing as the gather lists.  Whole target against the
