@@ -31,10 +31,11 @@ constexpr int kArriveStride = 64;
 // Device workspace layout, carved out of one allocation by the host.
 struct Workspace {
   RunPlan* plan;
-  int64_t* prefix;   // [P*P + 1] exclusive prefix of segment bytes in the flattened
-                     // order (d-major, or s-major for the row gather)
-  int64_t* src_off;  // [P*P] byte offset inside `input` of each segment, flattened order
-  int64_t* dst_off;  // [P*P] byte offset inside `target` of each segment, flattened order
+  int64_t* prefix;   // [nseg + 1] exclusive prefix of segment bytes in the flattened
+                     // order (d-major, or s-major for the row gather); nseg = P*P, or
+                     // P*P*nblk when the blocked byte copy takes a segment per sub-block
+  int64_t* src_off;  // [nseg] byte offset inside `input` of each segment, flattened order
+  int64_t* dst_off;  // [nseg] byte offset inside `target` of each segment, flattened order
   uint32_t* blk_cnt; // [max blocks] workgroups of each block that finished copying
   int64_t* sstride;  // [P] bytes per source block-row (blocked exchange)
   uint32_t* arrived; // [kArriveReplicas * kArriveStride] admitted blocks that have raised
@@ -52,6 +53,7 @@ struct CountParams {
   int32_t B;
   int32_t elem;
   int32_t nblk;       // sub-blocks per segment (1 = plain exchange)
+  int32_t expand;     // 1: one table entry per sub-block (P * P * nblk entries, byte copy)
   int64_t unit;       // every count must be a multiple of this (nblk, nblk * hidden, or a row)
   // Indexed exchange only (index != nullptr): the gather lists, their
   // stride, and the whole rows each input table holds.

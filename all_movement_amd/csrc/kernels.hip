@@ -123,6 +123,7 @@ __device__ void write_tables(const CountParams& p, const int32_t* C, int64_t* so
   constexpr int kWaves = kCountThreads / kWave;
   const int P = p.P;
   const int PP = P * P;
+  __shared__ int64_t rstride[kMaxP];  // bytes per source block-row
 
   // The flattened order K2 partitions.  The copy and bias bodies take it
   // destination-major (segment j = d*P + s): the tiles in flight then write
@@ -153,7 +154,10 @@ __device__ void write_tables(const CountParams& p, const int32_t* C, int64_t* so
       soff[lds_at(s2, lane)] = int64_t(s2) * p.in_slab + sex;
       if (!dmajor) pre[lds_at(s2, lane)] = rowbase[s2] + ex;
     }
-    if (lane == P - 1) p.ws.sstride[s2] = sex + sv;
+    if (lane == P - 1) {
+      p.ws.sstride[s2] = sex + sv;
+      rstride[s2] = sex + sv;
+    }
   }
   for (int d = wave; d < P; d += kWaves) {
     const int64_t v = lane < P ? int64_t(C[lds_at(lane, d)]) * p.elem : 0;
@@ -164,21 +168,39 @@ __device__ void write_tables(const CountParams& p, const int32_t* C, int64_t* so
     }
   }
   __syncthreads();
-  for (int i = tid; i < PP; i += kCountThreads) {
-    // Flattened segment i is s -> d: i = d*P + s (destination-major) or
-    // s*P + d (source-major); pre holds it at lds_at(d, s) or lds_at(s, d).
-    const int hi = i / P;
-    const int lo = i - hi * P;
-    const int s2 = dmajor ? lo : hi;
-    const int d = dmajor ? hi : lo;
-    p.ws.src_off[i] = soff[lds_at(s2, d)];
-    p.ws.prefix[i] = pre[lds_at(hi, lo)];
-    p.ws.dst_off[i] = doff[lds_at(s2, d)];
+  if (p.expand) {
+    // The blocked byte copy, one segment per sub-block: entry v is sub-block
+    // a = v % nblk of destination-major pair j = v / nblk (d = j / P, s = j %
+    // P), so K2 copies every piece as in the plain exchange.  The flattened
+    // order is the same bytes in the same order as with P * P segments.
+    const int nb = p.nblk;
+    for (int v = tid; v < PP * nb; v += kCountThreads) {
+      const int j = v / nb;
+      const int a = v - j * nb;
+      const int d = j / P;
+      const int s2 = j - d * P;
+      const int64_t sub = int64_t(C[lds_at(s2, d)] / nb) * p.elem;
+      p.ws.prefix[v] = pre[lds_at(d, s2)] + a * sub;
+      p.ws.src_off[v] = soff[lds_at(s2, d)] + a * rstride[s2];
+      p.ws.dst_off[v] = doff[lds_at(s2, d)] + a * sub;
+    }
+  } else {
+    for (int i = tid; i < PP; i += kCountThreads) {
+      // Flattened segment i is s -> d: i = d*P + s (destination-major) or
+      // s*P + d (source-major); pre holds it at lds_at(d, s) or lds_at(s, d).
+      const int hi = i / P;
+      const int lo = i - hi * P;
+      const int s2 = dmajor ? lo : hi;
+      const int d = dmajor ? hi : lo;
+      p.ws.src_off[i] = soff[lds_at(s2, d)];
+      p.ws.prefix[i] = pre[lds_at(hi, lo)];
+      p.ws.dst_off[i] = doff[lds_at(s2, d)];
+    }
   }
   for (int b = tid; b < p.B; b += kCountThreads) p.ws.blk_cnt[b] = 0u;
   if (tid < kArriveReplicas) p.ws.arrived[int64_t(tid) * kArriveStride] = 0u;
   if (tid == 0) {
-    p.ws.prefix[PP] = rowbase[kMaxP];
+    p.ws.prefix[p.expand ? PP * p.nblk : PP] = rowbase[kMaxP];
     p.ws.plan->claim[0] = 0u;
     p.ws.plan->claim[1] = 0u;
   }
@@ -1147,7 +1169,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
   // d*P + s): the run's checks have passed, so a run that fails them, or whose
   // launches fail before the final one is enqueued, leaves it untouched.
   if (p.last && blockIdx.x == 0)
-    for (int i = tid; i < nseg; i += NT)
+    for (int i = tid; i < p.P * p.P; i += NT)
       p.recv_counts[i] = p.send_counts[(i % p.P) * p.P + i / p.P];
 
   // Tile size: at most tile_bytes<MODE>(), chosen so W workgroups take the

@@ -40,6 +40,23 @@ def test_blocked_sweep(P, nblk, dtype):
         check_case(w, nblk=nblk)
 
 
+@pytest.mark.parametrize("P,nblk", [(16, 16), (16, 17), (8, 64), (64, 1), (64, 2)])
+def test_blocked_segment_per_sub_block_bound(P, nblk):
+    # A handle's tables hold 4,096 entries: up to P * P * nblk = 4,096 the
+    # blocked byte copy takes one segment per sub-block (P = 16 with 16
+    # sub-blocks, P = 8 with 64), past it K2 walks the sub-blocks of each
+    # segment (P = 16 with 17, P = 64 with 2).  Both against the oracle, two
+    # runs each, with small chunks as well.
+    rng = np.random.default_rng(P * 1000 + nblk)
+    C = (rng.integers(0, 7, size=(P, P)) * nblk).astype(np.int32)
+    C[rng.random((P, P)) < 0.2] = 0
+    w = wl.custom(P, wl.INT8, C, core_num=2 * P + 1, seed=nblk)
+    w.in_slab += 24
+    say("P", P, "nblk", nblk, "entries", P * P * nblk)
+    check_case(w, nblk=nblk, runs=2)
+    check_case(w, nblk=nblk, chunk_limit_bytes=1000)
+
+
 @pytest.mark.parametrize("limit", [4096, 1000])
 def test_blocked_small_chunks(limit):
     rng = np.random.default_rng(limit)
