@@ -412,7 +412,11 @@ __device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, int64_t word) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, int(word * 16), 0, kLoadPolicy);
 }
 
-
+// The whole offset goes in the vector offset and soffset stays the constant
+// 0.  With an SGPR soffset this compiler leaves out the wait states it puts
+// between a 128-bit buffer store and a VALU write of the store's data
+// registers, and on gfx950 the stores then wrote the new values: a bias body
+// that stepped through its words by soffset gave wrong results.
 __device__ inline void store16(__amdgpu_buffer_rsrc_t r, int64_t word, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, int(word * 16), 0, kStorePolicy);
 }
