@@ -113,6 +113,18 @@ __device__ inline int64_t wave_inclusive_scan(int64_t v) {
   return v;
 }
 
+// The same scan on 32-bit values, when every partial sum fits: one DPP add
+// per step instead of two moves and a 64-bit add.
+__device__ inline int32_t wave_inclusive_scan32(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
 // K1's outputs for a valid run, by workgroup 0: the segment tables and the
 // cleared counters of the run.
 __device__ void write_tables(const CountParams& p, const int32_t* C, int64_t* soff, int64_t* pre,
@@ -132,6 +144,13 @@ __device__ void write_tables(const CountParams& p, const int32_t* C, int64_t* so
   // round.  The row gather takes it source-major (j = s*P + d), measured
   // faster for it.
   const bool dmajor = p.index == nullptr;
+  // A row's bytes never exceed in_slab and a column's never exceed tgt_slab
+  // (the capacity checks passed), so below 2^31 bytes per slab every partial
+  // sum fits a 32-bit scan.
+  const bool narrow = p.in_slab < (int64_t(1) << 31) && p.tgt_slab < (int64_t(1) << 31);
+  auto exclusive = [&](int64_t v) -> int64_t {
+    return narrow ? int64_t(wave_inclusive_scan32(int32_t(v))) - v : wave_inclusive_scan(v) - v;
+  };
 
   // Send side, one wave per source row s (lane d): the exclusive prefix
   // along d of the row's bytes (input packed by destination) gives the
@@ -143,12 +162,12 @@ __device__ void write_tables(const CountParams& p, const int32_t* C, int64_t* so
   for (int s2 = wave; s2 < P; s2 += kWaves) {
     const int32_t c = lane < P ? C[lds_at(s2, lane)] : 0;
     const int64_t v = int64_t(c) * p.elem;
-    const int64_t ex = wave_inclusive_scan(v) - v;
+    const int64_t ex = exclusive(v);
     int64_t sv = v;
     int64_t sex = ex;
     if (p.nblk != 1) {
       sv = int64_t(c / p.nblk) * p.elem;
-      sex = wave_inclusive_scan(sv) - sv;
+      sex = exclusive(sv);
     }
     if (lane < P) {
       soff[lds_at(s2, lane)] = int64_t(s2) * p.in_slab + sex;
@@ -161,7 +180,7 @@ __device__ void write_tables(const CountParams& p, const int32_t* C, int64_t* so
   }
   for (int d = wave; d < P; d += kWaves) {
     const int64_t v = lane < P ? int64_t(C[lds_at(lane, d)]) * p.elem : 0;
-    const int64_t ex = wave_inclusive_scan(v) - v;
+    const int64_t ex = exclusive(v);
     if (lane < P) {
       doff[lds_at(lane, d)] = int64_t(d) * p.tgt_slab + ex;
       if (dmajor) pre[lds_at(d, lane)] = colbase[d] + ex;
