@@ -144,10 +144,13 @@ __device__ void write_tables(const CountParams& p, const int32_t* C, int64_t* so
   // round.  The row gather takes it source-major (j = s*P + d), measured
   // faster for it.
   const bool dmajor = p.index == nullptr;
-  // A row's bytes never exceed in_slab and a column's never exceed tgt_slab
-  // (the capacity checks passed), so below 2^31 bytes per slab every partial
-  // sum fits a 32-bit scan.
-  const bool narrow = p.in_slab < (int64_t(1) << 31) && p.tgt_slab < (int64_t(1) << 31);
+  // A column's bytes never exceed tgt_slab, and outside the row gather a
+  // row's never exceed in_slab (the capacity checks passed), so below 2^31
+  // bytes per slab every partial sum fits a 32-bit scan.  The row gather
+  // bounds a row by its gather list instead (rows may repeat), which can
+  // pass 2^31 bytes from a small table: it keeps the 64-bit scans.
+  const bool narrow = dmajor && p.in_slab < (int64_t(1) << 31) &&
+                      p.tgt_slab < (int64_t(1) << 31);
   auto exclusive = [&](int64_t v) -> int64_t {
     return narrow ? int64_t(wave_inclusive_scan32(int32_t(v))) - v : wave_inclusive_scan(v) - v;
   };

@@ -246,6 +246,51 @@ def test_indexed_moe_full_size():
     assert torch.equal(c3.target, c.target)
 
 
+def test_indexed_source_sends_past_2_gib_from_a_small_table():
+    # A source may name a row many times, so what it sends is bounded by its
+    # gather list, not by its table: source 0 sends 1.25 GiB to each of three
+    # destinations from a 64 KiB table, so its send-side offsets pass 2^31
+    # while both slabs are below 2 GiB (K1's row scans must stay 64-bit here).
+    # Checked on the GPU against torch's gather of the named rows, with the
+    # unwritten tails, recv_counts and the signal.
+    P, R = 3, 4096
+    table_rows = 16
+    in_slab = table_rows * R
+    heavy, light = 327680, 5
+    rows = np.array([[heavy] * P, [light] * P, [light] * P], np.int64)
+    C = (rows * R).astype(np.int32)
+    tgt_slab = int(rows[:, 0].sum()) * R
+    assert int(rows[0].sum()) * R > (1 << 31) and tgt_slab < (1 << 31)
+    w = wl.custom(P, wl.INT8, C, core_num=8, seed=5, in_slab=in_slab, tgt_slab=tgt_slab)
+    rng = np.random.default_rng(5)
+    index = rng.integers(0, table_rows, size=(P, P * heavy + 1)).astype(np.int32)
+    say("row bytes of source 0", int(rows[0].sum()) * R, "tgt_slab", tgt_slab)
+    c = Case(w, host_input=False)
+    ix = upload(index)
+    ex = exchange_for(w)
+    try:
+        assert c.run_gpu(ex, index=ix, row_elems=R) == a2av.OK
+        idx = ix.long()
+        for d in range(P):
+            off = d * tgt_slab
+            for s in range(P):
+                k0, n = int(rows[s, :d].sum()), int(rows[s, d])
+                table = c.input[s * in_slab:(s + 1) * in_slab].view(table_rows, R)
+                want = table[idx[s, k0:k0 + n]].reshape(-1)
+                assert torch.equal(c.target[off:off + n * R], want), (s, d)
+                off += n * R
+            assert (c.target[off:(d + 1) * tgt_slab] == wl.SENTINEL).all()
+        np.testing.assert_array_equal(c.recv.cpu().numpy(), C.T)
+        B = a2av.a2av_blocks(P, 8)
+        sig = c.signal.cpu().numpy()
+        assert (sig[:, :B] == c.signal_np0[:, :B] + 1).all()
+        assert (sig[:, B:] == c.signal_np0[:, B:]).all()
+    finally:
+        ex.close()
+        del c
+        torch.cuda.empty_cache()
+
+
 def test_indexed_table_past_2_gib():
     # Token tables of more than 2^31 bytes: rows past the 2 GiB mark take the
     # 64-bit position path of the gather body, rows below it mix in.  The
