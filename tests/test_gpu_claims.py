@@ -1,8 +1,9 @@
 """GPU parity of K2's claimed tiles: a launch deals the first eighth of its
 tile rounds statically and hands the rest out from a counter, two counters
 alternating between the launches of a run and reused by the next run.  These
-cases make every launch large enough to claim (more than one round of 128 KiB
-tiles per workgroup), with odd and even numbers of launches, several runs on
+cases make every launch large enough to claim (more than one round of tiles
+per workgroup: 64 KiB for the byte copy, 128 KiB for the bias and gather
+bodies), with odd and even numbers of launches, several runs on
 one handle, several workgroups per block, and every body (plain, blocked,
 bias, row gather).  Bit-exact against the oracle after every run."""
 import numpy as np
