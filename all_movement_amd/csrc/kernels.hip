@@ -1067,7 +1067,9 @@ __device__ inline void tile_bounds(const SegTables& tab, int nseg, const uint8_t
 // Copy the flattened bytes [x, b) that start in segment i, piece by piece.
 // The target side of a segment is contiguous.  In the blocked exchange the
 // source side is nblk sub-blocks, sub-block a at tab.src[i] + a * sstride[s],
-// so a piece is also cut where a sub-block ends.
+// so a piece is also cut where a sub-block ends (the byte copy gets each
+// sub-block as a segment of its own when the tables hold them, and then
+// arrives here with nblk = 1).
 template <int MODE>
 __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int64_t x, int64_t b,
                                   int i, int tid, int lane, int wave, int& small) {
