@@ -125,6 +125,18 @@ __device__ inline int32_t wave_inclusive_scan32(int32_t v) {
   return v;
 }
 
+// Inclusive scans of two 32-lane halves of a wave at once (lanes 0-31 and
+// 32-63): the row steps, then lane 15 of each half into its upper row; the
+// last step, which would carry lane 31 into the upper half, is left out.
+__device__ inline int32_t wave_half_scan32(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  return v;
+}
+
 // K1's outputs for a valid run, by workgroup 0: the segment tables and the
 // cleared counters of the run.
 __device__ void write_tables(const CountParams& p, const int32_t* C, int64_t* soff, int64_t* pre,
@@ -162,31 +174,44 @@ __device__ void write_tables(const CountParams& p, const int32_t* C, int64_t* so
   // are sstride[s] bytes apart).  Receive side, one wave per destination
   // column d (lane s): the exclusive prefix along s (target packed by
   // source).  Each side writes the flattened prefix in its own order.
-  for (int s2 = wave; s2 < P; s2 += kWaves) {
-    const int32_t c = lane < P ? C[lds_at(s2, lane)] : 0;
+  // With 32-bit scans and P <= 32 a wave takes two rows (columns) at once,
+  // one per 32-lane half.
+  const bool pairs = narrow && P <= 32;
+  const int half = pairs ? lane >> 5 : 0;
+  const int l = pairs ? lane & 31 : lane;
+  const int per_wave = pairs ? 2 : 1;
+  auto excl = [&](int64_t v) -> int64_t {
+    return pairs ? int64_t(wave_half_scan32(int32_t(v))) - v : exclusive(v);
+  };
+  for (int s0 = wave * per_wave; s0 < P; s0 += kWaves * per_wave) {
+    const int s2 = s0 + half;
+    const bool on = l < P && s2 < P;
+    const int32_t c = on ? C[lds_at(s2, l)] : 0;
     const int64_t v = int64_t(c) * p.elem;
-    const int64_t ex = exclusive(v);
+    const int64_t ex = excl(v);
     int64_t sv = v;
     int64_t sex = ex;
     if (p.nblk != 1) {
       sv = int64_t(c / p.nblk) * p.elem;
-      sex = exclusive(sv);
+      sex = excl(sv);
     }
-    if (lane < P) {
-      soff[lds_at(s2, lane)] = int64_t(s2) * p.in_slab + sex;
-      if (!dmajor) pre[lds_at(s2, lane)] = rowbase[s2] + ex;
+    if (on) {
+      soff[lds_at(s2, l)] = int64_t(s2) * p.in_slab + sex;
+      if (!dmajor) pre[lds_at(s2, l)] = rowbase[s2] + ex;
     }
-    if (lane == P - 1) {
+    if (l == P - 1 && s2 < P) {
       p.ws.sstride[s2] = sex + sv;
       rstride[s2] = sex + sv;
     }
   }
-  for (int d = wave; d < P; d += kWaves) {
-    const int64_t v = lane < P ? int64_t(C[lds_at(lane, d)]) * p.elem : 0;
-    const int64_t ex = exclusive(v);
-    if (lane < P) {
-      doff[lds_at(lane, d)] = int64_t(d) * p.tgt_slab + ex;
-      if (dmajor) pre[lds_at(d, lane)] = colbase[d] + ex;
+  for (int d0 = wave * per_wave; d0 < P; d0 += kWaves * per_wave) {
+    const int d = d0 + half;
+    const bool on = l < P && d < P;
+    const int64_t v = on ? int64_t(C[lds_at(l, d)]) * p.elem : 0;
+    const int64_t ex = excl(v);
+    if (on) {
+      doff[lds_at(l, d)] = int64_t(d) * p.tgt_slab + ex;
+      if (dmajor) pre[lds_at(d, l)] = colbase[d] + ex;
     }
   }
   __syncthreads();
