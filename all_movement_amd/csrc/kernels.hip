@@ -1012,6 +1012,10 @@ struct SegTables {
   int64_t src[kMaxP * kMaxP];
   int64_t dst[kMaxP * kMaxP];
   int64_t sstride[kMaxP];  // bytes per source block-row (blocked exchange)
+  // prefix[64 k] for 64 k <= nseg, side by side: the first level of the
+  // whole-wave search reads it with consecutive lanes (prefix itself, read
+  // 64 entries apart, put every lane on the same LDS bank).
+  int64_t coarse[kWave];
 };
 
 // Largest segment i in [0, nseg) with prefix[i] <= x (prefix[0] = 0 <= x),
@@ -1027,23 +1031,21 @@ __device__ inline int seg_of(const int64_t* prefix, int nseg, int64_t x) {
 }
 
 // The same for a wave-uniform x, found by the wave's 64 lanes together: each
-// level reads one prefix entry per lane (64 candidates), and the ballot of
-// "prefix <= x", true on a leading run of lanes since the prefix never
-// falls, gives the next base.  One LDS round trip per level of 64 (nseg <=
-// 4096: at most two) where the binary search takes up to 12 in turn.  All
-// lanes of the wave must be active.
-__device__ inline int wave_seg_of(const int64_t* prefix, int nseg, int64_t x, int lane) {
+// level reads one entry per lane (64 candidates), and the ballot of "entry
+// <= x", true on a leading run of lanes since the prefix never falls, gives
+// the next base.  One LDS round trip per level of 64 (nseg <= 4096: at most
+// two) where the binary search takes up to 12 in turn; the first level reads
+// the side-by-side copy of every 64th entry.  All lanes of the wave must be
+// active.
+__device__ inline int wave_seg_of(const SegTables& t, int nseg, int64_t x, int lane) {
   int base = 0;
-  int span = nseg > kWave ? kWave : 1;
-  for (;;) {
-    const int i = base + lane * span;
-    const bool le = i < nseg && prefix[i] <= x;
-    const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(le));
-    base += (cnt - 1) * span;
-    if (span == 1) break;
-    span = 1;
+  if (nseg > kWave) {
+    const bool le = lane * kWave < nseg && t.coarse[lane] <= x;
+    base = (__builtin_popcountll(__builtin_amdgcn_ballot_w64(le)) - 1) * kWave;
   }
-  return base;
+  const int i = base + lane;
+  const bool le = i < nseg && t.prefix[i] <= x;
+  return base + __builtin_popcountll(__builtin_amdgcn_ballot_w64(le)) - 1;
 }
 
 // A tile boundary x moved forward (never past its segment's end or c_hi) so
@@ -1062,12 +1064,13 @@ __device__ inline int64_t align_boundary(const SegTables& t, int nseg, const uin
 // align_boundary for a wave-uniform x (the claimed tiles' bounds), searched
 // by the whole wave.
 __device__ inline int64_t align_boundary_w(const SegTables& t, int nseg, const uint8_t* target,
-                                           int64_t x, int64_t c_hi, int lane) {
-  const int i = wave_seg_of(t.prefix, nseg, x, lane);
+                                           int64_t x, int64_t c_hi, int lane, int& seg) {
+  const int i = wave_seg_of(t, nseg, x, lane);
   const uintptr_t a = uintptr_t(target) + uintptr_t(t.dst[i] + (x - t.prefix[i]));
   int64_t y = x + int64_t((0u - a) & 127u);
   if (y > t.prefix[i + 1]) y = t.prefix[i + 1];
   if (y > c_hi) y = c_hi;
+  seg = i;
   return y;
 }
 
@@ -1194,6 +1197,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
       tab.dst[i] = p.ws.dst_off[i];
     }
     if (tid < p.P) tab.sstride[tid] = p.ws.sstride[tid];
+    if (tid < kWave && tid * kWave < nseg) tab.coarse[tid] = p.ws.prefix[tid * kWave];
   };
   // The flag and the payload size are loaded together (one round trip).  The
   // final launch has payload whenever the run has any, so it stages the
@@ -1285,12 +1289,16 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
       if (tid == 0) next = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int64_t x0 = c_lo + t * tile;
       const int64_t x1 = x0 + tile < c_hi ? x0 + tile : c_hi;
-      const int64_t a = t == 0 ? c_lo : align_boundary_w(tab, nseg, p.target, x0, c_hi, lane);
-      const int64_t b = x1 >= c_hi ? c_hi : align_boundary_w(tab, nseg, p.target, x1, c_hi, lane);
+      // The segment that holds a: the one x0 lies in, unless a was moved to
+      // that segment's end (or the tile is the launch's first).
+      int ia = 0;
+      int ib = 0;
+      const int64_t a = t == 0 ? c_lo : align_boundary_w(tab, nseg, p.target, x0, c_hi, lane, ia);
+      const int64_t b = x1 >= c_hi ? c_hi : align_boundary_w(tab, nseg, p.target, x1, c_hi, lane, ib);
+      if (t == 0 || a >= tab.prefix[ia + 1]) ia = wave_seg_of(tab, nseg, a, lane);
       if (a < b)
         copy_range<MODE>(p, tab, wave_uniform(a), wave_uniform(b),
-                         __builtin_amdgcn_readfirstlane(wave_seg_of(tab.prefix, nseg, a, lane)),
-                         tid, lane, wave, small);
+                         __builtin_amdgcn_readfirstlane(ia), tid, lane, wave, small);
       // The next claim goes to the other slot: every thread read it at the
       // start of the previous tile, before the barrier that ended that tile.
       if (tid == 0) s_claim[slot ^ 1] = nstatic + int64_t(next);
