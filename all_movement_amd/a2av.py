@@ -42,12 +42,13 @@ EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_run_bias", "a2av
            "a2av_profile_sample", "a2av_status_string", "a2av_last_hip_error"]
 
 
-# Streaming probes (include/a2av_probe.h): measurement of the copy kernel's
-# instructions alone, not part of the exchange.
+# Probes (include/a2av_probe.h): measurement of the copy kernel's
+# instructions alone and of the cooperative launch's own cost, not part of
+# the exchange.
 PROBE_READ = 0
 PROBE_WRITE = 1
 PROBE_COPY = 2
-PROBE_EXPORTS = ["a2av_probe_stream"]
+PROBE_EXPORTS = ["a2av_probe_stream", "a2av_probe_launch"]
 
 
 class a2av_config(ctypes.Structure):
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
     L.a2av_run_noalloc.restype = ctypes.c_int
     L.a2av_probe_stream.argtypes = [i32, vp, vp, i64, i32, vp]
     L.a2av_probe_stream.restype = ctypes.c_int
+    L.a2av_probe_launch.argtypes = [i32, vp, i64, i32, vp]
+    L.a2av_probe_launch.restype = ctypes.c_int
     L.a2av_destroy.argtypes = [vp]
     L.a2av_destroy.restype = ctypes.c_int
     L.a2av_blocks.argtypes = [i64, i64]
@@ -188,6 +191,10 @@ def a2av_run_noalloc(input, target, signal, send_counts, recv_counts, status, P,
 
 def a2av_probe_stream(kind, src, dst, nbytes, workgroups, stream) -> int:
     return lib().a2av_probe_stream(kind, src, dst, nbytes, workgroups, stream)
+
+
+def a2av_probe_launch(cooperative, dst, nbytes, workgroups, stream) -> int:
+    return lib().a2av_probe_launch(cooperative, dst, nbytes, workgroups, stream)
 
 
 def a2av_destroy(h) -> int:

@@ -1,7 +1,9 @@
-// probe.hip -- the streaming probes of include/a2av_probe.h: read-only,
-// write-only and copy kernels built from the copy kernel's memory
-// instructions and launch shape, to measure the rates those instructions
-// reach on the device (the exchange's achievable ceiling).
+// probe.hip -- the probes of include/a2av_probe.h: read-only, write-only and
+// copy kernels built from the copy kernel's memory instructions and launch
+// shape, to measure the rates those instructions reach on the device (the
+// exchange's achievable ceiling); and a store kernel launched either as a
+// regular or as a cooperative launch, to measure what the cooperative launch
+// itself costs.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -89,7 +91,50 @@ __global__ __launch_bounds__(kThreads) void probe_kernel(const uint8_t* src, uin
   }
 }
 
+// The launch probe: each thread stores its 16-byte words of `bytes` with the
+// copy kernel's store instruction, grid-stride; bytes = 0 stores nothing.
+__global__ __launch_bounds__(kThreads) void launch_probe_kernel(uint8_t* dst, int64_t bytes) {
+  const int64_t K = bytes >> 4;
+  if (K == 0) return;
+  const __amdgpu_buffer_rsrc_t rd = rsrc(dst, bytes);
+  const u32x4 pattern = u32x4{0xA5A5A5A5u, 0xA5A5A5A5u, 0xA5A5A5A5u, 0xA5A5A5A5u};
+  for (int64_t k = int64_t(blockIdx.x) * kThreads + threadIdx.x; k < K;
+       k += int64_t(gridDim.x) * kThreads)
+    __builtin_amdgcn_raw_buffer_store_b128(pattern, rd, int(k * 16), 0, kStorePolicy);
+}
+
 }  // namespace
+
+extern "C" int a2av_probe_launch(int32_t cooperative, void* dst, int64_t bytes,
+                                 int32_t workgroups, void* stream) {
+  if (cooperative != 0 && cooperative != 1) return A2AV_ERR_INVALID_ARGS;
+  if (bytes < 0 || bytes % 16 != 0 || bytes >= (int64_t(1) << 31) || workgroups < 0)
+    return A2AV_ERR_INVALID_ARGS;
+  if (bytes > 0 && !dst) return A2AV_ERR_NULLPTR;
+  if ((uintptr_t(dst) & 15u) != 0) return A2AV_ERR_INVALID_ARGS;
+  int W = workgroups;
+  if (W == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&W, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return A2AV_ERR_HIP;
+    }
+  }
+  uint8_t* d = static_cast<uint8_t*>(dst);
+  void* args[] = {&d, &bytes};
+  const void* f = reinterpret_cast<const void*>(&launch_probe_kernel);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = cooperative
+                           ? hipLaunchCooperativeKernel(f, dim3(W), dim3(kThreads), args, 0, s)
+                           : hipLaunchKernel(f, dim3(W), dim3(kThreads), args, 0, s);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return cooperative && e == hipErrorCooperativeLaunchTooLarge ? A2AV_ERR_LAUNCH_CAPACITY
+                                                                 : A2AV_ERR_HIP;
+  }
+  return A2AV_OK;
+}
 
 extern "C" int a2av_probe_stream(int32_t kind, const void* src, void* dst, int64_t bytes,
                                  int32_t workgroups, void* stream) {

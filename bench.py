@@ -10,7 +10,9 @@ timed on a bounded sample of the same workload on the host.  Each workload
 is also timed cache-cold: a 1 GiB buffer is written before every run, and
 the medians of the single runs are reported under "cold".  The small
 exchanges (c1, c2) are also timed as replays of one run captured into a HIP
-graph ("graph").
+graph ("graph").  Beside them: the rates of the copy kernel's own
+instructions streaming 1 GiB ("ceiling"), and what a cooperative launch
+costs on the stream against a regular one ("launch_cost").
 
     python bench.py [--steps K] [--warmup W] [--workload c5] [--also c3,c4]
 """
@@ -306,6 +308,46 @@ def stream_ceiling(nbytes: int = 1 << 30, reps: int = 10, warmup: int = 3):
     return out
 
 
+def launch_cost(nbytes: int = 64 << 20, reps: int = 40, warmup: int = 5):
+    """What a cooperative launch costs on the stream, apart from any exchange
+    (the library's launch probe): pairs of launches, one workgroup per CU, a
+    store kernel writing `nbytes` with the copy kernel's store instruction and
+    then the same kernel storing nothing, each launch regular or cooperative,
+    back to back on one stream, timed with HIP events on that stream.  A
+    cooperative launch's cost is the pair time with it less the pair time
+    with both launches regular."""
+    import torch
+    from all_movement_amd import a2av
+    dev = torch.device("cuda:0")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {"bytes_first_launch": nbytes, "pairs": reps}
+    for name, (c0, c1) in [("regular_regular", (0, 0)), ("coop_regular", (1, 0)),
+                           ("regular_coop", (0, 1)), ("coop_coop", (1, 1))]:
+        def pair():
+            for coop, n in ((c0, nbytes), (c1, 0)):
+                st = a2av.a2av_probe_launch(coop, dst.data_ptr(), n, 0, stream.cuda_stream)
+                if st != a2av.OK:
+                    raise RuntimeError(f"a2av_probe_launch: {a2av.a2av_status_string(st)}")
+        for _ in range(warmup):
+            pair()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            pair()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    rr = out["regular_regular_us"]
+    extra = [out["coop_regular_us"] - rr, out["regular_coop_us"] - rr,
+             (out["coop_coop_us"] - rr) / 2]
+    out["per_cooperative_launch_us"] = round(sum(extra) / len(extra), 2)
+    del dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(spec: Spec, min_seconds: float = 10.0):
     """The oracle (as it stands) on a bounded sample of the workload on the host."""
     import numpy as np
@@ -389,7 +431,11 @@ def main():
     ap.add_argument("--ceiling-only", action="store_true",
                     help="only time the streaming probes (read-only, write-only, copy of 1 GiB "
                          "with the copy kernel's instructions) and print them")
-    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming probes")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming probes and the launch probe")
+    ap.add_argument("--launch-cost-only", action="store_true",
+                    help="only time the launch probe (regular against cooperative launches, "
+                         "--steps pairs of each kind) and print it")
     ap.add_argument("--no-block-wait", action="store_true",
                     help="run the main workload on a handle with A2AV_FLAG_NO_BLOCK_WAIT (a "
                          "regular final launch; for counter runs under a profiler)")
@@ -408,6 +454,9 @@ def main():
         return
     if args.ceiling_only:
         print(json.dumps({"ceiling": stream_ceiling(reps=args.steps)}), flush=True)
+        return
+    if args.launch_cost_only:
+        print(json.dumps({"launch_cost": launch_cost(reps=args.steps)}), flush=True)
         return
     spec = WORKLOADS[args.workload]
     if args.no_block_wait:
@@ -447,6 +496,7 @@ def main():
         roofline["frac_of_ceiling"] = round(roofline["achieved"] / ceiling["copy"]["gbps"], 4)
     else:
         ceiling = None
+    coop_cost = None if args.no_ceiling else launch_cost()
     out = {
         "metric": METRIC, "value": round(main_res["gbps"], 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
@@ -462,6 +512,7 @@ def main():
         "cold": main_res["cold"],
         "graph": main_res["graph"],
         "ceiling": ceiling,
+        "launch_cost": coop_cost,
         "also": also,
     }
     if not args.no_cpu:

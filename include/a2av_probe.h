@@ -1,9 +1,11 @@
 /*
- * a2av_probe.h -- streaming probes of the MI355X library: the rates that the
- * copy kernel's own memory instructions reach on the device when they only
- * read, only write, or copy.  They are measurement, not part of the exchange:
- * they give the achievable ceiling against which the exchange's bandwidth
- * is read, beside the published HBM peak.
+ * a2av_probe.h -- probes of the MI355X library: the rates that the copy
+ * kernel's own memory instructions reach on the device when they only read,
+ * only write, or copy, and the cost of a cooperative launch against a
+ * regular one.  They are measurement, not part of the exchange: they give
+ * the achievable ceiling against which the exchange's bandwidth is read,
+ * beside the published HBM peak, and the fixed cost its final launch pays
+ * when it is cooperative.
  *
  * Each probe streams `bytes` through the same instructions and launch shape
  * as the segment-copy kernel's byte copy: 1024-thread workgroups (one per
@@ -34,6 +36,25 @@ enum a2av_probe_kind { A2AV_PROBE_READ = 0, A2AV_PROBE_WRITE = 1, A2AV_PROBE_COP
 
 int a2av_probe_stream(int32_t kind, const void *src, void *dst, int64_t bytes,
                       int32_t workgroups, void *stream);
+
+/*
+ * Launch probe: one launch of `workgroups` 1024-thread workgroups (0 = one
+ * per compute unit) that stores `bytes` bytes of the pattern 0xA5 into dst
+ * with the copy kernel's store instruction (buffer_store nt sc1, grid-stride;
+ * bytes = 0 stores nothing), enqueued on `stream` either as a regular launch
+ * (cooperative = 0, hipLaunchKernel) or as a cooperative one (cooperative =
+ * 1, hipLaunchCooperativeKernel, as the exchange's final launch when it
+ * admits more than one block).  Timing launches of each kind back to back
+ * gives the cooperative launch's own cost on the stream, apart from any
+ * exchange.  Measurement only.  dst is a device pointer, 16-byte aligned,
+ * and may be NULL when bytes = 0; bytes is a multiple of 16 in [0, 2^31).
+ * The call does not synchronize.
+ * Returns A2AV_OK, A2AV_ERR_NULLPTR, A2AV_ERR_INVALID_ARGS (cooperative not
+ * 0 or 1, size, alignment, workgroups < 0), A2AV_ERR_LAUNCH_CAPACITY (a
+ * cooperative grid the device cannot hold at once) or A2AV_ERR_HIP.
+ */
+int a2av_probe_launch(int32_t cooperative, void *dst, int64_t bytes, int32_t workgroups,
+                      void *stream);
 
 #ifdef __cplusplus
 }

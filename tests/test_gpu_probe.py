@@ -1,6 +1,7 @@
-"""The streaming probes (include/a2av_probe.h) run and move what they say:
-the copy probe's output equals its input, the write probe fills its buffer
-with 0xA5, the read probe writes nothing; bad arguments are refused."""
+"""The probes (include/a2av_probe.h) run and move what they say: the copy
+probe's output equals its input, the write probe fills its buffer with 0xA5,
+the read probe writes nothing, the launch probe writes its bytes and nothing
+past them, regular or cooperative; bad arguments are refused."""
 import pytest
 
 torch = pytest.importorskip("torch")
@@ -56,4 +57,33 @@ def test_probe_rejects_bad_arguments():
     assert run(n=0) == a2av.ERR_INVALID_ARGS
     assert run(n=1000) == a2av.ERR_INVALID_ARGS
     assert run(s=p + 4) == a2av.ERR_INVALID_ARGS
+    assert run(w=-1) == a2av.ERR_INVALID_ARGS
+
+
+@pytest.mark.parametrize("coop", [0, 1])
+@pytest.mark.parametrize("nbytes", [0, 16, (1 << 20) + 32, 64 << 20])
+def test_launch_probe_writes_its_bytes(coop, nbytes):
+    buf = torch.zeros(nbytes + 4096, dtype=torch.uint8, device=DEV)
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    say("launch probe", coop, nbytes)
+    for w in (0, 64):
+        assert a2av.a2av_probe_launch(coop, buf.data_ptr(), nbytes, w, stream) == a2av.OK
+        torch.cuda.synchronize()
+        assert bool((buf[:nbytes] == 0xA5).all())
+        assert int(buf[nbytes:].count_nonzero()) == 0
+    assert a2av.a2av_probe_launch(coop, None, 0, 0, stream) == a2av.OK
+    torch.cuda.synchronize()
+
+
+def test_launch_probe_rejects_bad_arguments():
+    buf = torch.empty(4096, dtype=torch.uint8, device=DEV)
+    p = buf.data_ptr()
+    run = lambda coop=0, d=p, n=1024, w=0: a2av.a2av_probe_launch(coop, d, n, w, None)  # noqa: E731
+    assert run(coop=2) == a2av.ERR_INVALID_ARGS
+    assert run(coop=-1) == a2av.ERR_INVALID_ARGS
+    assert run(d=None) == a2av.ERR_NULLPTR
+    assert run(n=-16) == a2av.ERR_INVALID_ARGS
+    assert run(n=1000) == a2av.ERR_INVALID_ARGS
+    assert run(n=1 << 31) == a2av.ERR_INVALID_ARGS
+    assert run(d=p + 4) == a2av.ERR_INVALID_ARGS
     assert run(w=-1) == a2av.ERR_INVALID_ARGS
