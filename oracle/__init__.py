@@ -65,37 +65,51 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(_LIB):
             build(force=False)
-        L = ctypes.CDLL(_LIB)
-        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
-        L.a2av_oracle_blocks.argtypes = [i64, i64]
-        L.a2av_oracle_blocks.restype = i64
-        run_args = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i64]
-        L.a2av_oracle_run.argtypes = run_args
-        L.a2av_oracle_run.restype = ctypes.c_int
-        L.a2av_oracle_check.argtypes = run_args
-        L.a2av_oracle_check.restype = ctypes.c_int
-        L.a2av_oracle_run_blocked.argtypes = run_args + [i32]
-        L.a2av_oracle_run_blocked.restype = ctypes.c_int
-        L.a2av_oracle_run_bias.argtypes = run_args + [i32, vp, i32]
-        L.a2av_oracle_run_bias.restype = ctypes.c_int
-        L.a2av_oracle_run_indexed.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i64,
-                                              i32, i64, i32, i64]
-        L.a2av_oracle_run_indexed.restype = ctypes.c_int
-        u16, u32 = ctypes.c_uint16, ctypes.c_uint32
-        L.a2av_oracle_f32_to_bf16.argtypes = [u32]
-        L.a2av_oracle_f32_to_bf16.restype = u16
-        L.a2av_oracle_bf16_to_f32.argtypes = [u16]
-        L.a2av_oracle_bf16_to_f32.restype = u32
-        L.a2av_oracle_f32_to_f16.argtypes = [u32]
-        L.a2av_oracle_f32_to_f16.restype = u16
-        L.a2av_oracle_f16_to_f32.argtypes = [u16]
-        L.a2av_oracle_f16_to_f32.restype = u32
-        L.a2av_oracle_displacements.argtypes = [vp, i32, i32, vp, vp]
-        L.a2av_oracle_displacements.restype = None
-        L.a2av_oracle_move.argtypes = [vp, vp, vp, i32, i32, i64, i64]
-        L.a2av_oracle_move.restype = None
-        _lib = L
+        _lib = load(_LIB)
     return _lib
+
+
+def use_library(path: str) -> None:
+    """Route every call of this module to the oracle library at ``path``
+    (the tests' mutation pins run the pins against deliberately broken
+    copies of ``a2av_oracle.c``, one process per copy)."""
+    global _lib
+    _lib = load(path)
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Load an oracle library built from ``a2av_oracle.c`` and declare its
+    functions' argument and return types."""
+    L = ctypes.CDLL(path)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    L.a2av_oracle_blocks.argtypes = [i64, i64]
+    L.a2av_oracle_blocks.restype = i64
+    run_args = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i64]
+    L.a2av_oracle_run.argtypes = run_args
+    L.a2av_oracle_run.restype = ctypes.c_int
+    L.a2av_oracle_check.argtypes = run_args
+    L.a2av_oracle_check.restype = ctypes.c_int
+    L.a2av_oracle_run_blocked.argtypes = run_args + [i32]
+    L.a2av_oracle_run_blocked.restype = ctypes.c_int
+    L.a2av_oracle_run_bias.argtypes = run_args + [i32, vp, i32]
+    L.a2av_oracle_run_bias.restype = ctypes.c_int
+    L.a2av_oracle_run_indexed.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i64,
+                                          i32, i64, i32, i64]
+    L.a2av_oracle_run_indexed.restype = ctypes.c_int
+    u16, u32 = ctypes.c_uint16, ctypes.c_uint32
+    L.a2av_oracle_f32_to_bf16.argtypes = [u32]
+    L.a2av_oracle_f32_to_bf16.restype = u16
+    L.a2av_oracle_bf16_to_f32.argtypes = [u16]
+    L.a2av_oracle_bf16_to_f32.restype = u32
+    L.a2av_oracle_f32_to_f16.argtypes = [u32]
+    L.a2av_oracle_f32_to_f16.restype = u16
+    L.a2av_oracle_f16_to_f32.argtypes = [u16]
+    L.a2av_oracle_f16_to_f32.restype = u32
+    L.a2av_oracle_displacements.argtypes = [vp, i32, i32, vp, vp]
+    L.a2av_oracle_displacements.restype = None
+    L.a2av_oracle_move.argtypes = [vp, vp, vp, i32, i32, i64, i64]
+    L.a2av_oracle_move.restype = None
+    return L
 
 
 def blocks(P: int, L: int) -> int:

@@ -290,6 +290,12 @@ def test_diagnostics_each_row():
     assert _chk(b, P, S, 16, 16, core_num=2**31 - 1) == oracle.ERR_INVALID_ARGS  # B huge > S
     assert _chk(b, P, S, 16, 16, core_num=5) == oracle.OK                         # B = 4 = S
     assert _chk(b, P, S, 16, 16, core_num=8) == oracle.ERR_INVALID_ARGS           # B = 8 > S
+    # S >= B exactly ("Launch width": the signal holds a column per admitted
+    # block): S = B passes, S = B - 1 does not.
+    b7, b8 = list(_buffers(P, 7, 16, 16)), _buffers(P, 8, 16, 16)
+    b7[2] = np.zeros(P * 8, np.int32)[:P * 7].reshape(P, 7)   # zeros past the last row too
+    assert _chk(b7, P, 7, 16, 16, core_num=8) == oracle.ERR_INVALID_ARGS          # S = B - 1
+    assert _chk(b8, P, 8, 16, 16, core_num=8) == oracle.OK                        # S = B
     bS = _buffers(P, 8, 16, 16)
     assert _chk(bS, P, 8, 16, 16, core_num=8, capacity=4) == oracle.ERR_LAUNCH_CAPACITY
     assert _chk(bS, P, 8, 16, 16, core_num=8, capacity=8) == oracle.OK
@@ -320,6 +326,29 @@ def test_diagnostics_each_row():
     bs[2][3, 3] = 0
     bs[2][3, 5] = 9
     assert _chk(bs, P, 8, 16, 16, core_num=4) == oracle.OK
+
+
+def test_adjacent_operands_are_distinct():
+    # "Current limitations" asks for distinct windows: operands that touch
+    # without sharing a byte are distinct, one shared byte is not.  The five
+    # operands carved back to back from one allocation.
+    P, S, slab = 4, 4, 16
+    sizes = [P * slab, P * slab, P * S * 4, P * P * 4, P * P * 4]
+    pool = np.zeros(sum(sizes) + 8, np.uint8)
+    base = (pool.ctypes.data + 3) & ~3
+    ptrs, at = [], base
+    for n in sizes:
+        ptrs.append(at)
+        at += n
+    counts = np.ones((P, P), np.int32)
+    ctypes.memmove(ptrs[3], counts.ctypes.data, counts.nbytes)
+    chk = lambda q: oracle.check(*q, P=P, S=S, in_slab=slab, tgt_slab=slab,  # noqa: E731
+                                 core_num=1, dtype=wl.INT8, capacity=0)
+    assert chk(ptrs) == oracle.OK
+    for i in range(1, 5):                    # operand i moved one byte into operand i - 1
+        q = list(ptrs)
+        q[i] -= 1
+        assert chk(q) == oracle.ERR_INVALID_ARGS, i
 
 
 def test_diagnostics_precedence():
