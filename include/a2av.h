@@ -85,8 +85,10 @@ enum a2av_status {
  * cooperative run: on one GPU the wait is not observable, since the flags are
  * raised before it and the kernel's end already orders every copy before
  * later work on the stream.  What it saves is the cooperative launch's own
- * cost (about 20 us of idle GPU per run on an MI355X).  The default keeps the
- * all-resident launch of the "Launch width" section of the PyPTO page. */
+ * cost (about 20 us of idle GPU per run on an MI355X: the HIP runtime runs
+ * cooperative launches on a second hardware queue, and the hand-offs to and
+ * from it leave the GPU idle).  The default keeps the all-resident launch of
+ * the "Launch width" section of the PyPTO page. */
 #define A2AV_FLAG_NO_BLOCK_WAIT 2u
 
 typedef struct a2av_config {
