@@ -37,6 +37,8 @@ FLAG_NO_BLOCK_WAIT = 2
 
 EXPORTS = ["a2av_create", "a2av_run", "a2av_run_blocked", "a2av_run_bias", "a2av_run_indexed",
            "a2av_run_noalloc", "a2av_run_host_counts", "a2av_check_host_counts",
+           "a2av_run_blocked_host_counts", "a2av_run_bias_host_counts",
+           "a2av_run_indexed_host_counts", "a2av_check_host_counts_ex",
            "a2av_check_bias_args", "a2av_check_indexed_args", "a2av_destroy",
            "a2av_blocks", "a2av_check_args", "a2av_query_error", "a2av_launch_info_get", "a2av_profile_read",
            "a2av_profile_sample", "a2av_status_string", "a2av_last_hip_error"]
@@ -95,6 +97,17 @@ def lib() -> ctypes.CDLL:
     L.a2av_run_host_counts.restype = ctypes.c_int
     L.a2av_check_host_counts.argtypes = [cfgp, vp, i32, ctypes.POINTER(i64), ctypes.POINTER(i32)]
     L.a2av_check_host_counts.restype = ctypes.c_int
+    L.a2av_run_blocked_host_counts.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
+    L.a2av_run_blocked_host_counts.restype = ctypes.c_int
+    L.a2av_run_bias_host_counts.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                            i32, vp]
+    L.a2av_run_bias_host_counts.restype = ctypes.c_int
+    L.a2av_run_indexed_host_counts.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                               i64, vp]
+    L.a2av_run_indexed_host_counts.restype = ctypes.c_int
+    L.a2av_check_host_counts_ex.argtypes = [cfgp, vp, i32, i64, i64, ctypes.POINTER(i64),
+                                            ctypes.POINTER(i32)]
+    L.a2av_check_host_counts_ex.restype = ctypes.c_int
     L.a2av_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i32, i64, i32, vp]
     L.a2av_run_noalloc.restype = ctypes.c_int
     L.a2av_probe_stream.argtypes = [i32, vp, vp, i64, i32, vp]
@@ -168,18 +181,54 @@ def a2av_run_host_counts(h, input, target, signal, send_counts, recv_counts, hos
                                       host_send_counts, P, core_num, dtype, stream)
 
 
-def a2av_check_host_counts(cfg: a2av_config, host_send_counts, dtype) -> tuple[int, int, int]:
-    """(status, payload bytes, chunk launches); host_send_counts is an int32
-    numpy array [P, P] (or a raw host address)."""
+def a2av_run_blocked_host_counts(h, input, target, signal, send_counts, recv_counts,
+                                 host_send_counts, P, core_num, dtype, nblk, stream) -> int:
+    return lib().a2av_run_blocked_host_counts(h, input, target, signal, send_counts, recv_counts,
+                                              host_send_counts, P, core_num, dtype, nblk, stream)
+
+
+def a2av_run_bias_host_counts(h, input, target, signal, send_counts, recv_counts, bias,
+                              host_send_counts, P, core_num, dtype, nblk, hidden, stream) -> int:
+    return lib().a2av_run_bias_host_counts(h, input, target, signal, send_counts, recv_counts,
+                                           bias, host_send_counts, P, core_num, dtype, nblk,
+                                           hidden, stream)
+
+
+def a2av_run_indexed_host_counts(h, input, target, signal, send_counts, recv_counts, index,
+                                 host_send_counts, P, core_num, dtype, row_elems, index_stride,
+                                 stream) -> int:
+    return lib().a2av_run_indexed_host_counts(h, input, target, signal, send_counts, recv_counts,
+                                              index, host_send_counts, P, core_num, dtype,
+                                              row_elems, index_stride, stream)
+
+
+def _host_ptr(host_send_counts):
     import numpy as np
-    ptr = host_send_counts
     if isinstance(host_send_counts, np.ndarray):
         if host_send_counts.dtype != np.int32 or not host_send_counts.flags.c_contiguous:
             raise ValueError("host_send_counts must be a contiguous int32 array")
-        ptr = host_send_counts.ctypes.data
+        return host_send_counts.ctypes.data
+    return host_send_counts
+
+
+def a2av_check_host_counts(cfg: a2av_config, host_send_counts, dtype) -> tuple[int, int, int]:
+    """(status, payload bytes, chunk launches); host_send_counts is an int32
+    numpy array [P, P] (or a raw host address)."""
     payload, launches = ctypes.c_int64(), ctypes.c_int32()
-    st = lib().a2av_check_host_counts(ctypes.byref(cfg), ptr, dtype, ctypes.byref(payload),
-                                      ctypes.byref(launches))
+    st = lib().a2av_check_host_counts(ctypes.byref(cfg), _host_ptr(host_send_counts), dtype,
+                                      ctypes.byref(payload), ctypes.byref(launches))
+    return st, payload.value, launches.value
+
+
+def a2av_check_host_counts_ex(cfg: a2av_config, host_send_counts, dtype, unit: int,
+                              index_stride: int) -> tuple[int, int, int]:
+    """a2av_check_host_counts for every exchange: (status, payload bytes,
+    chunk launches) with counts in multiples of ``unit`` and, when
+    ``index_stride`` > 0, the indexed exchange's row limit."""
+    payload, launches = ctypes.c_int64(), ctypes.c_int32()
+    st = lib().a2av_check_host_counts_ex(ctypes.byref(cfg), _host_ptr(host_send_counts), dtype,
+                                         unit, index_stride, ctypes.byref(payload),
+                                         ctypes.byref(launches))
     return st, payload.value, launches.value
 
 
@@ -335,9 +384,11 @@ class Exchange:
         (a2av_run_bias); an ``index`` tensor (int32 [P, index_stride] gather
         lists of rows of ``row_elems`` elements) runs the indexed exchange
         (a2av_run_indexed); a ``host_counts`` array (numpy int32 [P, P], the
-        same counts as ``send_counts``) runs a2av_run_host_counts: count
-        errors are raised before anything is enqueued, and the chunk plan
-        follows the payload.
+        same counts as ``send_counts``), alone or with any of these, runs the
+        host-count form of the exchange (a2av_run_host_counts,
+        a2av_run_blocked_host_counts, a2av_run_bias_host_counts,
+        a2av_run_indexed_host_counts): count errors are raised before
+        anything is enqueued, and the chunk plan follows the payload.
 
         The count and signal checks run on the device, so by default a
         failure is latched and reported by :meth:`query_error`.  With
@@ -345,10 +396,18 @@ class Exchange:
         failure (ValueError for INVALID_ARGS / OVER_CAPACITY, A2avError for
         TIMEOUT), as if the checks had run before the call returned."""
         import torch
-        if sum(x is not None for x in (index, bias, host_counts)) > 1:
-            raise ValueError("index, bias and host_counts select different exchanges; give at most one")
+        if index is not None and bias is not None:
+            raise ValueError("index and bias select different exchanges; give at most one")
         if index is not None and nblk != 1:
             raise ValueError("the indexed exchange takes no nblk")
+        hc = None
+        if host_counts is not None:
+            import numpy as np
+            hc = np.ascontiguousarray(host_counts, dtype=np.int32)
+            if hc.shape != (self.cfg.P, self.cfg.P) or hc is not host_counts:
+                raise ValueError("host_counts must be a contiguous int32 numpy array [P, P] "
+                                 "(the exchange never copies operands)")
+            hc = hc.ctypes.data
         c = self.cfg
         P = c.P
         ip = self._check(input, P * c.in_slab_bytes, "input")
@@ -363,26 +422,31 @@ class Exchange:
                 raise ValueError(f"index must be [P={P}, index_stride], got {tuple(index.shape)}")
             stride = index.shape[1]
             xp = self._check(index, P * stride * 4, "index", torch.int32)
-            st = a2av_run_indexed(self.h, ip, tp, sp, scp, rcp, xp, P, core_num, dtype, row_elems,
-                                  stride, stream.cuda_stream)
+            if hc is not None:
+                st = a2av_run_indexed_host_counts(self.h, ip, tp, sp, scp, rcp, xp, hc, P,
+                                                  core_num, dtype, row_elems, stride,
+                                                  stream.cuda_stream)
+            else:
+                st = a2av_run_indexed(self.h, ip, tp, sp, scp, rcp, xp, P, core_num, dtype,
+                                      row_elems, stride, stream.cuda_stream)
         elif bias is not None:
             be = {BF16: (torch.float32, 4), FP16: (torch.float16, 2)}.get(dtype)
             if be is None:  # the library reports the unsupported dtype
                 bp = self._check(bias, bias.numel() * bias.element_size(), "bias")
             else:
                 bp = self._check(bias, P * nblk * hidden * be[1], "bias", be[0])
-            st = a2av_run_bias(self.h, ip, tp, sp, scp, rcp, bp, P, core_num, dtype, nblk, hidden,
-                               stream.cuda_stream)
-        elif host_counts is not None:
-            import numpy as np
-            hc = np.ascontiguousarray(host_counts, dtype=np.int32)
-            if hc.shape != (P, P) or hc is not host_counts:
-                raise ValueError("host_counts must be a contiguous int32 numpy array [P, P] "
-                                 "(the exchange never copies operands)")
-            if nblk != 1:
-                raise ValueError("host_counts is taken by the plain exchange only")
-            st = a2av_run_host_counts(self.h, ip, tp, sp, scp, rcp, hc.ctypes.data, P, core_num,
-                                      dtype, stream.cuda_stream)
+            if hc is not None:
+                st = a2av_run_bias_host_counts(self.h, ip, tp, sp, scp, rcp, bp, hc, P, core_num,
+                                               dtype, nblk, hidden, stream.cuda_stream)
+            else:
+                st = a2av_run_bias(self.h, ip, tp, sp, scp, rcp, bp, P, core_num, dtype, nblk,
+                                   hidden, stream.cuda_stream)
+        elif hc is not None and nblk == 1:
+            st = a2av_run_host_counts(self.h, ip, tp, sp, scp, rcp, hc, P, core_num, dtype,
+                                      stream.cuda_stream)
+        elif hc is not None:
+            st = a2av_run_blocked_host_counts(self.h, ip, tp, sp, scp, rcp, hc, P, core_num,
+                                              dtype, nblk, stream.cuda_stream)
         elif nblk == 1:
             st = a2av_run(self.h, ip, tp, sp, scp, rcp, P, core_num, dtype, stream.cuda_stream)
         else:

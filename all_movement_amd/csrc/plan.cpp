@@ -173,15 +173,19 @@ int32_t chunk_launches(const a2av_config* cfg, int64_t limit) {
 }
 
 int check_host_counts(const a2av_config* cfg, const int32_t* counts, int64_t elem,
-                      int64_t* payload) {
+                      int64_t unit, int64_t index_stride, int64_t* payload) {
   const int32_t P = cfg->P;
-  for (int64_t i = 0; i < int64_t(P) * P; ++i)
+  const int64_t PP = int64_t(P) * P;
+  for (int64_t i = 0; i < PP; ++i)
     if (counts[i] < 0) return A2AV_ERR_INVALID_ARGS;
+  for (int64_t i = 0; i < PP; ++i)
+    if (counts[i] % unit != 0) return A2AV_ERR_INVALID_ARGS;
   int64_t total = 0;
   for (int32_t s = 0; s < P; ++s) {
     int64_t row = 0;
     for (int32_t d = 0; d < P; ++d) row += counts[int64_t(s) * P + d];
-    if (row * elem > cfg->in_slab_bytes) return A2AV_ERR_OVER_CAPACITY;
+    if (index_stride > 0 ? row / unit > index_stride : row * elem > cfg->in_slab_bytes)
+      return A2AV_ERR_OVER_CAPACITY;
     total += row * elem;
   }
   for (int32_t d = 0; d < P; ++d) {

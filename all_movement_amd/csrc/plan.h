@@ -66,12 +66,16 @@ int64_t gather_max_payload(const a2av_config* cfg, int64_t row_bytes, int64_t in
 // the device skips the part of a chunk past the run's real payload.
 int32_t chunk_launches(const a2av_config* cfg, int64_t limit);
 
-// The count checks of a2av_run on a host copy of the counts (elements of
-// `elem` bytes), in the device's order: a negative count (INVALID_ARGS),
-// then a source row over in_slab or a destination column over tgt_slab
-// (OVER_CAPACITY).  On success *payload is the run's payload in bytes.
+// The device's count checks on a host copy of the counts (elements of
+// `elem` bytes), in the device's order: a negative count (INVALID_ARGS); a
+// count that `unit` does not divide (INVALID_ARGS: not whole sub-blocks, bias
+// rows or gathered rows; unit 1 for the plain exchange); a source row over
+// its limit (over in_slab bytes, or with index_stride > 0 more than
+// index_stride rows of `unit` elements) or a destination column over
+// tgt_slab (OVER_CAPACITY).  On success *payload is the run's payload in
+// bytes.
 int check_host_counts(const a2av_config* cfg, const int32_t* counts, int64_t elem,
-                      int64_t* payload);
+                      int64_t unit, int64_t index_stride, int64_t* payload);
 
 // Launches of at most `limit` bytes that cover `payload` (at least one: the
 // final launch also writes recv_counts and raises the flags).

@@ -478,9 +478,81 @@ int a2av_run_host_counts(a2av_handle* h, const void* input, void* target, int32_
                                 recv_counts, P, core_num, dtype);
   if (st != A2AV_OK) return st;
   int64_t payload = 0;
-  st = a2av::check_host_counts(&h->cfg, host_send_counts, a2av::elem_bytes(dtype), &payload);
+  st = a2av::check_host_counts(&h->cfg, host_send_counts, a2av::elem_bytes(dtype), 1, 0, &payload);
   if (st != A2AV_OK) return st;
   RunExtras x;
+  x.launches = a2av::launches_for(payload, h->chunk_limit);
+  return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, x,
+                     stream);
+}
+
+int a2av_run_blocked_host_counts(a2av_handle* h, const void* input, void* target,
+                                 int32_t* signal, const int32_t* send_counts,
+                                 int32_t* recv_counts, const int32_t* host_send_counts,
+                                 int32_t P, int64_t core_num, int32_t dtype, int32_t nblk,
+                                 void* stream) {
+  if (!h) return A2AV_ERR_NULLPTR;
+  if (!host_send_counts) return A2AV_ERR_NULLPTR;
+  int st = a2av::check_run_args(&h->cfg, h->capacity, input, target, signal, send_counts,
+                                recv_counts, P, core_num, dtype, nblk);
+  if (st != A2AV_OK) return st;
+  int64_t payload = 0;
+  st = a2av::check_host_counts(&h->cfg, host_send_counts, a2av::elem_bytes(dtype), nblk, 0,
+                               &payload);
+  if (st != A2AV_OK) return st;
+  RunExtras x;
+  x.nblk = nblk;
+  x.launches = a2av::launches_for(payload, h->chunk_limit);
+  return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, x,
+                     stream);
+}
+
+int a2av_run_bias_host_counts(a2av_handle* h, const void* input, void* target, int32_t* signal,
+                              const int32_t* send_counts, int32_t* recv_counts,
+                              const void* bias, const int32_t* host_send_counts, int32_t P,
+                              int64_t core_num, int32_t dtype, int32_t nblk, int32_t hidden,
+                              void* stream) {
+  if (!h) return A2AV_ERR_NULLPTR;
+  if (!host_send_counts) return A2AV_ERR_NULLPTR;
+  int st = a2av::check_bias_args(&h->cfg, h->capacity, h->chunk_limit, input, target, signal,
+                                 send_counts, recv_counts, bias, P, core_num, dtype, nblk,
+                                 hidden);
+  if (st != A2AV_OK) return st;
+  int64_t payload = 0;
+  st = a2av::check_host_counts(&h->cfg, host_send_counts, a2av::elem_bytes(dtype),
+                               int64_t(nblk) * hidden, 0, &payload);
+  if (st != A2AV_OK) return st;
+  RunExtras x;
+  x.nblk = nblk;
+  x.bias = bias;
+  x.hidden = hidden;
+  x.mode = dtype == A2AV_BF16 ? 1 : 2;
+  x.launches = a2av::launches_for(payload, h->chunk_limit);
+  return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, x,
+                     stream);
+}
+
+int a2av_run_indexed_host_counts(a2av_handle* h, const void* input, void* target,
+                                 int32_t* signal, const int32_t* send_counts,
+                                 int32_t* recv_counts, const int32_t* index,
+                                 const int32_t* host_send_counts, int32_t P, int64_t core_num,
+                                 int32_t dtype, int32_t row_elems, int64_t index_stride,
+                                 void* stream) {
+  if (!h) return A2AV_ERR_NULLPTR;
+  if (!host_send_counts) return A2AV_ERR_NULLPTR;
+  int st = a2av::check_indexed_args(&h->cfg, h->capacity, input, target, signal, send_counts,
+                                    recv_counts, index, P, core_num, dtype, row_elems,
+                                    index_stride);
+  if (st != A2AV_OK) return st;
+  int64_t payload = 0;
+  st = a2av::check_host_counts(&h->cfg, host_send_counts, a2av::elem_bytes(dtype), row_elems,
+                               index_stride, &payload);
+  if (st != A2AV_OK) return st;
+  RunExtras x;
+  x.index = index;
+  x.index_stride = index_stride;
+  x.row_elems = row_elems;
+  x.mode = 3;
   x.launches = a2av::launches_for(payload, h->chunk_limit);
   return enqueue_run(h, input, target, signal, send_counts, recv_counts, P, core_num, dtype, x,
                      stream);
@@ -490,9 +562,20 @@ int a2av_check_host_counts(const a2av_config* cfg, const int32_t* host_send_coun
                            int32_t dtype, int64_t* payload_bytes, int32_t* launches) {
   if (!cfg || !host_send_counts || !payload_bytes || !launches) return A2AV_ERR_NULLPTR;
   if (dtype != A2AV_FP32 && dtype != A2AV_INT8) return A2AV_ERR_UNSUPPORTED_DTYPE;
-  if (a2av::check_config(cfg) != A2AV_OK) return A2AV_ERR_INVALID_ARGS;
+  return a2av_check_host_counts_ex(cfg, host_send_counts, dtype, 1, 0, payload_bytes, launches);
+}
+
+int a2av_check_host_counts_ex(const a2av_config* cfg, const int32_t* host_send_counts,
+                              int32_t dtype, int64_t unit, int64_t index_stride,
+                              int64_t* payload_bytes, int32_t* launches) {
+  if (!cfg || !host_send_counts || !payload_bytes || !launches) return A2AV_ERR_NULLPTR;
+  if (dtype != A2AV_FP32 && dtype != A2AV_INT8 && dtype != A2AV_FP16 && dtype != A2AV_BF16)
+    return A2AV_ERR_UNSUPPORTED_DTYPE;
+  if (a2av::check_config(cfg) != A2AV_OK || unit < 1 || index_stride < 0)
+    return A2AV_ERR_INVALID_ARGS;
   int64_t payload = 0;
-  const int st = a2av::check_host_counts(cfg, host_send_counts, a2av::elem_bytes(dtype), &payload);
+  const int st = a2av::check_host_counts(cfg, host_send_counts, a2av::elem_bytes(dtype), unit,
+                                         index_stride, &payload);
   if (st != A2AV_OK) return st;
   const int64_t limit = cfg->chunk_limit_bytes > 0 ? cfg->chunk_limit_bytes
                                                    : a2av::kDefaultChunkLimit;

@@ -283,6 +283,57 @@ int a2av_check_host_counts(const a2av_config *cfg, const int32_t *host_send_coun
                            int32_t dtype, int64_t *payload_bytes, int32_t *launches);
 
 /*
+ * a2av_run_blocked, a2av_run_bias and a2av_run_indexed with a host copy of
+ * the counts (the host-side counts of log C, section 7 of the vccl alltoallv
+ * dev log), as a2av_run_host_counts is to a2av_run.  Each takes its
+ * exchange's arguments and host_send_counts (host int32 [P, P], row-major
+ * [s][d], read only, the same counts as send_counts on the device), runs that
+ * exchange's host checks, then the count checks on the host copy in the
+ * device's order, whose status the call returns before anything is enqueued:
+ *   1. a negative count                                  -> INVALID_ARGS
+ *   2. a count that is not whole sub-blocks (blocked: a multiple of nblk),
+ *      whole bias rows (bias: of nblk * hidden) or whole gathered rows
+ *      (indexed: of row_elems)                           -> INVALID_ARGS
+ *   3. a source over its limit (blocked and bias: its row's bytes over
+ *      in_slab; indexed: more rows than index_stride) or a destination
+ *      column's bytes over tgt_slab                     -> OVER_CAPACITY
+ * The chunk plan follows the payload T: ceil(T / limit) launches (at least
+ * one).  The device still checks send_counts, the gather-list entries in use
+ * (indexed) and the signal, latched for a2av_query_error, and refuses a
+ * payload the planned launches cannot cover (OVER_CAPACITY, nothing
+ * written).  NULLPTR when h or host_send_counts is NULL.
+ */
+int a2av_run_blocked_host_counts(a2av_handle *h, const void *input, void *target,
+                                 int32_t *signal, const int32_t *send_counts,
+                                 int32_t *recv_counts, const int32_t *host_send_counts,
+                                 int32_t P, int64_t core_num, int32_t dtype, int32_t nblk,
+                                 void *stream);
+int a2av_run_bias_host_counts(a2av_handle *h, const void *input, void *target, int32_t *signal,
+                              const int32_t *send_counts, int32_t *recv_counts,
+                              const void *bias, const int32_t *host_send_counts, int32_t P,
+                              int64_t core_num, int32_t dtype, int32_t nblk, int32_t hidden,
+                              void *stream);
+int a2av_run_indexed_host_counts(a2av_handle *h, const void *input, void *target,
+                                 int32_t *signal, const int32_t *send_counts,
+                                 int32_t *recv_counts, const int32_t *index,
+                                 const int32_t *host_send_counts, int32_t P, int64_t core_num,
+                                 int32_t dtype, int32_t row_elems, int64_t index_stride,
+                                 void *stream);
+
+/* The count checks of the *_host_counts entry points alone (no GPU needed),
+ * for a handle created with `cfg`: elements of `dtype` (FP32, INT8, FP16 or
+ * BF16), every count a multiple of `unit` (1 for the plain exchange, nblk,
+ * nblk * hidden or row_elems), and with index_stride > 0 the indexed
+ * exchange's row limit in place of in_slab.  Returns the status the run
+ * would return for the counts and, on A2AV_OK, the payload in bytes and the
+ * number of chunk launches (cfg's chunk limit, 0 = 1 GiB).  Errors: NULLPTR,
+ * UNSUPPORTED_DTYPE, INVALID_ARGS (cfg geometry, unit < 1, index_stride < 0,
+ * or a count check), OVER_CAPACITY. */
+int a2av_check_host_counts_ex(const a2av_config *cfg, const int32_t *host_send_counts,
+                              int32_t dtype, int64_t unit, int64_t index_stride,
+                              int64_t *payload_bytes, int32_t *launches);
+
+/*
  * a2av_run without a handle, for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Nothing is allocated: the workspace is one array of 192 KiB per

@@ -72,19 +72,24 @@ typedef struct {
     int64_t chunk;     /* chunk_limit_bytes, 0 = default */
     int32_t nblk;      /* bias: sub-blocks per segment */
     int32_t hidden;    /* bias: row length */
+    int32_t host;      /* blocked, bias, indexed: 1 = the *_host_counts entry point */
 } Case;
 
 static const Case kCases[] = {
-    {"plain_fp32_cooperative", PLAIN, 8, A2AV_FP32, 64, 3000, 1, 0, 0, 0},
-    {"plain_int8_one_block", PLAIN, 4, A2AV_INT8, 1, 9000, 1, 0, 0, 0},
-    {"plain_int8_chunked", PLAIN, 5, A2AV_INT8, 10, 40000, 1, 65536, 0, 0},
-    {"plain_fp32_p64", PLAIN, 64, A2AV_FP32, 256, 300, 1, 0, 0, 0},
-    {"blocked_fp32_nblk4", BLOCKED, 8, A2AV_FP32, 16, 300, 4, 0, 0, 0},
-    {"indexed_int8_rows448", INDEXED, 8, A2AV_INT8, 64, 12, 448, 0, 0, 0},
-    {"bias_bf16_nblk2_h64", BIAS, 8, A2AV_BF16, 16, 10, 2 * 64, 0, 2, 64},
-    {"bias_fp16_nblk3_h24_chunked", BIAS, 5, A2AV_FP16, 5, 12, 3 * 24, 1024, 3, 24},
-    {"host_counts_fp32_chunked", HOSTC, 6, A2AV_FP32, 12, 5000, 1, 16384, 0, 0},
-    {"noalloc_int8_cooperative", NOALLOC, 8, A2AV_INT8, 64, 9000, 1, 0, 0, 0},
+    {"plain_fp32_cooperative", PLAIN, 8, A2AV_FP32, 64, 3000, 1, 0, 0, 0, 0},
+    {"plain_int8_one_block", PLAIN, 4, A2AV_INT8, 1, 9000, 1, 0, 0, 0, 0},
+    {"plain_int8_chunked", PLAIN, 5, A2AV_INT8, 10, 40000, 1, 65536, 0, 0, 0},
+    {"plain_fp32_p64", PLAIN, 64, A2AV_FP32, 256, 300, 1, 0, 0, 0, 0},
+    {"blocked_fp32_nblk4", BLOCKED, 8, A2AV_FP32, 16, 300, 4, 0, 0, 0, 0},
+    {"indexed_int8_rows448", INDEXED, 8, A2AV_INT8, 64, 12, 448, 0, 0, 0, 0},
+    {"bias_bf16_nblk2_h64", BIAS, 8, A2AV_BF16, 16, 10, 2 * 64, 0, 2, 64, 0},
+    {"bias_fp16_nblk3_h24_chunked", BIAS, 5, A2AV_FP16, 5, 12, 3 * 24, 1024, 3, 24, 0},
+    {"host_counts_fp32_chunked", HOSTC, 6, A2AV_FP32, 12, 5000, 1, 16384, 0, 0, 0},
+    {"noalloc_int8_cooperative", NOALLOC, 8, A2AV_INT8, 64, 9000, 1, 0, 0, 0, 0},
+    {"blocked_int8_nblk3_host_counts_chunked", BLOCKED, 6, A2AV_INT8, 12, 2000, 3, 4096, 0, 0, 1},
+    {"bias_bf16_nblk2_h16_host_counts_chunked", BIAS, 4, A2AV_BF16, 8, 10, 2 * 16, 1024, 2, 16,
+     1},
+    {"indexed_fp32_rows5_host_counts_chunked", INDEXED, 5, A2AV_FP32, 10, 20, 5, 4096, 0, 0, 1},
 };
 
 /* A finite 16-bit value: random sign and mantissa, exponent kept well inside
@@ -211,12 +216,23 @@ static int run_case(const Case *c, uint64_t seed)
         else if (c->kind == NOALLOC)
             gpu_st = a2av_run_noalloc(d_in, d_tgt, d_sig, d_send, d_recv, (int32_t *)d_status, P,
                                       in_slab, tgt_slab, S, c->core_num, c->dtype, stream);
+        else if (c->kind == BLOCKED && c->host)
+            gpu_st = a2av_run_blocked_host_counts(h, d_in, d_tgt, d_sig, d_send, d_recv, counts,
+                                                  P, c->core_num, c->dtype, c->unit, stream);
         else if (c->kind == BLOCKED)
             gpu_st = a2av_run_blocked(h, d_in, d_tgt, d_sig, d_send, d_recv, P, c->core_num,
                                       c->dtype, c->unit, stream);
+        else if (c->kind == BIAS && c->host)
+            gpu_st = a2av_run_bias_host_counts(h, d_in, d_tgt, d_sig, d_send, d_recv, d_bias,
+                                               counts, P, c->core_num, c->dtype, c->nblk,
+                                               c->hidden, stream);
         else if (c->kind == BIAS)
             gpu_st = a2av_run_bias(h, d_in, d_tgt, d_sig, d_send, d_recv, d_bias, P, c->core_num,
                                    c->dtype, c->nblk, c->hidden, stream);
+        else if (c->host)
+            gpu_st = a2av_run_indexed_host_counts(h, d_in, d_tgt, d_sig, d_send, d_recv, d_idx,
+                                                  counts, P, c->core_num, c->dtype, c->unit,
+                                                  stride, stream);
         else
             gpu_st = a2av_run_indexed(h, d_in, d_tgt, d_sig, d_send, d_recv, d_idx, P,
                                       c->core_num, c->dtype, c->unit, stride, stream);

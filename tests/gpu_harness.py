@@ -52,11 +52,12 @@ class Case:
         self.recv = torch.full((P, P), -7, dtype=torch.int32, device=DEV)
 
     def run_gpu(self, ex: a2av.Exchange, core_num: int | None = None, sync: bool = True,
-                nblk: int = 1, bias=None, hidden: int = 0, index=None, row_elems: int = 0) -> int:
+                nblk: int = 1, bias=None, hidden: int = 0, index=None, row_elems: int = 0,
+                host_counts: np.ndarray | None = None) -> int:
         w = self.w
         ex.run(self.input, self.target, self.signal, self.send, self.recv,
                w.core_num if core_num is None else core_num, w.dtype, nblk=nblk, bias=bias,
-               hidden=hidden, index=index, row_elems=row_elems)
+               hidden=hidden, index=index, row_elems=row_elems, host_counts=host_counts)
         if sync:
             torch.cuda.synchronize()
             return ex.query_error()

@@ -1,7 +1,8 @@
-"""a2av_run_host_counts: the exchange with a host copy of the counts.  Count
-errors come back from the call itself, before anything is enqueued, and the
-chunk plan follows the payload (ceil(T / limit) launches) instead of the
-geometry bound.  Results against the oracle, byte for byte."""
+"""The exchanges with a host copy of the counts (a2av_run_host_counts and the
+blocked, bias and indexed *_host_counts entry points).  Count errors come back
+from the call itself, before anything is enqueued, and the chunk plan follows
+the payload (ceil(T / limit) launches) instead of the geometry bound.  Results
+against the oracle, byte for byte."""
 import numpy as np
 import pytest
 
@@ -11,7 +12,8 @@ pytestmark = pytest.mark.gpu
 
 from all_movement_amd import a2av  # noqa: E402
 from all_movement_amd import workloads as wl  # noqa: E402
-from tests.gpu_harness import Case, exchange_for, say  # noqa: E402
+from tests.gpu_harness import DEV, Case, exchange_for, say, upload  # noqa: E402
+from tests.test_gpu_random import _case  # noqa: E402
 
 
 @pytest.fixture(autouse=True)
@@ -134,5 +136,73 @@ def test_device_counts_decide_when_the_host_copy_differs():
         ex.run(c.input, c.target, c.signal, c.send, c.recv, 8, wl.FP32, host_counts=hc)
         torch.cuda.synchronize()
         c.assert_matches(ex.query_error(), c.run_oracle())
+    finally:
+        ex.close()
+
+
+def _kind_kwargs(c):
+    """The GPU and oracle arguments of one random case's exchange."""
+    w, kind = c["w"], c["kind"]
+    if kind == "blocked":
+        return dict(nblk=c["nblk"]), dict(nblk=c["nblk"])
+    if kind == "bias":
+        b = c["bias"]
+        bt = torch.from_numpy(b.view(np.float16) if w.dtype == wl.FP16 else b).to(DEV)
+        return (dict(nblk=c["nblk"], bias=bt, hidden=c["hidden"]),
+                dict(nblk=c["nblk"], bias=b, hidden=c["hidden"]))
+    return (dict(index=upload(c["index"]), row_elems=c["R"]),
+            dict(index=c["index"], row_elems=c["R"]))
+
+
+# Seeds of the random mixtures whose exchange is blocked, bias or indexed
+# (seed % 4 = 1, 2, 3), at every chunk limit they draw.
+@pytest.mark.parametrize("seed", [s for s in range(60) if s % 4 != 0])
+def test_every_exchange_with_host_counts(seed):
+    c = _case(seed)
+    w, kind = c["w"], c["kind"]
+    T = w.payload_bytes
+    limit = c["chunk"] or (1 << 30)
+    say(seed, kind, "P", w.P, "dtype", w.dtype, "payload", T, "limit", limit)
+    inp = wl.input16_np(w) if kind == "bias" else wl.input_bytes_np(w)
+    case = Case(w, input_np=inp)
+    ex = exchange_for(w, wg_per_block=c["G"], chunk_limit_bytes=c["chunk"], profile=True)
+    try:
+        gkw, okw = _kind_kwargs(c)
+        st = case.run_gpu(ex, host_counts=np.ascontiguousarray(w.counts, np.int32), **gkw)
+        _, _, launches, runs = ex.profile()
+        case.assert_matches(st, case.run_oracle(**okw))
+        assert st == a2av.OK and launches == runs * max(1, -(-T // limit))
+    finally:
+        ex.close()
+
+
+@pytest.mark.parametrize("kind", ["blocked", "bias", "indexed"])
+@pytest.mark.parametrize("what", ["negative", "not_whole", "over_capacity"])
+def test_count_errors_of_every_exchange_are_returned_by_the_call(kind, what):
+    seed = {"blocked": 1, "bias": 2, "indexed": 3}[kind] + 4 * 3
+    c = _case(seed)
+    w = c["w"]
+    unit = {"blocked": c["nblk"], "bias": c["nblk"] * c["hidden"], "indexed": c["R"]}[kind]
+    if what == "not_whole" and unit == 1:
+        pytest.skip("every count is whole at a unit of one")
+    hc = np.ascontiguousarray(w.counts, np.int32).copy()
+    if what == "negative":
+        hc[0, 0] = -unit
+    elif what == "not_whole":
+        hc[0, 0] += 1
+    else:
+        hc[0, 0] += (w.tgt_slab // wl.ELEM_SIZE[w.dtype] // unit + 1) * unit   # column 0 over
+    case = Case(w, input_np=wl.input16_np(w) if kind == "bias" else wl.input_bytes_np(w))
+    ex = exchange_for(w, wg_per_block=c["G"], chunk_limit_bytes=c["chunk"])
+    try:
+        gkw, _ = _kind_kwargs(c)
+        want = "OVER_CAPACITY" if what == "over_capacity" else "INVALID_ARGS"
+        with pytest.raises(ValueError, match=want):
+            case.run_gpu(ex, host_counts=hc, **gkw)
+        torch.cuda.synchronize()
+        assert ex.query_error() == a2av.OK           # nothing was enqueued
+        assert (case.target.cpu().numpy() == wl.SENTINEL).all()
+        np.testing.assert_array_equal(case.signal.cpu().numpy(), case.signal_np0)
+        assert (case.recv.cpu().numpy() == -7).all()
     finally:
         ex.close()

@@ -352,7 +352,7 @@ def test_host_errors_raise_before_enqueue():
         with pytest.raises(ValueError, match="at most one"):       # two exchanges named
             ex.run(c.input, c.target, c.signal, c.send, c.recv, 4, wl.FP32,
                    index=torch.zeros((P, 4), dtype=torch.int32, device=DEV), row_elems=1,
-                   host_counts=w.counts)
+                   bias=torch.zeros((P, 1, 8), dtype=torch.float32, device=DEV), hidden=8)
         with pytest.raises(ValueError, match="no nblk"):
             ex.run(c.input, c.target, c.signal, c.send, c.recv, 4, wl.FP32, nblk=2,
                    index=torch.zeros((P, 4), dtype=torch.int32, device=DEV), row_elems=1)

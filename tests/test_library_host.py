@@ -382,3 +382,83 @@ def test_gather_chunk_plan_takes_the_smaller_bound():
     assert lib.a2av_check_indexed_args(*args(over, 1 << 18)) == a2av.ERR_INVALID_ARGS
     # 2^17 rows of 4 bytes per source: 2^22 bytes / 7 < 2^20 launches.
     assert lib.a2av_check_indexed_args(*args(over, 1 << 17)) == a2av.OK
+
+
+@pytest.mark.parametrize("kind", ["blocked", "bias", "indexed"])
+@pytest.mark.parametrize("seed", range(16))
+def test_host_count_checks_of_every_exchange_match_oracle(kind, seed):
+    # a2av_check_host_counts_ex (the host part of the blocked, bias and
+    # indexed *_host_counts entry points) against the oracle's status for the
+    # same counts: negative, then not whole sub-blocks / bias rows / gathered
+    # rows, then a source over in_slab (over index_stride rows for the row
+    # gather) or a column over tgt_slab.  Signal equal and gather entries in
+    # range, so the oracle's first failure, if any, is a count check; its
+    # chunk plan against ceil(T / limit).
+    rng = np.random.default_rng(1000 + seed)
+    P = int(rng.integers(1, 7))
+    if kind == "bias":
+        dtype = [wl.BF16, wl.FP16][seed % 2]
+        nblk, hidden = int(rng.choice([1, 2, 3])), int(rng.choice([1, 4, 8]))
+        unit = nblk * hidden
+    else:
+        dtype = [wl.FP32, wl.INT8][seed % 2]
+        nblk = int(rng.choice([1, 2, 4])) if kind == "blocked" else 1
+        hidden = 0
+        unit = nblk if kind == "blocked" else int(rng.choice([1, 3, 5]))
+    e = wl.ELEM_SIZE[dtype]
+    C = (rng.integers(0, 6, size=(P, P)) * unit).astype(np.int32)
+    what = seed % 4
+    if what == 1:
+        C[rng.integers(P), rng.integers(P)] = -unit
+    elif what == 2 and unit > 1:
+        C[rng.integers(P), rng.integers(P)] += 1             # not whole
+    elif what == 3:
+        C[rng.integers(P), rng.integers(P)] += 8 * unit      # some row or column over
+    rows = C.astype(np.int64).sum(axis=1) // unit
+    stride = int(max(rows.max(initial=0), 1)) if kind == "indexed" else 0
+    slack = int(rng.integers(0, 2)) * unit * e
+    in_slab = max(int(C.sum(axis=1).max(initial=0)) * e, unit * e) + slack
+    tgt_slab = max(int(C.sum(axis=0).max(initial=0)) * e, e) + slack
+    if what == 3:
+        stride = max(1, stride - 8)
+        in_slab, tgt_slab = max(unit * e, in_slab - 8 * unit * e), max(e, tgt_slab - 8 * unit * e)
+    limit = int(rng.choice([0, 64, 96]))
+    cfg = _hc_cfg(P, in_slab, tgt_slab, limit)
+    st, payload, launches = a2av.a2av_check_host_counts_ex(cfg, C, dtype, unit, stride)
+
+    inp = np.zeros(P * in_slab, np.uint8)
+    tgt = np.zeros(P * tgt_slab, np.uint8)
+    sig = np.zeros((P, 4), np.int32)
+    rc = np.zeros((P, P), np.int32)
+    geo = dict(P=P, S=4, in_slab=in_slab, tgt_slab=tgt_slab, core_num=1, dtype=dtype)
+    if kind == "blocked":
+        st_o = oracle.run_blocked(inp, tgt, sig, C, rc, nblk=nblk, **geo)
+    elif kind == "bias":
+        b = np.zeros(P * nblk * hidden, np.float32 if dtype == wl.BF16 else np.uint16)
+        st_o = oracle.run_bias(inp, tgt, sig, C, rc, b, nblk=nblk, hidden=hidden, **geo)
+    else:
+        index = np.zeros(P * stride, np.int32)               # row 0 of every table
+        st_o = oracle.run_indexed(inp, tgt, sig, C, rc, index, row_elems=unit,
+                                  index_stride=stride, **geo)
+    assert st == st_o, (kind, what, st, st_o)
+    if st == a2av.OK:
+        T = int(C.astype(np.int64).sum()) * e
+        assert payload == T and launches == max(1, -(-T // (limit or (1 << 30))))
+
+
+def test_host_count_checks_ex_arguments():
+    C = np.full((4, 4), 6, np.int32)
+    cfg = _hc_cfg(4, 1024, 1024)
+    assert a2av.a2av_check_host_counts_ex(cfg, C, 7, 1, 0)[0] == a2av.ERR_UNSUPPORTED_DTYPE
+    assert a2av.a2av_check_host_counts_ex(cfg, None, wl.FP32, 1, 0)[0] == a2av.ERR_NULLPTR
+    assert a2av.a2av_check_host_counts_ex(cfg, C, wl.FP32, 0, 0)[0] == a2av.ERR_INVALID_ARGS
+    assert a2av.a2av_check_host_counts_ex(cfg, C, wl.FP32, 1, -1)[0] == a2av.ERR_INVALID_ARGS
+    assert a2av.a2av_check_host_counts_ex(cfg, C, wl.FP16, 3, 0) == (a2av.OK, 192, 1)
+    assert a2av.a2av_check_host_counts_ex(cfg, C, wl.INT8, 4, 0)[0] == a2av.ERR_INVALID_ARGS
+    # Row gather: 4 sources x 4 destinations x 2 rows of 3 elements = 8 rows
+    # per source: a list of 8 holds them, 7 does not.
+    assert a2av.a2av_check_host_counts_ex(cfg, C, wl.INT8, 3, 8)[0] == a2av.OK
+    assert a2av.a2av_check_host_counts_ex(cfg, C, wl.INT8, 3, 7)[0] == a2av.ERR_OVER_CAPACITY
+    # The plain checker is the unit-1 case.
+    assert a2av.a2av_check_host_counts(cfg, C, wl.FP32) == \
+        a2av.a2av_check_host_counts_ex(cfg, C, wl.FP32, 1, 0)
