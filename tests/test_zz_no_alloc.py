@@ -3,7 +3,8 @@ the library's per-device array) against a2av_run (a handle's workspace) on
 the same inputs, through the C ABI: two calls in a row, the second with a
 smaller input (fewer ranks, fewer blocks, another dtype), then a device-side
 failure and a valid run after it.  Target, signal, recv_counts and the
-status word must match what a2av_run gives, byte for byte, and the oracle."""
+status word must match what a2av_run gives, byte for byte, and the oracle.
+Also a run captured into a HIP graph and replayed, against the oracle."""
 import numpy as np
 import pytest
 
@@ -73,6 +74,51 @@ def test_noalloc_matches_a2av_run_twice_then_error_then_valid():
     say("noalloc device-side error")
     assert _compare(bad, status) == a2av.ERR_INVALID_ARGS
     assert _compare(small, status) == a2av.OK
+
+
+@pytest.mark.parametrize("core_num", [64, 1])
+def test_noalloc_run_captured_into_a_graph_and_replayed(core_num):
+    # Code under HIP graph capture is among the callers this entry point is
+    # for: a run is captured once (after an eager run, so the device's array
+    # address is already known) and replayed three times, with a new payload
+    # before each replay; the status word, target, signal and recv_counts
+    # match the oracle after every replay.  core_num 64: a cooperative final
+    # launch (B = 64); 1: a regular one.
+    rng = np.random.default_rng(7 + core_num)
+    w = wl.custom(8, wl.INT8, wl.uniform_counts(rng, 8, 20000, 0.2), core_num=core_num, seed=61)
+    inp0 = wl.input_bytes_np(w)
+    c = Case(w, input_np=inp0)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+
+    def check():
+        exp = c.run_oracle()
+        assert int(status.item()) == a2av.OK
+        c.assert_matches(a2av.OK, exp)
+        c.signal_np0 = exp[2].copy()
+
+    assert _noalloc(c, w.core_num, status) == a2av.OK
+    torch.cuda.synchronize()
+    check()
+    g = torch.cuda.CUDAGraph()
+    try:
+        with torch.cuda.graph(g):
+            assert _noalloc(c, w.core_num, status) == a2av.OK
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(c.signal.cpu().numpy(), c.signal_np0)  # nothing ran
+        for rep in range(3):
+            say("noalloc replay", rep, "core_num", core_num)
+            new = np.roll(inp0, 1 + rep)
+            c.input.copy_(torch.from_numpy(new).to(DEV))
+            c.input_np = new
+            c.target.fill_(wl.SENTINEL)
+            c.recv.fill_(-7)
+            status.fill_(-99)
+            g.replay()
+            torch.cuda.synchronize()
+            check()
+    finally:
+        del g
+        torch.cuda.synchronize()
 
 
 def test_noalloc_host_errors():
