@@ -95,7 +95,11 @@ struct CopyParams {
 };
 
 constexpr int kCountThreads = 1024;
-constexpr int kCopyThreads = 1024;
+constexpr int kCopyThreads = 1024;  // K2 workgroups of the plain, blocked and indexed exchanges
+// K2 workgroups of the fused-bias exchange: 512 threads with 8 words in flight
+// per lane, 64 KiB tiles (measured on gfx950 against 1024 threads and 128 KiB
+// tiles: c5b 6,114 -> 6,324 GB/s over the whole run, c5h 6,247 -> 6,455).
+constexpr int kBiasThreads = 512;
 
 // Launch helpers (defined in kernels.hip).
 hipError_t launch_count(const CountParams& p, int workgroups, hipStream_t stream);

@@ -48,15 +48,17 @@ constexpr int kWave = 64;
 constexpr int kUnroll = 4;          // 16-byte words in flight per lane, aligned body
 constexpr int kRealignUnroll = 4;   // 64-word rows in flight per wave, realigned body
 
-// Flattened payload bytes per workgroup tile: one pass of the body, 64 KiB
-// for the byte copy (4 words per lane), 128 KiB for the bias and gather
-// bodies (8 words per lane).  With the copy body at 64 KiB tiles c5 ran
+// Flattened payload bytes per workgroup tile: one pass of the body.  64 KiB
+// for the byte copy (1024 threads, 4 words per lane) and for the bias body
+// (512 threads, 8 words per lane), 128 KiB for the gather body (1024
+// threads, 8 words per lane).  With the copy body at 64 KiB tiles c5 ran
 // 2,715 -> 2,624 us per run, c3 181.5 -> 176.4, c4 338.5 -> 328.1 (the
 // narrower window of tiles in flight streams better, as the probes show);
-// the bias and gather bodies lose 9 % at 64 KiB.
+// at 1024 threads the bias and gather bodies lost 9 % at 64 KiB, and the
+// gather body still loses at 512 threads.
 template <int MODE>
 constexpr int64_t tile_bytes() {
-  return MODE == 0 ? 65536 : 131072;
+  return MODE == 3 ? 131072 : 65536;
 }
 
 // Buffer resources: word 3 of a raw (untyped, stride 0) buffer descriptor on
@@ -775,10 +777,9 @@ __device__ inline u32x4 add_bias_word(u32x4 x, u32x4 b0, u32x4 b1) {
 // bias values once per piece.  Longer rows step NT words at a time and each
 // word loads its own bias values; the column then advances by 8 * NT
 // (mod hidden) per step.
-template <int MODE>
+template <int NT, int MODE>
 __device__ void wg_bias_piece(const uint8_t* src, uint8_t* dst, int64_t n, const uint8_t* brow,
                               int64_t e0, int32_t hidden, int tid) {
-  constexpr int NT = kCopyThreads;
   constexpr int BE = MODE == 1 ? 4 : 2;  // bias bytes per element
   src = wave_uniform(src);
   dst = wave_uniform(dst);
@@ -1098,7 +1099,7 @@ __device__ inline void tile_bounds(const SegTables& tab, int nseg, const uint8_t
 // so a piece is also cut where a sub-block ends (the byte copy gets each
 // sub-block as a segment of its own when the tables hold them, and then
 // arrives here with nblk = 1).
-template <int MODE>
+template <int NT, int MODE>
 __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int64_t x, int64_t b,
                                   int i, int tid, int lane, int wave, int& small) {
   while (x < b) {
@@ -1148,7 +1149,7 @@ __device__ inline void copy_range(const CopyParams& p, const SegTables& tab, int
                                 (int64_t(s) * p.nblk + a) * p.hidden * be;
           const uint8_t* src = p.input + tab.src[i] + a * stride + w;
           uint8_t* dst = p.target + tab.dst[i] + off;
-          wg_bias_piece<MODE>(src, dst, end - off, brow, w >> 1, p.hidden, tid);
+          wg_bias_piece<NT, MODE>(src, dst, end - off, brow, w >> 1, p.hidden, tid);
           off = end;
         }
       } else if (p.nblk == 1) {
@@ -1262,7 +1263,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
     int li = 0;
     if (tl < nstatic) tile_bounds(tab, nseg, p.target, c_lo, c_hi, tile, tl, la, lb, li);
     for (int j = 0; j < kWave && t0 + int64_t(j) * W < nstatic; ++j) {
-      copy_range<MODE>(p, tab, readlane64(la, j), readlane64(lb, j), __builtin_amdgcn_readlane(li, j),
+      copy_range<NT, MODE>(p, tab, readlane64(la, j), readlane64(lb, j), __builtin_amdgcn_readlane(li, j),
                  tid, lane, wave, small);
     }
   }
@@ -1297,7 +1298,7 @@ __global__ __launch_bounds__(NT) void copy_kernel(CopyParams p) {
       const int64_t b = x1 >= c_hi ? c_hi : align_boundary_w(tab, nseg, p.target, x1, c_hi, lane, ib);
       if (t == 0 || a >= tab.prefix[ia + 1]) ia = wave_seg_of(tab, nseg, a, lane);
       if (a < b)
-        copy_range<MODE>(p, tab, wave_uniform(a), wave_uniform(b),
+        copy_range<NT, MODE>(p, tab, wave_uniform(a), wave_uniform(b),
                          __builtin_amdgcn_readfirstlane(ia), tid, lane, wave, small);
       // The next claim goes to the other slot: every thread read it at the
       // start of the previous tile, before the barrier that ended that tile.
@@ -1375,12 +1376,14 @@ namespace {
 // One instantiation per body, so the plain kernel carries no bias code.
 const void* copy_kernel_for(int mode) {
   switch (mode) {
-    case 1: return reinterpret_cast<const void*>(&copy_kernel<kCopyThreads, 1>);
-    case 2: return reinterpret_cast<const void*>(&copy_kernel<kCopyThreads, 2>);
+    case 1: return reinterpret_cast<const void*>(&copy_kernel<kBiasThreads, 1>);
+    case 2: return reinterpret_cast<const void*>(&copy_kernel<kBiasThreads, 2>);
     case 3: return reinterpret_cast<const void*>(&copy_kernel<kCopyThreads, 3>);
     default: return reinterpret_cast<const void*>(&copy_kernel<kCopyThreads, 0>);
   }
 }
+
+int copy_threads_for(int mode) { return mode == 1 || mode == 2 ? kBiasThreads : kCopyThreads; }
 
 }  // namespace
 
@@ -1388,8 +1391,9 @@ hipError_t launch_copy(const CopyParams& p, int workgroups, bool cooperative, hi
   void* args[] = {const_cast<CopyParams*>(&p)};
   const void* f = copy_kernel_for(p.mode);
   if (cooperative)
-    return hipLaunchCooperativeKernel(f, dim3(workgroups), dim3(kCopyThreads), args, 0, stream);
-  return hipLaunchKernel(f, dim3(workgroups), dim3(kCopyThreads), args, 0, stream);
+    return hipLaunchCooperativeKernel(f, dim3(workgroups), dim3(copy_threads_for(p.mode)), args,
+                                      0, stream);
+  return hipLaunchKernel(f, dim3(workgroups), dim3(copy_threads_for(p.mode)), args, 0, stream);
 }
 
 hipError_t copy_occupancy(int* wgs_per_cu) {
@@ -1399,7 +1403,7 @@ hipError_t copy_occupancy(int* wgs_per_cu) {
   for (int mode = 0; mode < 4; ++mode) {
     int n = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, copy_kernel_for(mode),
-                                                                      kCopyThreads, 0);
+                                                                      copy_threads_for(mode), 0);
     if (e != hipSuccess) return e;
     if (n < best) best = n;
   }

@@ -109,7 +109,7 @@ typedef struct a2av_launch_info {
     int64_t blocks;            /* B = CalAllToAllVBlocks(P, core_num)                    */
     int32_t wg_per_block;      /* G: workgroups that execute one admitted block          */
     int32_t workgroups;        /* W = B * G workgroups per K2 launch                     */
-    int32_t threads_per_wg;    /* K2 workgroup size                                      */
+    int32_t threads_per_wg;    /* K2 workgroup size (the bias exchange's K2 runs 512)    */
     int32_t chunk_launches;    /* K2 launches per run (host chunk plan)                  */
     int64_t chunk_limit_bytes; /* payload bytes per K2 launch                            */
     int64_t capacity;          /* co-resident K2 workgroups on the device                */
