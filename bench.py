@@ -437,7 +437,7 @@ def main():
                     help="only time the launch probe (regular against cooperative launches, "
                          "--steps pairs of each kind) and print it")
     ap.add_argument("--no-block-wait", action="store_true",
-                    help="run the main workload on a handle with A2AV_FLAG_NO_BLOCK_WAIT (a "
+                    help="run every workload on a handle with A2AV_FLAG_NO_BLOCK_WAIT (a "
                          "regular final launch; for counter runs under a profiler)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain torch device copy of MIB MiB --steps times (the "
@@ -467,7 +467,10 @@ def main():
         f"{main_res['k2_gbps']:.1f} GB/s, {main_res['ms_per_step']:.3f} ms/step")
     also = {}
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
-        r = run_gpu(WORKLOADS[name], args.steps, args.warmup, cold=not args.no_cold)
+        also_spec = WORKLOADS[name]
+        if args.no_block_wait:
+            also_spec = dataclasses.replace(also_spec, block_wait=False)
+        r = run_gpu(also_spec, args.steps, args.warmup, cold=not args.no_cold)
         log(f"[bench] {r['w'].name}: {r['gbps']:.1f} GB/s whole run, K2 {r['k2_gbps']:.1f} GB/s")
         also[r["w"].name] = {"value": round(r["gbps"], 1), "frac_of_peak": round(r["gbps"] / PEAK_GBPS, 4),
                              "k2_gbps": round(r["k2_gbps"], 1), "ms_per_step": round(r["ms_per_step"], 4),
